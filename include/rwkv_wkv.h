@@ -1,0 +1,104 @@
+/*
+ * rwkv_wkv.h -- C ABI of librwkv_wkv, the RWKV-4 time-mixing WKV operator on gfx950.
+ *
+ * Operator. For one sequence b and one channel c, with 0-based token index t:
+ *
+ *     y_t = ( sum_{i<t} e^{-(t-1-i) w + k_i} v_i  +  e^{u + k_t} v_t )
+ *         / ( sum_{i<t} e^{-(t-1-i) w + k_i}      +  e^{u + k_t}     )
+ *
+ * a weighted average of v in which older tokens decay with their distance through one
+ * per-channel rate w, the current token gets a per-channel bonus u, and channels are
+ * independent ("RWKV解读：在Transformer的时代的新RNN", section 二.3 "RWKV的网络架构",
+ * formula (8); "RWKV についての調査記録", section 【wkvとは】). The same values have a
+ * recursive form (formula (8) remark on the first page), which is what the decode entry
+ * point advances one token at a time ("RWKV についての調査記録", section "RWKVとは？":
+ * at inference the model takes a token and a state and returns the new state).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are fp32, dense, row-major, and live in device memory owned by the
+ *     caller. k, v, y, dy, dk, dv are [B][T][C] with C fastest; decode tensors and the
+ *     state are [B][C]; w, u, dw, du are [C].
+ *   - w is the positive decay rate itself (weight of a token i steps back beyond the
+ *     previous one is e^{-i w}); it is not log w and not -w. Results are unspecified for
+ *     w < 0, for non-finite inputs, and for |v| > 1e20.
+ *   - Outputs must not alias inputs, except the decode state, which is updated in place.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
+ *     validates its arguments on the host, enqueues its kernels on `stream` and returns
+ *     without synchronizing; a kernel fault surfaces at the caller's next synchronization.
+ *   - Every call returns WKV_OK (0) or an error code. Argument errors are detected before
+ *     any HIP call and launch nothing; the message of the last failing call on the
+ *     calling thread is available from wkv_last_error(). A zero-sized dimension is a
+ *     successful no-op (dw and du are zero-filled when C > 0 and B*T == 0).
+ *   - The library allocates no device memory: scratch space is passed in by the caller.
+ */
+#ifndef RWKV_WKV_H
+#define RWKV_WKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV_OK 0
+#define WKV_ERR_INVALID_ARG 1 /* null pointer with a nonzero size, negative or too large dim, short buffer */
+#define WKV_ERR_UNSUPPORTED 2 /* the current device is not gfx950 */
+#define WKV_ERR_HIP 3         /* a HIP runtime call or kernel launch failed */
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int wkv_version(void);
+
+/* Static description of a status code ("ok", "invalid argument", ...). Never NULL. */
+const char *wkv_status_string(int status);
+
+/* Message of the last failing call made by this thread ("" if none). Never NULL. */
+const char *wkv_last_error(void);
+
+/* Bytes of the optional carry buffer that wkv_forward can fill for wkv_backward: the
+ * recurrent state (the two sums of the recursive form and their scale) at every 256-token
+ * boundary of every (b, c) sequence, 16 bytes each. Its content is opaque and only valid
+ * for the same B, T, C, w, k, v. Returns 0 for invalid dims. */
+size_t wkv_saved_size(int64_t B, int64_t T, int64_t C);
+
+/* Forward: y [B][T][C] from k, v [B][T][C] and w, u [C], starting from the empty state
+ * (formula (8) of "RWKV解读：在Transformer的时代的新RNN", section 二.3).
+ * `saved` may be NULL; otherwise it must hold at least wkv_saved_size(B, T, C) bytes
+ * (`saved_bytes`) and receives the carries that let wkv_backward skip its own pass over
+ * k and v. Requires B*T*C < 2^62, C <= 2^24 and B*ceil(C/64) < 2^31. */
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                const float *k, const float *v, float *y, void *saved, size_t saved_bytes,
+                void *stream);
+
+/* Bytes of device scratch that wkv_backward needs. With have_saved != 0 the caller will
+ * pass the buffer filled by wkv_forward; with have_saved == 0 the carries are recomputed
+ * into the workspace, which then also covers wkv_saved_size(B, T, C). */
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_saved);
+
+/* Backward of L = sum_{b,t,c} dy[b,t,c] * y[b,t,c] ("RWKV についての調査記録", section
+ * "Trainingについて": all parameters get gradients): dk, dv [B][T][C] and dw, du [C],
+ * where dw and du are summed over b and t and overwritten (not accumulated). dw is the
+ * gradient with respect to w itself (a caller that stores d = log w uses w * dw).
+ * `saved` is NULL or the buffer wkv_forward filled for the same inputs. `workspace`
+ * must hold wkv_backward_workspace_size(B, T, C, saved != NULL) bytes (`workspace_bytes`),
+ * be 256-byte aligned, and is clobbered. dw and du are computed in a fixed order and
+ * are bitwise reproducible run to run. */
+int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                 const float *k, const float *v, const float *dy, const void *saved,
+                 float *dk, float *dv, float *dw, float *du, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* One decode step for B sequences (the recursive form; "RWKV についての調査記録",
+ * section "RWKVとは？"). k, v, y are [B][C]; the state is three [B][C] arrays a, b, p
+ * meaning A = a e^p, B = b e^p, where A and B are the decayed sums of e^{k_i} v_i and
+ * e^{k_i} over the tokens seen so far; the empty state is a = b = 0, p = -1e38.
+ * y is computed from the state before the update, then the state is advanced by the
+ * token in place. Any rescaled equivalent (a e^d, b e^d, p - d) is the same state. */
+int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
+                    const float *v, float *a, float *b, float *p, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV_WKV_H */

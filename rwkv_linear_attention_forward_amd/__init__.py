@@ -1,0 +1,211 @@
+"""Python binding of librwkv_wkv, the RWKV-4 WKV operator for MI355X (gfx950).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels of
+librwkv_wkv.so (built in-tree by ``build.py``); PyTorch provides device memory and the
+current stream. Importing this module loads the library and fails loudly if it has not
+been built; there is no CPU fallback.
+
+Entry points mirror the C ABI in include/rwkv_wkv.h:
+
+    forward(w, u, k, v, saved=None) -> y
+    saved_size(B, T, C) -> int
+    backward(w, u, k, v, dy, saved=None) -> (dk, dv, dw, du)
+    decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
+
+Operator ("RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (8)):
+    y_t = (sum_{i<t} e^{-(t-1-i)w + k_i} v_i + e^{u+k_t} v_t)
+        / (sum_{i<t} e^{-(t-1-i)w + k_i}     + e^{u+k_t})
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # first: its HIP runtime is the one the library binds to
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librwkv_wkv.so")
+
+WKV_OK = 0
+WKV_ERR_INVALID_ARG = 1
+WKV_ERR_UNSUPPORTED = 2
+WKV_ERR_HIP = 3
+
+# Every symbol the header declares, for the export check.
+EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_saved_size",
+           "wkv_forward", "wkv_backward_workspace_size", "wkv_backward", "wkv_decode_step")
+
+_lib = None
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C ABI. Raises ImportError if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("librwkv_wkv.so not found at %s: run "
+                          "`python rwkv_linear_attention_forward_amd/build.py`" % path)
+    lib = ctypes.CDLL(path)
+    lib.wkv_version.restype = ctypes.c_int
+    lib.wkv_version.argtypes = []
+    lib.wkv_status_string.restype = ctypes.c_char_p
+    lib.wkv_status_string.argtypes = [ctypes.c_int]
+    lib.wkv_last_error.restype = ctypes.c_char_p
+    lib.wkv_last_error.argtypes = []
+    lib.wkv_saved_size.restype = ctypes.c_size_t
+    lib.wkv_saved_size.argtypes = [_I64, _I64, _I64]
+    lib.wkv_forward.restype = ctypes.c_int
+    lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_backward_workspace_size.restype = ctypes.c_size_t
+    lib.wkv_backward_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
+    lib.wkv_backward.restype = ctypes.c_int
+    lib.wkv_backward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, ctypes.c_size_t, _P]
+    lib.wkv_decode_step.restype = ctypes.c_int
+    lib.wkv_decode_step.argtypes = [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    _lib = lib
+    return lib
+
+
+class WKVError(RuntimeError):
+    """A nonzero status from librwkv_wkv, with the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d): %s" % (_status_name(status), status, message))
+        self.status = status
+
+
+def _status_name(status: int) -> str:
+    return load_library().wkv_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != WKV_OK:
+        raise WKVError(status, load_library().wkv_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU device" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_btc(w, u, k, v):
+    _need(k, "k", 3)
+    dev = k.device
+    _need(v, "v", 3, dev)
+    _need(w, "w", 1, dev)
+    _need(u, "u", 1, dev)
+    B, T, C = k.shape
+    if v.shape != k.shape:
+        raise ValueError("v shape %s != k shape %s" % (tuple(v.shape), tuple(k.shape)))
+    if w.shape[0] != C or u.shape[0] != C:
+        raise ValueError("w and u must have C=%d elements" % C)
+    return B, T, C, dev
+
+
+def saved_size(B: int, T: int, C: int) -> int:
+    """Bytes of the carry buffer wkv_forward can fill for wkv_backward."""
+    return int(load_library().wkv_saved_size(B, T, C))
+
+
+def new_saved(B: int, T: int, C: int, device) -> torch.Tensor:
+    """A uint8 device tensor large enough for the forward's saved carries."""
+    return torch.empty(max(1, saved_size(B, T, C)), dtype=torch.uint8, device=device)
+
+
+def forward(w, u, k, v, saved=None, out=None):
+    """y [B,T,C] = WKV(w, u, k, v); fills `saved` (uint8 tensor) if given."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    y = torch.empty_like(k) if out is None else out
+    _need(y, "out", 3, dev)
+    if y.shape != k.shape:
+        raise ValueError("out has the wrong shape")
+    sbytes = 0
+    if saved is not None:
+        if saved.dtype != torch.uint8 or saved.device != dev or not saved.is_contiguous():
+            raise ValueError("saved must be a contiguous uint8 tensor on %s" % dev)
+        sbytes = saved.numel()
+    _check(load_library().wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                      _ptr(saved), sbytes, _stream(dev)))
+    return y
+
+
+def backward(w, u, k, v, dy, saved=None, workspace=None):
+    """(dk, dv, dw, du) of sum(dy * y); `saved` from forward() for the same inputs."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    _need(dy, "dy", 3, dev)
+    if dy.shape != k.shape:
+        raise ValueError("dy has the wrong shape")
+    lib = load_library()
+    wsz = int(lib.wkv_backward_workspace_size(B, T, C, 1 if saved is not None else 0))
+    if workspace is None or workspace.numel() < wsz:
+        workspace = torch.empty(max(1, wsz), dtype=torch.uint8, device=dev)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(k)
+    dw = torch.empty_like(w)
+    du = torch.empty_like(u)
+    _check(lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy), _ptr(saved),
+                            _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(workspace),
+                            workspace.numel(), _stream(dev)))
+    return dk, dv, dw, du
+
+
+def decode_step(w, u, k, v, a, b, p, out=None):
+    """One token for B sequences: y [B,C]; the state (a, b, p) [B,C] is updated in place."""
+    _need(k, "k", 2)
+    dev = k.device
+    for t, n in ((v, "v"), (a, "a"), (b, "b"), (p, "p")):
+        _need(t, n, 2, dev)
+        if t.shape != k.shape:
+            raise ValueError("%s shape %s != k shape %s" % (n, tuple(t.shape), tuple(k.shape)))
+    _need(w, "w", 1, dev)
+    _need(u, "u", 1, dev)
+    B, C = k.shape
+    if w.shape[0] != C or u.shape[0] != C:
+        raise ValueError("w and u must have C=%d elements" % C)
+    y = torch.empty_like(k) if out is None else out
+    _check(load_library().wkv_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(a),
+                                          _ptr(b), _ptr(p), _ptr(y), _stream(dev)))
+    return y
+
+
+class WKV(torch.autograd.Function):
+    """Autograd wrapper: y = WKV(w, u, k, v); the forward keeps its carries for backward."""
+
+    @staticmethod
+    def forward(ctx, w, u, k, v):
+        B, T, C = k.shape
+        saved = new_saved(B, T, C, k.device)
+        y = forward(w, u, k, v, saved=saved)
+        ctx.save_for_backward(w, u, k, v, saved)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        w, u, k, v, saved = ctx.saved_tensors
+        dk, dv, dw, du = backward(w, u, k, v, dy.contiguous(), saved=saved)
+        return dw, du, dk, dv
+
+
+load_library()

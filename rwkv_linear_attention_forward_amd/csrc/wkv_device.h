@@ -1,0 +1,139 @@
+// wkv_device.h -- device helpers shared by the WKV kernels (gfx950, wave64).
+//
+// Two state representations are used:
+//
+//   Carry (a, b, P): the two sums of the recursive form of formula (8)
+//     ("RWKV解读：在Transformer的时代的新RNN", section 二.3),
+//       A_t = sum_{i<t} e^{-(t-1-i)w + k_i} v_i,   B_t = sum_{i<t} e^{-(t-1-i)w + k_i},
+//     held as A = a 2^P, B = b 2^P with a, b in fp32 and the base-2 log-scale P in fp64.
+//     Carries move between 32-token chunks; keeping P in fp64 means thousands of decay
+//     steps (P -= L w log2 e) add no rounding drift to the relative weight of old tokens.
+//
+//   Rs (a, b, p): the same sums per token, A = a e^p, B = b e^p, fp32, natural log-scale.
+//     Used by the decode step (whose state the public API exposes) and by the exact
+//     per-token path that chunks fall back to when their fixed frame would under- or
+//     overflow. Its update keeps p fixed while older mass dominates and applies the decay
+//     to a and b with a single rounding per step, so p carries no drift over long decode
+//     runs. The decay factor itself must be exact to a few 1e-8 relative: for small w it is
+//     applied as a - a (1 - e^{-w}) in one fma (1 - e^{-w} = -expm1(-w) is accurate, while
+//     e^{-w} rounded to fp32 is off by up to 3e-8 per step, which compounds); for large w
+//     as a e^{-w} (1 - fp32(1 - e^{-w}) would lose the small factor to cancellation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkvdev {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr double kLog2eD = 1.44269504088896340736;
+constexpr double kLn2D = 0.69314718055994530942;
+constexpr float kNegBig = -1e30f;   // "no mass yet" log-scale: finite, so no inf - inf
+constexpr double kNegBigD = -1e30;
+constexpr float kTinyDen = 0x1p-100f;  // smallest in-frame denominator the fast path accepts
+constexpr float kCarryGap = 64.0f;     // largest log2 gap (carry above chunk frame) accepted
+constexpr float kRenorm = 0x1p-40f;    // Rs renormalization threshold on b
+constexpr float kRenormUp = 0x1p40f;
+constexpr float kRenormLn = 27.725887222397812f;  // 40 ln 2
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float expn(float x) { return ex2(x * kLog2e); }
+__device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
+
+// ---- raw buffer access: per-lane byte offset in a VGPR, per-row offset in an SGPR ----
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base) {
+    // stride 0, maximal record count; word 3 = 0x00020000 selects the 32-bit raw format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+__device__ __forceinline__ float bload(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void bstore(rsrc_t r, float x, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------------------------
+// Carry (a, b, P), base 2.
+// ---------------------------------------------------------------------------------
+struct Carry {
+    float a, b;
+    double P;
+};
+
+// c <- c decayed by 2^{-dec}, plus a summary (al, be) at scale 2^{sc}. The larger of the
+// two scales becomes the new one, so every factor applied is <= 1.
+__device__ __forceinline__ void fold(Carry &c, float al, float be, double sc, double dec) {
+    const double Pd = c.P - dec;
+    const float d = (float)(sc - Pd);
+    const float f = ex2(-fabsf(d));
+    const bool up = d >= 0.0f;
+    const float ca = up ? f : 1.0f;
+    const float cs = up ? 1.0f : f;
+    c.a = fmaf(c.a, ca, al * cs);
+    c.b = fmaf(c.b, ca, be * cs);
+    c.P = up ? sc : Pd;
+}
+
+// ---------------------------------------------------------------------------------
+// Rs (a, b, p), natural log-scale, per token.
+// ---------------------------------------------------------------------------------
+struct Rs {
+    float a, b, p;
+};
+
+// Output for token (k, v) from the state before it:
+//   y = (e^p a + e^{u+k} v) / (e^p b + e^{u+k}), evaluated with the larger exponent as 0.
+__device__ __forceinline__ float rs_out(const Rs &s, float k, float v, float u) {
+    const float uk = u + k;
+    const float d = s.p - uk;
+    const float e = expn(-fabsf(d));
+    const bool sp = d >= 0.0f;
+    const float e1 = sp ? 1.0f : e;
+    const float e2 = sp ? e : 1.0f;
+    return fmaf(e1, s.a, e2 * v) / fmaf(e1, s.b, e2);
+}
+
+// Per-channel decay constants for rs_push.
+struct Decay {
+    float w;      // the rate
+    float dwf;    // e^{-w}
+    float omw;    // 1 - e^{-w}, accurate for small w
+    bool small;   // apply the decay as a - a*omw (small w) or a*dwf (large w)
+};
+
+__device__ __forceinline__ Decay make_decay(float w) {
+    Decay d;
+    d.w = w;
+    d.dwf = expf(-w);
+    d.omw = -expm1f(-w);
+    d.small = w < 0.5f;
+    return d;
+}
+
+// Advance the state by token (k, v): A <- e^{-w} A + e^k v, B <- e^{-w} B + e^k.
+// If k <= p the scale stays and the old sums are decayed in place; otherwise the scale
+// moves to k and the old sums are scaled by e^{p-w-k} <= 1.
+__device__ __forceinline__ void rs_push(Rs &s, float k, float v, const Decay &dc) {
+    const float d = k - s.p;
+    const bool keep = d <= 0.0f;
+    const float e = expn(keep ? d : -(d + dc.w));
+    const float ka = dc.small ? fmaf(-s.a, dc.omw, s.a) : s.a * dc.dwf;
+    const float kb = dc.small ? fmaf(-s.b, dc.omw, s.b) : s.b * dc.dwf;
+    const float ad = keep ? ka : s.a * e;
+    const float bd = keep ? kb : s.b * e;
+    const float f = keep ? e : 1.0f;
+    s.a = fmaf(v, f, ad);
+    s.b = bd + f;
+    s.p = keep ? s.p : k;
+    if (s.b < kRenorm) {
+        s.a *= kRenormUp;
+        s.b *= kRenormUp;
+        s.p -= kRenormLn;
+    }
+}
+
+}  // namespace wkvdev

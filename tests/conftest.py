@@ -8,3 +8,22 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def wkv():
+    """The HIP library binding on cuda:0 (GPU tests only; fails loudly without a GPU)."""
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible GPU")
+    import rwkv_linear_attention_forward_amd as m
+    return m
+
+
+@pytest.fixture(scope="session")
+def dev():
+    import torch
+    return torch.device("cuda:0")

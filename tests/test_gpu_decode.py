@@ -1,0 +1,105 @@
+"""GPU parity of wkv_decode_step against the fp64 oracle (marked gpu).
+
+The recursive form of formula (8) ("RWKV解读：在Transformer的时代的新RNN", section 二.3);
+inference takes a token and a state and returns the new state ("RWKV についての調査記録",
+section "RWKVとは？"). States are compared through what is unique about them: the ratio
+a/b (a convex combination of past v) and the log-mass p + ln b; (a e^d, b e^d, p - d)
+is the same state for any d.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import wkv_inputs
+from helpers import assert_wkv_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(dev, a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def test_decode_chain_equals_parallel_form(wkv, dev):
+    import torch
+    x = wkv_inputs.generate("l3b", seed=21, B=3, T=60, C=70, with_dy=False)
+    ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
+    w, u = _t(dev, x["w"]), _t(dev, x["u"])
+    a, b, p = (_t(dev, s) for s in wkv_inputs.empty_decode_state(3, 70))
+    for t in range(60):
+        y = wkv.decode_step(w, u, _t(dev, x["k"][:, t]), _t(dev, x["v"][:, t]), a, b, p)
+        torch.cuda.synchronize()
+        assert_wkv_close(y.cpu().numpy(), ref[:, t], "t=%d" % t)
+
+
+@pytest.mark.parametrize("layer,B,steps", [(0, 256, 100), (39, 256, 100), (7, 8, 1000)])
+def test_batched_decode_workload(wkv, dev, layer, B, steps):
+    """Full-width layer states; the 1000-step case covers the whole decode horizon."""
+    import torch
+    C = wkv_inputs.DECODE["C"]
+    wn, un = wkv_inputs.decode_layer_params(layer)
+    w, u = _t(dev, wn), _t(dev, un)
+    st = wkv_inputs.empty_decode_state(B, C)
+    a, b, p = (_t(dev, s) for s in st)
+    ost = st
+    worst = 0.0
+    for s in range(steps):
+        kn, vn = wkv_inputs.decode_step_inputs(s, layer, B=B)
+        y = wkv.decode_step(w, u, _t(dev, kn), _t(dev, vn), a, b, p)
+        yr, ost = oracle.decode_step(wn, un, kn, vn, ost)
+        torch.cuda.synchronize()
+        worst = max(worst, assert_wkv_close(y.cpu().numpy(), yr, "layer %d step %d" % (layer, s)))
+    ga, gb, gp = (t.cpu().numpy().astype(np.float64) for t in (a, b, p))
+    oa, ob, op = ost
+    assert_wkv_close(ga / gb, oa / ob, "state ratio")
+    np.testing.assert_allclose(gp + np.log(gb), op + np.log(ob), rtol=0, atol=1e-4)
+    print("[decode] layer %d steps %d max_violation=%.3g" % (layer, steps, worst), flush=True)
+
+
+def test_resume_through_host_is_bitwise(wkv, dev):
+    import torch
+    x = wkv_inputs.generate("l3b", seed=22, B=4, T=20, C=256, with_dy=False)
+    w, u = _t(dev, x["w"]), _t(dev, x["u"])
+
+    def run(a, b, p, t0, t1):
+        ys = []
+        for t in range(t0, t1):
+            ys.append(wkv.decode_step(w, u, _t(dev, x["k"][:, t]), _t(dev, x["v"][:, t]), a, b, p))
+        torch.cuda.synchronize()
+        return [y.cpu().numpy() for y in ys]
+
+    st = [_t(dev, s) for s in wkv_inputs.empty_decode_state(4, 256)]
+    y_all = run(*st, 0, 20)
+    st2 = [_t(dev, s) for s in wkv_inputs.empty_decode_state(4, 256)]
+    y1 = run(*st2, 0, 9)
+    host = [s.cpu().numpy() for s in st2]
+    st3 = [_t(dev, s) for s in host]
+    y2 = run(*st3, 9, 20)
+    for g, r in zip(y1 + y2, y_all):
+        assert np.array_equal(g, r)
+    for s, r in zip(st3, st):
+        assert np.array_equal(s.cpu().numpy(), r.cpu().numpy())
+
+
+def test_sentinels_and_large_keys(wkv, dev):
+    import torch
+    B, C = 2, 64
+    rng = np.random.default_rng(23)
+    w = np.exp(rng.uniform(-8, 2, C)).astype(np.float32)
+    u = rng.uniform(-1, 1, C).astype(np.float32)
+    a = np.zeros((B, C), np.float32)
+    b = np.zeros((B, C), np.float32)
+    p = np.full((B, C), -np.inf, np.float32)
+    p[0] = -1e38
+    ta, tb, tp = _t(dev, a), _t(dev, b), _t(dev, p)
+    st = (a.astype(np.float64), b.astype(np.float64), np.full((B, C), -1e38))
+    for s in range(40):
+        k = (rng.standard_normal((B, C)) * (1000.0 if s % 7 == 3 else 3.0)).astype(np.float32)
+        v = rng.standard_normal((B, C)).astype(np.float32)
+        y = wkv.decode_step(_t(dev, w), _t(dev, u), _t(dev, k), _t(dev, v), ta, tb, tp)
+        yr, st = oracle.decode_step(w, u, k, v, st)
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy()
+        assert np.all(np.isfinite(yg))
+        assert_wkv_close(yg, yr, "step %d" % s, rtol=2e-3)

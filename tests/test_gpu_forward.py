@@ -1,0 +1,101 @@
+"""GPU parity of wkv_forward against the fp64 oracle (marked gpu).
+
+Tolerance: |y - y_oracle| <= 1e-4 * max(|y_oracle|, 0.1) elementwise, and no inf/NaN.
+Operator: "RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (8).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import wkv_inputs
+from helpers import assert_wkv_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_forward(wkv, dev, x, saved=False):
+    import torch
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(dev) for n in ("w", "u", "k", "v")}
+    sv = None
+    if saved:
+        B, T, C = x["k"].shape
+        sv = wkv.new_saved(B, T, C, dev)
+    y = wkv.forward(t["w"], t["u"], t["k"], t["v"], saved=sv)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), (None if sv is None else sv.cpu().numpy())
+
+
+def _log(name, x, v):
+    print("[forward] %s shape=%s max_violation=%.3g" % (name, x["k"].shape, v), flush=True)
+
+
+def test_small_workload(wkv, dev):
+    x = wkv_inputs.generate("small")
+    y, _ = _gpu_forward(wkv, dev, x)
+    ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
+    _log("small", x, assert_wkv_close(y, ref, "small"))
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 37, 70), (3, 300, 130), (1, 257, 64),
+                                   (2, 513, 65), (1, 1000, 5), (4, 31, 200), (1, 2049, 3)])
+def test_ragged_shapes(wkv, dev, B, T, C):
+    x = wkv_inputs.generate("l3b", seed=7 + B * T + C, B=B, T=T, C=C)
+    y, _ = _gpu_forward(wkv, dev, x)
+    ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
+    _log("ragged", x, assert_wkv_close(y, ref, "B=%d T=%d C=%d" % (B, T, C)))
+
+
+@pytest.mark.parametrize("name", ["l169m", "l3b", "longctx"])
+def test_full_workloads(wkv, dev, name):
+    x = wkv_inputs.generate(name, with_dy=False)
+    y, _ = _gpu_forward(wkv, dev, x)
+    ref = oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
+    _log(name, x, assert_wkv_close(y, ref, name))
+
+
+def test_saved_carries_do_not_change_y_and_determinism(wkv, dev):
+    x = wkv_inputs.generate("longctx", B=2, T=1500, C=192, with_dy=False)
+    y0, _ = _gpu_forward(wkv, dev, x)
+    y1, sv = _gpu_forward(wkv, dev, x, saved=True)
+    y2, sv2 = _gpu_forward(wkv, dev, x, saved=True)
+    assert np.array_equal(y0, y1) and np.array_equal(y1, y2)
+    assert np.array_equal(sv, sv2)
+
+
+@pytest.mark.parametrize("kscale,spike", [(8.0, 0.0), (20.0, 80.0), (1.0, 1000.0),
+                                          (300.0, 0.0)])
+def test_large_keys_stay_finite(wkv, dev, kscale, spike):
+    rng = np.random.default_rng(int(kscale * 10 + spike))
+    B, T, C = 2, 400, 96
+    x = wkv_inputs.generate("l3b", seed=11, B=B, T=T, C=C, with_dy=False)
+    k = (x["k"] * np.float32(kscale)).astype(np.float32)
+    if spike:
+        m = rng.random((B, T, C)) < 0.02
+        k = np.where(m, np.float32(spike) * np.sign(rng.standard_normal((B, T, C))), k)
+    x["k"] = k.astype(np.float32)
+    y, _ = _gpu_forward(wkv, dev, x)
+    assert np.all(np.isfinite(y))
+    ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
+    # |k| near 1e3 has an input ulp of 6e-5, so only the looser bound is meaningful there
+    rtol = 1e-4 if max(kscale * 5, spike) < 200 else 2e-3
+    _log("large-k %g/%g" % (kscale, spike), x, assert_wkv_close(y, ref, "large k", rtol=rtol))
+    lo = np.minimum.accumulate(x["v"], axis=1)
+    hi = np.maximum.accumulate(x["v"], axis=1)
+    assert np.all(y >= lo - 1e-5) and np.all(y <= hi + 1e-5)
+
+
+@pytest.mark.parametrize("case", ["u_big", "u_huge", "w_fast", "w_slow"])
+def test_parameter_extremes(wkv, dev, case):
+    B, T, C = 2, 600, 128
+    x = wkv_inputs.generate("l3b", seed=13, B=B, T=T, C=C, with_dy=False)
+    if case == "u_big":
+        x["u"] = np.linspace(-50, 50, C).astype(np.float32)
+    elif case == "u_huge":
+        x["u"] = np.linspace(-200, 200, C).astype(np.float32)
+    elif case == "w_fast":
+        x["w"] = np.linspace(5, 200, C).astype(np.float32)
+    else:
+        x["w"] = np.geomspace(1e-7, 1e-3, C).astype(np.float32)
+    y, _ = _gpu_forward(wkv, dev, x)
+    ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
+    _log(case, x, assert_wkv_close(y, ref, case))
