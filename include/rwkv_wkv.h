@@ -55,36 +55,39 @@ const char *wkv_status_string(int status);
 /* Message of the last failing call made by this thread ("" if none). Never NULL. */
 const char *wkv_last_error(void);
 
-/* Bytes of the optional carry buffer that wkv_forward can fill for wkv_backward: the
- * recurrent state (the two sums of the recursive form and their scale) at every 256-token
- * boundary of every (b, c) sequence, 16 bytes each. Its content is opaque and only valid
- * for the same B, T, C, w, k, v. Returns 0 for invalid dims. */
-size_t wkv_saved_size(int64_t B, int64_t T, int64_t C);
+/* Bytes of device scratch that wkv_forward needs for (B, T, C): publication flags plus,
+ * for every (b, c) sequence and every 256-token window, the window's aggregate and the
+ * recurrent state after it (the two sums of the recursive form with their scale), 32 bytes
+ * per window. Returns 0 for invalid dims. */
+size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 
 /* Forward: y [B][T][C] from k, v [B][T][C] and w, u [C], starting from the empty state
  * (formula (8) of "RWKV解读：在Transformer的时代的新RNN", section 二.3).
- * `saved` may be NULL; otherwise it must hold at least wkv_saved_size(B, T, C) bytes
- * (`saved_bytes`) and receives the carries that let wkv_backward skip its own pass over
- * k and v. Requires B*T*C < 2^62, C <= 2^24 and B*ceil(C/64) < 2^31. */
+ * `workspace` (16-byte aligned, at least wkv_forward_workspace_size(B, T, C) bytes given in
+ * `workspace_bytes`) is required whenever B*T*C > 0; its previous content is ignored. After
+ * the call it holds the states at window boundaries, which wkv_backward can reuse to skip
+ * its own pass over k and v; it must not be used by two calls at the same time.
+ * Requires C <= 2^24 and B*ceil(C/64)*ceil(T/256) < 2^31. */
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                const float *k, const float *v, float *y, void *saved, size_t saved_bytes,
-                void *stream);
+                const float *k, const float *v, float *y, void *workspace,
+                size_t workspace_bytes, void *stream);
 
-/* Bytes of device scratch that wkv_backward needs. With have_saved != 0 the caller will
- * pass the buffer filled by wkv_forward; with have_saved == 0 the carries are recomputed
- * into the workspace, which then also covers wkv_saved_size(B, T, C). */
-size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_saved);
+/* Bytes of device scratch that wkv_backward needs. With have_fwd_workspace != 0 the caller
+ * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
+ * window states are recomputed into this workspace, which then also covers
+ * wkv_forward_workspace_size(B, T, C). */
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace);
 
 /* Backward of L = sum_{b,t,c} dy[b,t,c] * y[b,t,c] ("RWKV についての調査記録", section
  * "Trainingについて": all parameters get gradients): dk, dv [B][T][C] and dw, du [C],
  * where dw and du are summed over b and t and overwritten (not accumulated). dw is the
  * gradient with respect to w itself (a caller that stores d = log w uses w * dw).
- * `saved` is NULL or the buffer wkv_forward filled for the same inputs. `workspace`
- * must hold wkv_backward_workspace_size(B, T, C, saved != NULL) bytes (`workspace_bytes`),
- * be 256-byte aligned, and is clobbered. dw and du are computed in a fixed order and
- * are bitwise reproducible run to run. */
+ * `fwd_workspace` is NULL or the workspace wkv_forward filled for the same B, T, C, w, u,
+ * k, v (it is only read). `workspace` (16-byte aligned, wkv_backward_workspace_size(B, T,
+ * C, fwd_workspace != NULL) bytes given in `workspace_bytes`) is clobbered. dw and du are
+ * summed in a fixed order and are bitwise reproducible run to run. */
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                 const float *k, const float *v, const float *dy, const void *saved,
+                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream);
 

@@ -7,9 +7,9 @@ been built; there is no CPU fallback.
 
 Entry points mirror the C ABI in include/rwkv_wkv.h:
 
-    forward(w, u, k, v, saved=None) -> y
-    saved_size(B, T, C) -> int
-    backward(w, u, k, v, dy, saved=None) -> (dk, dv, dw, du)
+    forward(w, u, k, v, workspace=None) -> y
+    forward_workspace(B, T, C, device) -> uint8 tensor sized for the forward
+    backward(w, u, k, v, dy, fwd_workspace=None) -> (dk, dv, dw, du)
     decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
 
 Operator ("RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (8)):
@@ -32,7 +32,7 @@ WKV_ERR_UNSUPPORTED = 2
 WKV_ERR_HIP = 3
 
 # Every symbol the header declares, for the export check.
-EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_saved_size",
+EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
            "wkv_forward", "wkv_backward_workspace_size", "wkv_backward", "wkv_decode_step")
 
 _lib = None
@@ -55,8 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_last_error.restype = ctypes.c_char_p
     lib.wkv_last_error.argtypes = []
-    lib.wkv_saved_size.restype = ctypes.c_size_t
-    lib.wkv_saved_size.argtypes = [_I64, _I64, _I64]
+    lib.wkv_forward_workspace_size.restype = ctypes.c_size_t
+    lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
     lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_backward_workspace_size.restype = ctypes.c_size_t
@@ -124,50 +124,63 @@ def _check_btc(w, u, k, v):
     return B, T, C, dev
 
 
-def saved_size(B: int, T: int, C: int) -> int:
-    """Bytes of the carry buffer wkv_forward can fill for wkv_backward."""
-    return int(load_library().wkv_saved_size(B, T, C))
+def forward_workspace_size(B: int, T: int, C: int) -> int:
+    """Bytes of scratch wkv_forward needs (it also keeps the states wkv_backward reuses)."""
+    return int(load_library().wkv_forward_workspace_size(B, T, C))
 
 
-def new_saved(B: int, T: int, C: int, device) -> torch.Tensor:
-    """A uint8 device tensor large enough for the forward's saved carries."""
-    return torch.empty(max(1, saved_size(B, T, C)), dtype=torch.uint8, device=device)
+def forward_workspace(B: int, T: int, C: int, device) -> torch.Tensor:
+    """A uint8 device tensor sized for wkv_forward."""
+    return torch.empty(max(16, forward_workspace_size(B, T, C)), dtype=torch.uint8,
+                       device=device)
 
 
-def forward(w, u, k, v, saved=None, out=None):
-    """y [B,T,C] = WKV(w, u, k, v); fills `saved` (uint8 tensor) if given."""
+def _check_ws(ws, dev, name):
+    if ws.dtype != torch.uint8 or ws.device != dev or not ws.is_contiguous():
+        raise ValueError("%s must be a contiguous uint8 tensor on %s" % (name, dev))
+
+
+def forward(w, u, k, v, workspace=None, out=None):
+    """y [B,T,C] = WKV(w, u, k, v). `workspace` (uint8, forward_workspace_size bytes) is
+    allocated if not given; after the call it holds the states backward() can reuse."""
     B, T, C, dev = _check_btc(w, u, k, v)
     y = torch.empty_like(k) if out is None else out
     _need(y, "out", 3, dev)
     if y.shape != k.shape:
         raise ValueError("out has the wrong shape")
-    sbytes = 0
-    if saved is not None:
-        if saved.dtype != torch.uint8 or saved.device != dev or not saved.is_contiguous():
-            raise ValueError("saved must be a contiguous uint8 tensor on %s" % dev)
-        sbytes = saved.numel()
+    if workspace is None:
+        workspace = forward_workspace(B, T, C, dev)
+    _check_ws(workspace, dev, "workspace")
     _check(load_library().wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                      _ptr(saved), sbytes, _stream(dev)))
+                                      _ptr(workspace), workspace.numel(), _stream(dev)))
     return y
 
 
-def backward(w, u, k, v, dy, saved=None, workspace=None):
-    """(dk, dv, dw, du) of sum(dy * y); `saved` from forward() for the same inputs."""
+def backward_workspace_size(B: int, T: int, C: int, have_fwd_workspace: bool) -> int:
+    return int(load_library().wkv_backward_workspace_size(B, T, C, 1 if have_fwd_workspace else 0))
+
+
+def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None):
+    """(dk, dv, dw, du) of sum(dy * y). `fwd_workspace` is the workspace forward() filled for
+    the same inputs (optional: without it the window states are recomputed)."""
     B, T, C, dev = _check_btc(w, u, k, v)
     _need(dy, "dy", 3, dev)
     if dy.shape != k.shape:
         raise ValueError("dy has the wrong shape")
+    if fwd_workspace is not None:
+        _check_ws(fwd_workspace, dev, "fwd_workspace")
     lib = load_library()
-    wsz = int(lib.wkv_backward_workspace_size(B, T, C, 1 if saved is not None else 0))
+    wsz = backward_workspace_size(B, T, C, fwd_workspace is not None)
     if workspace is None or workspace.numel() < wsz:
-        workspace = torch.empty(max(1, wsz), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
+    _check_ws(workspace, dev, "workspace")
     dk = torch.empty_like(k)
     dv = torch.empty_like(k)
     dw = torch.empty_like(w)
     du = torch.empty_like(u)
-    _check(lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy), _ptr(saved),
-                            _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(workspace),
-                            workspace.numel(), _stream(dev)))
+    _check(lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                            _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
+                            _ptr(workspace), workspace.numel(), _stream(dev)))
     return dk, dv, dw, du
 
 
@@ -191,20 +204,20 @@ def decode_step(w, u, k, v, a, b, p, out=None):
 
 
 class WKV(torch.autograd.Function):
-    """Autograd wrapper: y = WKV(w, u, k, v); the forward keeps its carries for backward."""
+    """Autograd wrapper: y = WKV(w, u, k, v); the forward's workspace is kept for backward."""
 
     @staticmethod
     def forward(ctx, w, u, k, v):
         B, T, C = k.shape
-        saved = new_saved(B, T, C, k.device)
-        y = forward(w, u, k, v, saved=saved)
-        ctx.save_for_backward(w, u, k, v, saved)
+        ws = forward_workspace(B, T, C, k.device)
+        y = forward(w, u, k, v, workspace=ws)
+        ctx.save_for_backward(w, u, k, v, ws)
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        w, u, k, v, saved = ctx.saved_tensors
-        dk, dv, dw, du = backward(w, u, k, v, dy.contiguous(), saved=saved)
+        w, u, k, v, ws = ctx.saved_tensors
+        dk, dv, dw, du = backward(w, u, k, v, dy.contiguous(), fwd_workspace=ws)
         return dw, du, dk, dv
 
 

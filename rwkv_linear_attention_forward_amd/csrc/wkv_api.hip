@@ -7,8 +7,11 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <atomic>
+#include <chrono>
 #include <cstring>
 #include <mutex>
+#include <random>
 
 #include "../../include/rwkv_wkv.h"
 #include "wkv_launch.h"
@@ -107,13 +110,79 @@ int check_device(const char *fn) {
     return WKV_OK;
 }
 
-int64_t nsave_of(int64_t T) { return (T + wkvdev::kSaveStride - 1) / wkvdev::kSaveStride; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t saved_bytes_of(int64_t B, int64_t T, int64_t C) {
-    return (size_t)B * (size_t)nsave_of(T) * (size_t)C * 16u;
+int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
+
+// Forward workspace: flags, aggregates, inclusive carries (see wkv_launch.h).
+size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
+    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256);
 }
 
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
+    wkvdev::FwdLayout L;
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
+    char *p = static_cast<char *>(ws);
+    L.nseg = (int64_t)nseg;
+    L.flags = reinterpret_cast<uint64_t *>(p);
+    p += round_up((size_t)B * ngrp * nseg * 8u, 256);
+    L.agg = reinterpret_cast<wkvdev::Rec *>(p);
+    p += round_up(recs, 256);
+    L.incl = reinterpret_cast<wkvdev::Rec *>(p);
+    return L;
+}
+
+// Backward workspace: flags, reverse aggregates, reverse inclusive carries, per-window dw/du
+// partials, then (without a forward workspace) a forward workspace of its own.
+size_t bwd_own_bytes(int64_t B, int64_t T, int64_t C) {
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t n = (size_t)B * nseg * (size_t)C;
+    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(n * sizeof(wkvdev::RevRec), 256) +
+           round_up(n * 2 * sizeof(double), 256);
+}
+
+wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
+    wkvdev::BwdLayout L;
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t n = (size_t)B * nseg * (size_t)C;
+    char *p = static_cast<char *>(ws);
+    L.nseg = (int64_t)nseg;
+    L.flags = reinterpret_cast<uint64_t *>(p);
+    p += round_up((size_t)B * ngrp * nseg * 8u, 256);
+    L.ragg = reinterpret_cast<wkvdev::RevRec *>(p);
+    p += round_up(n * sizeof(wkvdev::RevRec), 256);
+    L.rincl = reinterpret_cast<wkvdev::RevRec *>(p);
+    p += round_up(n * sizeof(wkvdev::RevRec), 256);
+    L.part = reinterpret_cast<double *>(p);
+    return L;
+}
+
+// Publication epochs: unique per call, seeded randomly per process so that flags left in a
+// reused buffer by another process or an earlier call never match.
+std::atomic<uint64_t> g_epoch{0};
+std::once_flag g_epoch_once;
+
+uint64_t next_epoch() {
+    std::call_once(g_epoch_once, [] {
+        std::random_device rd;
+        const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+        const uint64_t seed = (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull));
+        g_epoch.store(seed & ((uint64_t(1) << 60) - 1));
+    });
+    return (g_epoch.fetch_add(1) + 1) & ((uint64_t(1) << 61) - 1);
+}
+
+bool grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
+    const int64_t units = B * ((C + 63) / 64) * nseg_of(T);
+    if (units > INT32_MAX) {
+        fail(WKV_ERR_INVALID_ARG, "%s: %lld workgroups exceed 2^31-1", fn, (long long)units);
+        return false;
+    }
+    return true;
+}
 
 }  // namespace
 
@@ -133,70 +202,116 @@ const char *wkv_status_string(int status) {
 
 const char *wkv_last_error(void) { return g_err; }
 
-size_t wkv_saved_size(int64_t B, int64_t T, int64_t C) {
+size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0 || C > kMaxC) return 0;
     if (B > 0 && T > 0 && C > 0 && (T > kMaxElems / B || B * T > kMaxElems / C)) return 0;
-    return saved_bytes_of(B, T, C);
+    return fwd_ws_bytes(B, T, C);
 }
 
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                const float *k, const float *v, float *y, void *saved, size_t saved_bytes,
-                void *stream) {
+                const float *k, const float *v, float *y, void *workspace,
+                size_t workspace_bytes, void *stream) {
     static const char *fn = "wkv_forward";
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    if (!grid_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (!nonnull(w, "w", fn) || !nonnull(u, "u", fn) || !nonnull(k, "k", fn) ||
-        !nonnull(v, "v", fn) || !nonnull(y, "y", fn))
+        !nonnull(v, "v", fn) || !nonnull(y, "y", fn) || !nonnull(workspace, "workspace", fn))
         return WKV_ERR_INVALID_ARG;
     if (!aligned(w, 4, "w", fn) || !aligned(u, 4, "u", fn) || !aligned(k, 4, "k", fn) ||
-        !aligned(v, 4, "v", fn) || !aligned(y, 4, "y", fn))
+        !aligned(v, 4, "v", fn) || !aligned(y, 4, "y", fn) ||
+        !aligned(workspace, 16, "workspace", fn))
         return WKV_ERR_INVALID_ARG;
     const size_t nb = (size_t)(B * T * C) * 4u;
+    const size_t need = fwd_ws_bytes(B, T, C);
+    if (workspace_bytes < need)
+        return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
     if (overlap(y, nb, k, nb) || overlap(y, nb, v, nb) || overlap(y, nb, w, C * 4u) ||
         overlap(y, nb, u, C * 4u))
         return fail(WKV_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
-    float *sva = nullptr, *svb = nullptr;
-    double *svP = nullptr;
-    if (saved != nullptr) {
-        const size_t need = saved_bytes_of(B, T, C);
-        if (saved_bytes < need)
-            return fail(WKV_ERR_INVALID_ARG, "%s: saved buffer has %zu bytes, needs %zu", fn,
-                        saved_bytes, need);
-        if (!aligned(saved, 8, "saved", fn)) return WKV_ERR_INVALID_ARG;
-        if (overlap(saved, need, y, nb) || overlap(saved, need, k, nb) || overlap(saved, need, v, nb))
-            return fail(WKV_ERR_INVALID_ARG, "%s: saved overlaps a tensor", fn);
-        const size_t n = (size_t)B * (size_t)nsave_of(T) * (size_t)C;
-        sva = static_cast<float *>(saved);
-        svb = sva + n;
-        svP = reinterpret_cast<double *>(svb + n);
-    }
+    if (overlap(workspace, need, y, nb) || overlap(workspace, need, k, nb) ||
+        overlap(workspace, need, v, nb) || overlap(workspace, need, w, C * 4u) ||
+        overlap(workspace, need, u, C * 4u))
+        return fail(WKV_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
-    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, y, sva, svb, svP,
-                                          static_cast<hipStream_t>(stream));
+    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, y, fwd_layout(B, T, C, workspace),
+                                          next_epoch(), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
 }
 
-size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_saved) {
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace) {
     if (B < 0 || T < 0 || C < 0 || C > kMaxC) return 0;
     if (B > 0 && T > 0 && C > 0 && (T > kMaxElems / B || B * T > kMaxElems / C)) return 0;
-    size_t ws = round_up((size_t)B * (size_t)C * 16u, 256);
-    if (!have_saved) ws += round_up(saved_bytes_of(B, T, C), 256);
+    size_t ws = bwd_own_bytes(B, T, C);
+    if (!have_fwd_workspace) ws += fwd_ws_bytes(B, T, C);
     return ws;
 }
 
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                 const float *k, const float *v, const float *dy, const void *saved,
+                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream) {
     static const char *fn = "wkv_backward";
     g_err[0] = '\0';
-    (void)w; (void)u; (void)k; (void)v; (void)dy; (void)saved; (void)dk; (void)dv;
-    (void)dw; (void)du; (void)workspace; (void)workspace_bytes; (void)stream;
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
-    return fail(WKV_ERR_UNSUPPORTED, "%s: not built in this version", fn);
+    if (C == 0) return WKV_OK;
+    if (!nonnull(dw, "dw", fn) || !nonnull(du, "du", fn)) return WKV_ERR_INVALID_ARG;
+    if (!aligned(dw, 4, "dw", fn) || !aligned(du, 4, "du", fn)) return WKV_ERR_INVALID_ARG;
+    if (overlap(dw, C * 4u, du, C * 4u)) return fail(WKV_ERR_INVALID_ARG, "%s: dw overlaps du", fn);
+    if (B == 0 || T == 0) {
+        int rc = check_device(fn);
+        if (rc != WKV_OK) return rc;
+        hipError_t e = wkvdev::launch_zero2(dw, du, C, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, fn);
+        return WKV_OK;
+    }
+    if (!grid_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    const void *ptrs[9] = {w, u, k, v, dy, dk, dv, workspace, nullptr};
+    const char *names[9] = {"w", "u", "k", "v", "dy", "dk", "dv", "workspace", ""};
+    for (int i = 0; i < 8; ++i)
+        if (!nonnull(ptrs[i], names[i], fn)) return WKV_ERR_INVALID_ARG;
+    for (int i = 0; i < 7; ++i)
+        if (!aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
+    if (!aligned(workspace, 16, "workspace", fn)) return WKV_ERR_INVALID_ARG;
+    if (fwd_workspace != nullptr && !aligned(fwd_workspace, 16, "fwd_workspace", fn))
+        return WKV_ERR_INVALID_ARG;
+    const size_t need = wkv_backward_workspace_size(B, T, C, fwd_workspace != nullptr);
+    if (workspace_bytes < need)
+        return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    const size_t nb = (size_t)(B * T * C) * 4u, nc = (size_t)C * 4u;
+    const void *outs[5] = {dk, dv, dw, du, workspace};
+    const size_t osz[5] = {nb, nb, nc, nc, need};
+    const void *ins[6] = {w, u, k, v, dy, fwd_workspace};
+    const size_t isz[6] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], osz[i], ins[j], isz[j]))
+                return fail(WKV_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], osz[i], outs[j], osz[j]))
+                return fail(WKV_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    }
+    int rc = check_device(fn);
+    if (rc != WKV_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    wkvdev::FwdLayout F;
+    char *own = static_cast<char *>(workspace);
+    if (fwd_workspace != nullptr) {
+        F = fwd_layout(B, T, C, const_cast<void *>(fwd_workspace));
+    } else {
+        F = fwd_layout(B, T, C, own + bwd_own_bytes(B, T, C));
+        hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, F, next_epoch(), st);
+        if (e != hipSuccess) return fail_hip(e, fn);
+    }
+    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, F.incl, dk, dv, dw, du,
+                                           bwd_layout(B, T, C, own), next_epoch(), st);
+    if (e != hipSuccess) return fail_hip(e, fn);
+    return WKV_OK;
 }
 
 int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,

@@ -50,10 +50,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base) {
                                              0x00020000);
 }
 __device__ __forceinline__ float bload(rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2));
 }
 __device__ __forceinline__ void bstore(rsrc_t r, float x, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 2);
 }
 
 // ---------------------------------------------------------------------------------
@@ -76,6 +76,17 @@ __device__ __forceinline__ void fold(Carry &c, float al, float be, double sc, do
     c.a = fmaf(c.a, ca, al * cs);
     c.b = fmaf(c.b, ca, be * cs);
     c.P = up ? sc : Pd;
+}
+
+// Move a carry's scale so that b lies in [1, 2) (exact: a power-of-two rescale), so that
+// the scale P says how large the mass is. Empty carries are left alone.
+__device__ __forceinline__ void normalize(Carry &c) {
+    if (c.b > 0.0f) {
+        const int e = __builtin_amdgcn_frexp_expf(c.b) - 1;
+        c.a = ldexpf(c.a, -e);
+        c.b = ldexpf(c.b, -e);
+        c.P += (double)e;
+    }
 }
 
 // ---------------------------------------------------------------------------------

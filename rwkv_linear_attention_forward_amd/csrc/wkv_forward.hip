@@ -1,25 +1,32 @@
-// wkv_forward.hip -- WKV forward on gfx950: chunked time scan, one lane per (b, c).
+// wkv_forward.hip -- WKV forward on gfx950: time-split chunked scan with decoupled look-back.
 //
 // Operator: "RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (8), evaluated
 // through its recursive form (same section) as an associative scan over time, which is
 // possible because the decay w does not depend on the data ("RWKV についての調査記録",
 // section "Trainingについて").
 //
-// Work decomposition. A workgroup owns 64 channels of one sequence and NW waves; it walks
-// the sequence in windows of NW*CH tokens, wave q taking the q-th CH-token chunk of each
-// window. Each lane streams its channel's k and v rows (one dword per token, 256 B per
-// wave per token, coalesced along C) into registers, so k and v are read from HBM exactly
-// once and y is written exactly once: 12 bytes per element.
+// Work decomposition. One workgroup = one unit = 64 channels x one window of WIN = NW*CH
+// tokens of one sequence; wave q owns the q-th CH-token chunk of the window, one lane per
+// channel. Units are numbered window-major (all units of window 0 first), so a unit's
+// predecessor in time was launched earlier; there are B * ceil(C/64) * ceil(T/WIN) units,
+// many more than CUs, which keeps all 256 CUs evenly busy even when B*C is small.
+// k and v are streamed once with non-temporal loads (one dword per lane per token, 256 B
+// per wave per token, coalesced along C) and y is written once: 12 bytes per element.
 //
 // Per chunk, with frame ref = max_j k_j of the lane's chunk and e_j = e^{k_j - ref} <= 1:
 //   phase 1  summary from the empty state: S = sum_j e^{-(CH-1-j)w} e_j v_j, Z likewise
-//            without v (Horner with the fp32 factor e^{-w}; at most CH steps, so its
+//            without v (Horner with the fp32 factor e^{-w}: at most CH steps, so its
 //            rounding cannot compound); the chunk adds S 2^{ref log2 e} to A and Z to B.
-//   scan     summaries go to LDS; after one barrier every wave folds the NW summaries of
-//            the window into the window's incoming carry in order, keeping its own
-//            incoming carry on the way (identical arithmetic in every wave, so the
-//            window's outgoing carry needs no second barrier). Carries keep their
+//   window   summaries go to LDS; after one barrier every wave folds the NW summaries in
+//            order from the empty state (identical arithmetic in every wave), giving its own
+//            chunk's local incoming carry and the window aggregate. Carries keep their
 //            log-scale in fp64 (see wkv_device.h).
+//   look-back  the aggregate is published; the carry entering the window is then the fold
+//            of the nearest predecessor's published inclusive carry and the aggregates in
+//            between (a predecessor that has not published within a bounded wait has its
+//            aggregate recomputed from k, v here, so no unit ever blocks on another). The
+//            window's inclusive carry is published for its successors and kept for the
+//            backward pass.
 //   phase 3  outputs from the incoming carry put into the chunk frame:
 //            y_j = (S_j + e^u e_j v_j) / (Z_j + e^u e_j),  S_{j+1} = e^{-w} S_j + e_j v_j.
 // One exp2 per element in each phase, one reciprocal in phase 3.
@@ -29,64 +36,28 @@
 // by 2^64. Such chunks (rare; only far outside the training distributions) are detected
 // per wave and recomputed with the per-token rescaled recursion (Rs in wkv_device.h),
 // which is safe for any finite k.
-#include "wkv_device.h"
-#include "wkv_launch.h"
+#include "wkv_chunk.h"
 
 namespace wkvdev {
 
-// Load a CH-token chunk of one lane's channel starting at token t0 (rows past T are 0).
-template <int CH>
-__device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
-                                           const float *__restrict__ k,
-                                           const float *__restrict__ v, int64_t row0,
-                                           int64_t t0, int64_t T, int64_t C, int voff) {
-    if (t0 >= T) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            kc[j] = 0.0f;
-            vc[j] = 0.0f;
-        }
-        return;
-    }
-    const rsrc_t rk = make_rsrc(k + (row0 + t0) * C);
-    const rsrc_t rv = make_rsrc(v + (row0 + t0) * C);
-    const int stride = (int)(C * 4);
-    if (t0 + CH <= T) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            kc[j] = bload(rk, voff, j * stride);
-            vc[j] = bload(rv, voff, j * stride);
-        }
-    } else {
-        const int Lv = (int)(T - t0);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            if (j < Lv) {
-                kc[j] = bload(rk, voff, j * stride);
-                vc[j] = bload(rv, voff, j * stride);
-            } else {
-                kc[j] = 0.0f;
-                vc[j] = 0.0f;
-            }
-        }
-    }
-}
-
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
-    int64_t T, int64_t C, int ngrp, const float *__restrict__ w, const float *__restrict__ u,
-    const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ y,
-    float *__restrict__ sva, float *__restrict__ svb, double *__restrict__ svP) {
+    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
+    const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
+    const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
+    Rec *__restrict__ agg, Rec *__restrict__ incl) {
     constexpr int WIN = NW * CH;
-    static_assert(kSaveStride % WIN == 0, "window must divide the carry save stride");
-    __shared__ float s_al[2][NW][64];
-    __shared__ float s_be[2][NW][64];
-    __shared__ double s_sc[2][NW][64];
+    __shared__ float s_al[NW][64];
+    __shared__ float s_be[NW][64];
+    __shared__ double s_sc[NW][64];
+    __shared__ int s_status[2];
 
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t bidx = blockIdx.x / ngrp;
-    const int grp = (int)(blockIdx.x - bidx * ngrp);
+    const int64_t s = (int64_t)blockIdx.x / nbg;
+    const int64_t bg = (int64_t)blockIdx.x - s * nbg;
+    const int64_t bidx = bg / ngrp;
+    const int grp = (int)(bg - bidx * ngrp);
     const int64_t c = (int64_t)grp * 64 + lane;
     const bool cval = c < C;
     const int cl = (int)(cval ? c : C - 1);
@@ -95,145 +66,172 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const float wc = w[cl];
     const float uc = u[cl];
     const Decay dc = make_decay(wc);
-    const float dwf = dc.dwf;
     const float eu = expf(uc);
-    const double dec = (double)CH * ((double)wc * kLog2eD);
-    const bool slow_lane = !(fabsf(uc) <= 60.0f);
-    const bool slow_wave = wave_any(slow_lane);
+    const double w2 = (double)wc * kLog2eD;
+    const bool slow_wave = wave_any(!(fabsf(uc) <= 60.0f));
 
     const int64_t row0 = bidx * T;
-    const int64_t nwin = (T + WIN - 1) / WIN;
-    const int64_t nsave = (T + kSaveStride - 1) / kSaveStride;
+    const int64_t t0 = s * WIN + (int64_t)q * CH;
+    const int Lv = (int)(t0 >= T ? 0 : (T - t0 < CH ? T - t0 : CH));
 
-    Carry carry{0.0f, 0.0f, kNegBigD};
+    // ---- phase 1: frame and summary of this wave's chunk ----
     float kc[CH], vc[CH];
-    load_chunk<CH>(kc, vc, k, v, row0, (int64_t)q * CH, T, C, voff);
-    int buf = 0;
+    load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+    const float ref = chunk_ref<CH>(kc, Lv);
+    float S, Z;
+    double sc;
+    bool exact = chunk_summary<CH>(kc, vc, Lv, ref, slow_wave, dc, S, Z, sc);
+    if (exact) {
+        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+        exact_summary<CH>(kc, vc, Lv, ref, dc, S, Z, sc);
+    }
 
-    for (int64_t win = 0; win < nwin; ++win) {
-        const int64_t tw = win * WIN;
-        const int64_t t0 = tw + (int64_t)q * CH;
-        const int Lv = (int)(t0 >= T ? 0 : (T - t0 < CH ? T - t0 : CH));
+    // ---- window: local carries and aggregate ----
+    s_al[q][lane] = S;
+    s_be[q][lane] = Z;
+    s_sc[q][lane] = sc;
+    __syncthreads();
+    Carry run{0.0f, 0.0f, kNegBigD};
+    Carry lexcl = run;
+#pragma unroll
+    for (int qq = 0; qq < NW; ++qq) {
+        if (qq == q) lexcl = run;
+        fold(run, s_al[qq][lane], s_be[qq][lane], s_sc[qq][lane], (double)CH * w2);
+    }
+    const int64_t rec = (bidx * nseg + s) * C + cl;
+    uint64_t *myflag = flags + s * nbg + bg;
+    if (q == 0) {
+        if (cval) put_rec(agg + rec, run);
+        put_flag(myflag, epoch, kAggregate);
+    }
 
-        if (svP != nullptr && q == 0 && cval && (tw % kSaveStride) == 0) {
-            const int64_t si = (bidx * nsave + tw / kSaveStride) * C + c;
-            sva[si] = carry.a;
-            svb[si] = carry.b;
-            svP[si] = carry.P;
+    // ---- look-back: carry entering this window ----
+    // Walk back to the nearest window whose inclusive carry is published (or the sequence
+    // start), making sure every window in between has its aggregate in memory; then fold
+    // those aggregates forward in order. The result is bitwise the sequential chain
+    // incl[s] = fold(incl[s-1], agg[s]) whatever the timing, so every run is deterministic.
+    Carry prefix{0.0f, 0.0f, kNegBigD};
+    bool own_clobbered = false;
+    if (s > 0) {
+        int64_t j = s - 1;
+        int it = 0;
+        for (;;) {
+            if (q == 0) {
+                const int st = poll_flag(flags + j * nbg + bg, epoch, kPollTries);
+                if (lane == 0) s_status[it & 1] = st;
+            }
+            __syncthreads();
+            const int st = s_status[it & 1];
+            ++it;
+            if (st == (int)kInclusive) break;
+            if (st != (int)kAggregate) {
+                // not published in time: compute window j's aggregate here and publish it
+                // (bitwise what unit j itself publishes)
+                const int64_t tj = j * WIN + (int64_t)q * CH;
+                const int Lj = chunk_len(tj, T, CH);
+                load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
+                own_clobbered = true;
+                const float rj = chunk_ref<CH>(kc, Lj);
+                float Sj, Zj;
+                double scj;
+                if (chunk_summary<CH>(kc, vc, Lj, rj, slow_wave, dc, Sj, Zj, scj)) {
+                    load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
+                    exact_summary<CH>(kc, vc, Lj, rj, dc, Sj, Zj, scj);
+                }
+                __syncthreads();
+                s_al[q][lane] = Sj;
+                s_be[q][lane] = Zj;
+                s_sc[q][lane] = scj;
+                __syncthreads();
+                Carry X{0.0f, 0.0f, kNegBigD};
+#pragma unroll
+                for (int qq = 0; qq < NW; ++qq)
+                    fold(X, s_al[qq][lane], s_be[qq][lane], s_sc[qq][lane], (double)CH * w2);
+                if (q == 0) {
+                    if (cval) put_rec(agg + (bidx * nseg + j) * C + cl, X);
+                    raise_flag(flags + j * nbg + bg, epoch, kAggregate);
+                }
+                __syncthreads();
+            }
+            if (j == 0) {
+                j = -1;
+                break;
+            }
+            --j;
         }
+        // j is the window with a published inclusive carry, or -1
+        if (j >= 0) prefix = get_rec(incl + (bidx * nseg + j) * C + cl);
+        for (int64_t m = j + 1; m < s; ++m)
+            prefix = follow(prefix, get_rec(agg + (bidx * nseg + m) * C + cl), (double)WIN * w2);
+    }
+    if (q == 0) {
+        if (cval) put_rec(incl + rec, follow(prefix, run, (double)WIN * w2));
+        put_flag(myflag, epoch, kInclusive);
+    }
+    if (y == nullptr) return;
 
-        float kn[CH], vn[CH];
-        const bool more = win + 1 < nwin;
-        if (more) load_chunk<CH>(kn, vn, k, v, row0, t0 + WIN, T, C, voff);
-
-        // ---- phase 1: frame and summary of this chunk ----
-        float ref = kNegBig;
+    // ---- phase 3: outputs ----
+    Carry mine = follow(prefix, lexcl, (double)(q * CH) * w2);
+    normalize(mine);
+    if (own_clobbered) {
+        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+        if (!exact) {
+            float S2, Z2;
+            double sc2;
+            exact = chunk_summary<CH>(kc, vc, Lv, ref, slow_wave, dc, S2, Z2, sc2);
+            if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+        }
+    }
+    if (!exact) {
+        const float ref2 = ref * kLog2e;
+        const float gap = (float)(mine.P - (double)ref2);
+        bool bad = gap > kCarryGap;
+        const float s0 = ex2(gap);
+        float Sx = mine.a * s0, Zx = mine.b * s0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float e = kc[j], ev = vc[j];
+            const float num = fmaf(eu, ev, Sx);
+            const float den = fmaf(eu, e, Zx);
+            if (j < Lv) bad |= !(den >= kTinyDen);
+            kc[j] = num * rcpf(den);
+            Sx = fmaf(Sx, dc.dwf, ev);
+            Zx = fmaf(Zx, dc.dwf, e);
+        }
+        exact = wave_any(bad);
+        if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+    }
+    if (exact) {
+        const float ref2 = ref * kLog2e;
+        Rs st{mine.a, mine.b, (float)((mine.P - (double)ref2) * kLn2D)};
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (j < Lv) {
+                const float kr = kc[j] - ref;
+                const float yj = rs_out(st, kr, vc[j], uc);
+                rs_push(st, kr, vc[j], dc);
+                kc[j] = yj;
+            }
+        }
+    }
+    if (Lv > 0 && cval) {
+        const rsrc_t ry = make_rsrc(y + (row0 + t0) * C);
+        const int stride = (int)(C * 4);
 #pragma unroll
         for (int j = 0; j < CH; ++j)
-            if (j < Lv) ref = fmaxf(ref, kc[j]);
-        const float ref2 = ref * kLog2e;
-        bool exact = slow_wave;
-        float S = 0.0f, Z = 0.0f;
-        double sc = (double)ref2;
-        if (!exact) {
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const float e = (j < Lv) ? ex2(fmaf(kc[j], kLog2e, -ref2)) : 0.0f;
-                const float ev = e * vc[j];
-                kc[j] = e;
-                vc[j] = ev;
-                S = fmaf(S, dwf, ev);
-                Z = fmaf(Z, dwf, e);
-            }
-            exact = wave_any(Lv > 0 && !(Z >= kTinyDen));
-            if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        }
-        if (exact) {
-            Rs s{0.0f, 0.0f, kNegBig};
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                if (j < Lv)
-                    rs_push(s, kc[j] - ref, vc[j], dc);
-                else
-                    s.p -= wc;
-            }
-            S = s.a;
-            Z = s.b;
-            sc = (double)ref2 + (double)s.p * kLog2eD;
-        }
-
-        // ---- scan over the window's chunks ----
-        s_al[buf][q][lane] = S;
-        s_be[buf][q][lane] = Z;
-        s_sc[buf][q][lane] = sc;
-        __syncthreads();
-        Carry mine = carry;
-#pragma unroll
-        for (int qq = 0; qq < NW; ++qq) {
-            if (qq == q) mine = carry;
-            fold(carry, s_al[buf][qq][lane], s_be[buf][qq][lane], s_sc[buf][qq][lane], dec);
-        }
-        buf ^= 1;
-
-        // ---- phase 3: outputs ----
-        if (!exact) {
-            const float gap = (float)(mine.P - (double)ref2);
-            bool bad = gap > kCarryGap;
-            const float s0 = ex2(gap);
-            float Sx = mine.a * s0, Zx = mine.b * s0;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const float e = kc[j], ev = vc[j];
-                const float num = fmaf(eu, ev, Sx);
-                const float den = fmaf(eu, e, Zx);
-                if (j < Lv) bad |= !(den >= kTinyDen);
-                kc[j] = num * rcpf(den);
-                Sx = fmaf(Sx, dwf, ev);
-                Zx = fmaf(Zx, dwf, e);
-            }
-            exact = wave_any(bad);
-            if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        }
-        if (exact) {
-            Rs s{mine.a, mine.b, (float)((mine.P - (double)ref2) * kLn2D)};
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                if (j < Lv) {
-                    const float kr = kc[j] - ref;
-                    const float yj = rs_out(s, kr, vc[j], uc);
-                    rs_push(s, kr, vc[j], dc);
-                    kc[j] = yj;
-                }
-            }
-        }
-
-        // ---- store y ----
-        if (Lv > 0 && cval) {
-            const rsrc_t ry = make_rsrc(y + (row0 + t0) * C);
-            const int stride = (int)(C * 4);
-#pragma unroll
-            for (int j = 0; j < CH; ++j)
-                if (j < Lv) bstore(ry, kc[j], voff, j * stride);
-        }
-
-        if (more) {
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                kc[j] = kn[j];
-                vc[j] = vn[j];
-            }
-        }
+            if (j < Lv) bstore(ry, kc[j], voff, j * stride);
     }
 }
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, float *sva, float *svb,
-                          double *svP, hipStream_t stream) {
-    constexpr int NW = 8, CH = 32;
+                          const float *k, const float *v, float *y, const FwdLayout &L,
+                          uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
-    const int64_t nblk = B * ngrp;
-    hipLaunchKernelGGL((wkv_forward_kernel<NW, CH>), dim3((unsigned)nblk), dim3(NW * 64), 0,
-                       stream, T, C, ngrp, w, u, k, v, y, sva, svb, svP);
+    const int64_t nbg = B * ngrp;
+    const int64_t units = nbg * L.nseg;
+    hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
+                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
+                       k, v, y, L.flags, L.agg, L.incl);
     return hipGetLastError();
 }
 

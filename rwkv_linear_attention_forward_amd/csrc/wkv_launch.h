@@ -1,4 +1,4 @@
-// wkv_launch.h -- kernel launchers behind the C ABI (internal to librwkv_wkv).
+// wkv_launch.h -- kernel launchers and workspace layouts behind the C ABI (internal).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,14 +6,69 @@
 
 namespace wkvdev {
 
-// Tokens between two carries saved by the forward for the backward. Every kernel window
-// divides it, and the saved-carry layout is [B][ceil(T / kSaveStride)][C] for each of
-// a (fp32), b (fp32) and P (fp64), in that order in one buffer.
-constexpr int kSaveStride = 256;
+// Forward geometry: a unit is 64 channels x one window of kFwdWaves * kFwdChunk tokens.
+constexpr int kFwdWaves = 8;
+constexpr int kFwdChunk = 32;
+constexpr int kFwdWindow = kFwdWaves * kFwdChunk;
+
+// Publication status of a unit (low 2 bits of its flag; the high bits hold the call epoch).
+constexpr uint64_t kAggregate = 1;
+constexpr uint64_t kInclusive = 2;
+constexpr int kPollTries = 2000;  // bounded wait before a missing aggregate is recomputed
+
+// A carry or window summary as published: A = a 2^P, B = b 2^P (a, b packed in `ab`).
+struct Rec {
+    uint64_t ab;
+    uint64_t P;  // fp64 bits
+};
+
+// Forward workspace, carved out of the caller's buffer (see wkv_api.hip):
+//   flags[nseg][B * ngrp]   uint64 publication flags
+//   agg[B][nseg][C]         window aggregates (from the empty state)
+//   incl[B][nseg][C]        inclusive carries: the state after window s, i.e. entering s+1
+struct FwdLayout {
+    int64_t nseg;
+    uint64_t *flags;
+    Rec *agg;
+    Rec *incl;
+};
+
+// A reverse carry or reverse window summary as published: the future sums
+//   G = sum_{t>=t0} e^{-(t-t0)w} s_t,  H = same with s_t y_t,
+//   G' = sum_{t>=t0} (t-t0) e^{-(t-t0)w} s_t,  H' = same with s_t y_t
+// (s_t = dy_t / D_t), held as (g, h, gp, hp) 2^r with fp32 mantissas and an fp64 scale.
+struct RevRec {
+    uint64_t gh;    // g, h (fp32 bits)
+    uint64_t gphp;  // gp, hp (fp32 bits)
+    uint64_t r;     // fp64 bits
+    uint64_t pad;
+};
+
+// Backward workspace:
+//   flags[nseg][B * ngrp]    uint64 publication flags (reverse direction)
+//   ragg[B][nseg][C]         reverse window aggregates (from a zero future)
+//   rincl[B][nseg][C]        reverse inclusive carries: the future sums entering window s
+//   part[B][nseg][C][2]      per-window dw, du partials (fp64), summed by a second kernel
+struct BwdLayout {
+    int64_t nseg;
+    uint64_t *flags;
+    RevRec *ragg;
+    RevRec *rincl;
+    double *part;
+};
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, float *sva, float *svb,
-                          double *svP, hipStream_t stream);
+                          const float *k, const float *v, float *y, const FwdLayout &L,
+                          uint64_t epoch, hipStream_t stream);
+
+// `fincl` is the forward workspace's inclusive-carry array for the same inputs.
+hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                           const float *k, const float *v, const float *dy, const Rec *fincl,
+                           float *dk, float *dv, float *dw, float *du, const BwdLayout &L,
+                           uint64_t epoch, hipStream_t stream);
+
+// dw = du = 0 over C channels (backward of an empty batch or sequence).
+hipError_t launch_zero2(float *dw, float *du, int64_t C, hipStream_t stream);
 
 hipError_t launch_decode(int64_t B, int64_t C, const float *w, const float *u, const float *k,
                          const float *v, float *a, float *b, float *p, float *y,

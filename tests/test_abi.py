@@ -41,24 +41,30 @@ def test_status_strings_and_version(pkg):
     assert lib.wkv_status_string(99) == b"unknown status"
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_sizes(pkg):
     lib = pkg.load_library()
-    assert lib.wkv_saved_size(8, 4096, 2560) == 8 * 16 * 2560 * 16
-    assert lib.wkv_saved_size(1, 257, 3) == 1 * 2 * 3 * 16
-    assert lib.wkv_saved_size(-1, 4, 4) == 0
-    assert lib.wkv_saved_size(1, 4, (1 << 24) + 1) == 0
-    assert lib.wkv_backward_workspace_size(8, 4096, 2560, 1) == 8 * 2560 * 16
-    assert (lib.wkv_backward_workspace_size(8, 4096, 2560, 0)
-            == 8 * 2560 * 16 + 8 * 16 * 2560 * 16)
-    assert lib.wkv_backward_workspace_size(1, 1, 3, 1) == 256  # rounded to 256 bytes
+    B, T, C = 8, 4096, 2560
+    nseg, ngrp = 16, 40
+    fwd = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 16)
+    assert lib.wkv_forward_workspace_size(B, T, C) == fwd
+    own = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 32) + _r256(B * nseg * C * 16)
+    assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
+    assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
+    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 256
+    assert lib.wkv_forward_workspace_size(-1, 4, 4) == 0
+    assert lib.wkv_forward_workspace_size(1, 4, (1 << 24) + 1) == 0
 
 
 FAKE = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(12)]
 
 
-def _fwd(lib, B, T, C, ptrs=None, saved=None, sbytes=0):
+def _fwd(lib, B, T, C, ptrs=None, ws=FAKE[6], wsbytes=1 << 40):
     p = FAKE if ptrs is None else ptrs
-    return lib.wkv_forward(B, T, C, p[0], p[1], p[2], p[3], p[4], saved, sbytes, None)
+    return lib.wkv_forward(B, T, C, p[0], p[1], p[2], p[3], p[4], ws, wsbytes, None)
 
 
 def test_forward_rejects_bad_arguments(pkg):
@@ -77,17 +83,46 @@ def test_forward_rejects_bad_arguments(pkg):
     alias = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], ctypes.c_void_p(FAKE[2].value + 16)]
     assert _fwd(lib, 2, 3, 4, alias) == pkg.WKV_ERR_INVALID_ARG
     assert b"overlaps" in lib.wkv_last_error()
-    assert _fwd(lib, 2, 300, 4, saved=FAKE[6], sbytes=10) == pkg.WKV_ERR_INVALID_ARG
-    assert b"saved buffer" in lib.wkv_last_error()
+    assert _fwd(lib, 2, 300, 4, wsbytes=10) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace has 10 bytes" in lib.wkv_last_error()
+    assert _fwd(lib, 2, 300, 4, ws=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace is NULL" in lib.wkv_last_error()
+    assert _fwd(lib, 2, 300, 4, ws=ctypes.c_void_p(FAKE[6].value + 8)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"16-byte aligned" in lib.wkv_last_error()
+    # a workspace overlapping k
+    assert _fwd(lib, 2, 300, 4, ws=ctypes.c_void_p(FAKE[2].value + 64)) == pkg.WKV_ERR_INVALID_ARG
 
 
 def test_zero_sized_forward_is_a_noop(pkg):
     lib = pkg.load_library()
     none = [None] * 5
-    assert _fwd(lib, 0, 5, 5, none) == pkg.WKV_OK
-    assert _fwd(lib, 3, 0, 5, none) == pkg.WKV_OK
-    assert _fwd(lib, 3, 5, 0, none) == pkg.WKV_OK
+    assert _fwd(lib, 0, 5, 5, none, ws=None) == pkg.WKV_OK
+    assert _fwd(lib, 3, 0, 5, none, ws=None) == pkg.WKV_OK
+    assert _fwd(lib, 3, 5, 0, none, ws=None) == pkg.WKV_OK
     assert lib.wkv_last_error() == b""
+
+
+def _bwd(lib, B, T, C, fws=None, ws=FAKE[11], wsbytes=1 << 40, dw=FAKE[9], du=FAKE[10]):
+    f = FAKE
+    return lib.wkv_backward(B, T, C, f[0], f[1], f[2], f[3], f[4], fws, f[5], f[6], dw, du, ws,
+                            wsbytes, None)
+
+
+def test_backward_rejects_bad_arguments(pkg):
+    lib = pkg.load_library()
+    assert _bwd(lib, 2, -3, 4) == pkg.WKV_ERR_INVALID_ARG
+    assert _bwd(lib, 2, 3, 4, dw=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"dw is NULL" in lib.wkv_last_error()
+    assert _bwd(lib, 2, 3, 4, ws=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace is NULL" in lib.wkv_last_error()
+    assert _bwd(lib, 2, 3, 4, wsbytes=100) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace has 100 bytes" in lib.wkv_last_error()
+    # dk aliasing dy
+    f = FAKE
+    rc = lib.wkv_backward(2, 3, 4, f[0], f[1], f[2], f[3], f[4], None, f[4], f[6], f[9], f[10],
+                          f[11], 1 << 40, None)
+    assert rc == pkg.WKV_ERR_INVALID_ARG and b"overlaps" in lib.wkv_last_error()
+    assert _bwd(lib, 2, 3, 0, dw=None, du=None) == pkg.WKV_OK
 
 
 def test_decode_rejects_bad_arguments(pkg):

@@ -13,16 +13,12 @@ from helpers import assert_wkv_close
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_forward(wkv, dev, x, saved=False):
+def _gpu_forward(wkv, dev, x, ws=None):
     import torch
     t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(dev) for n in ("w", "u", "k", "v")}
-    sv = None
-    if saved:
-        B, T, C = x["k"].shape
-        sv = wkv.new_saved(B, T, C, dev)
-    y = wkv.forward(t["w"], t["u"], t["k"], t["v"], saved=sv)
+    y = wkv.forward(t["w"], t["u"], t["k"], t["v"], workspace=ws)
     torch.cuda.synchronize()
-    return y.cpu().numpy(), (None if sv is None else sv.cpu().numpy())
+    return y.cpu().numpy(), ws
 
 
 def _log(name, x, v):
@@ -53,13 +49,23 @@ def test_full_workloads(wkv, dev, name):
     _log(name, x, assert_wkv_close(y, ref, name))
 
 
-def test_saved_carries_do_not_change_y_and_determinism(wkv, dev):
+def test_determinism_and_workspace_reuse(wkv, dev):
+    """Bitwise identical results run to run, with a fresh workspace, a reused one, and a
+    workspace holding another call's stale records."""
+    import torch
     x = wkv_inputs.generate("longctx", B=2, T=1500, C=192, with_dy=False)
     y0, _ = _gpu_forward(wkv, dev, x)
-    y1, sv = _gpu_forward(wkv, dev, x, saved=True)
-    y2, sv2 = _gpu_forward(wkv, dev, x, saved=True)
-    assert np.array_equal(y0, y1) and np.array_equal(y1, y2)
-    assert np.array_equal(sv, sv2)
+    B, T, C = x["k"].shape
+    ws = wkv.forward_workspace(B, T, C, dev)
+    ws.fill_(0xA5)
+    y1, _ = _gpu_forward(wkv, dev, x, ws)
+    y2, _ = _gpu_forward(wkv, dev, x, ws)
+    x2 = dict(x)
+    x2["k"] = (x["k"] + np.float32(1.5)).astype(np.float32)
+    _gpu_forward(wkv, dev, x2, ws)  # leaves records of different inputs behind
+    y3, _ = _gpu_forward(wkv, dev, x, ws)
+    assert np.array_equal(y0, y1) and np.array_equal(y1, y2) and np.array_equal(y1, y3)
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("kscale,spike", [(8.0, 0.0), (20.0, 80.0), (1.0, 1000.0),
