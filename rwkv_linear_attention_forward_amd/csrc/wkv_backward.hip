@@ -4,246 +4,239 @@
 // formula (8); "RWKV についての調査記録", section "Trainingについて" (all parameters are
 // trained by gradient descent, w and u being per-channel vectors).
 //
-// With D_t the denominator of y_t, s_t = dy_t / D_t, and the future sums
+// With D_t the denominator of y_t, s_t = dy_t / D_t, the past sums A_t, B_t of the
+// recursive form and their age-weighted versions A'_t = sum_{i<t} (t-1-i) e^{-(t-1-i)w+k_i}
+// v_i, B'_t likewise (dA_t/dw = -A'_t), and the future sums
 //   G_i = sum_{t>i} e^{-(t-1-i)w} s_t,   H_i = same with s_t y_t,
-//   G'_i = sum_{t>i} (t-1-i) e^{-(t-1-i)w} s_t,   H'_i = same with s_t y_t,
 // the gradients are
 //   dv_i = s_i e^{u+k_i} + e^{k_i} G_i
 //   dk_i = s_i e^{u+k_i} (v_i - y_i) + e^{k_i} (v_i G_i - H_i)
-//   du   = sum_i s_i e^{u+k_i} (v_i - y_i)
-//   dw   = -sum_i e^{k_i} (v_i G'_i - H'_i)
-// (the O(T^2) softmax form gives the same sums term by term).
+//   du   = sum_t s_t e^{u+k_t} (v_t - y_t)
+//   dw   = -sum_t s_t (A'_t - y_t B'_t)
+// (the O(T^2) softmax form gives the same sums term by term). dw and du are thus sums over
+// the forward direction, formed where y_t and D_t are computed; only dk and dv need the
+// future sums.
 //
 // Work decomposition as in the forward (64 channels x one 256-token window per workgroup,
 // one CH-token chunk per wave), with units numbered from the last window backwards so that
 // the future of a unit was launched first. Each unit reads k, v, dy once and writes dk, dv
-// once: 20 bytes per element. The forward state entering the window is read from the
-// forward's workspace, so no extra pass over k and v is needed.
+// once: 20 bytes per element. The forward state entering the window (with A', B') is read
+// from the forward's workspace, so no extra pass over k and v is needed.
 //
 // Per chunk, in the forward pass's chunk frame (ref = max k, e_j = e^{k_j - ref}):
-//   F1/F3  recompute y_j and den_j exactly as the forward does; sigma_j = dy_j / den_j is
-//          s_t expressed in the frame.
+//   F1     forward summary of the chunk (fp64, as the forward computes it); the window's
+//          summaries are folded through LDS into the carry entering each chunk.
+//   F3     y_j, den_j, sigma_j = dy_j / den_j (s_t in the frame) and the dw, du terms,
+//          all in fp64 from fp64 weights e_j: dw is a sum over B*T tokens whose terms
+//          cancel by factors of 10^4 on some channels (and its per-sequence parts cancel
+//          again over the batch), so any fp32 rounding of e_j, y_j or sigma_j inside it
+//          shows up. e_j, y_j, sigma_j are then kept in fp32 for dk, dv.
 //   R1     reverse summary of the chunk from a zero future, by Horner from the chunk end:
-//          R_{j-1} = e^{-w} R_j + sigma_j, Q likewise with sigma_j y_j,
-//          X_{j-1} = e^{-w} (X_j + R_j), Y likewise with Q (the age-weighted sums).
+//          R_{j-1} = e^{-w} R_j + sigma_j, Q likewise with sigma_j y_j (fp64).
 //   scan   reverse summaries are folded through LDS and across windows (decoupled
 //          look-back toward later windows) into the future sums at each chunk's end.
 //   R3     the same recursion from the incoming future sums gives, per token,
-//          e^{k_i} G_i = e_i R_i etc., hence dv, dk, and the dw, du contributions.
-// The fixed frame needs no exponential in R1/R3 at all. Chunks whose frame would under- or
-// overflow are redone with a per-token rescaled recursion (exact_chunk_bwd).
+//          e^{k_i} G_i = e_i R_i and e^{k_i} H_i = e_i Q_i, hence dv and dk.
+// Chunks whose frame would under- or overflow are redone with a per-token rescaled
+// recursion in fp64 (exact_chunk).
 #include "wkv_chunk.h"
 
 namespace wkvdev {
 
-// Future sums (G, H, G', H') = (g, h, gp, hp) 2^r.
+// Future sums (G, H) = (g, h) 2^r.
 struct RevCarry {
-    float g, h, gp, hp;
+    double g, h;
     double r;
 };
 
-__device__ __forceinline__ RevCarry rev_zero() { return RevCarry{0.f, 0.f, 0.f, 0.f, kNegBigD}; }
+__device__ __forceinline__ RevCarry rev_zero() { return RevCarry{0.0, 0.0, kNegBigD}; }
 
-// c <- the future seen from `len` tokens earlier, where `sum` summarizes those `len` tokens
-// (from a zero future) and c was the future beyond them:
-//   G <- e^{-len w} G + sum.G,   G' <- e^{-len w} (G' + len G) + sum.G'   (H, H' alike).
-__device__ __forceinline__ void rfold(RevCarry &c, const RevCarry &sum, double len_w2,
-                                      float len) {
+// c <- the future seen from `len` tokens earlier (len_w2 = len w log2 e), where `sum`
+// summarizes those tokens from a zero future and c was the future beyond them:
+//   G <- e^{-len w} G + sum.G   (H alike).
+__device__ __forceinline__ void rfold(RevCarry &c, const RevCarry &sum, double len_w2) {
     const double rd = c.r - len_w2;
-    const float d = (float)(sum.r - rd);
-    const float f = ex2(-fabsf(d));
-    const bool up = d >= 0.0f;
-    const float ca = up ? f : 1.0f;
-    const float cs = up ? 1.0f : f;
-    const float g = c.g, h = c.h;
-    c.g = fmaf(g, ca, sum.g * cs);
-    c.h = fmaf(h, ca, sum.h * cs);
-    c.gp = fmaf(fmaf(len, g, c.gp), ca, sum.gp * cs);
-    c.hp = fmaf(fmaf(len, h, c.hp), ca, sum.hp * cs);
+    const double d = sum.r - rd;
+    const double f = exp2_64(-fabs(d));
+    const bool up = d >= 0.0;
+    const double ca = up ? f : 1.0;
+    const double cs = up ? 1.0 : f;
+    c.g = fma(c.g, ca, sum.g * cs);
+    c.h = fma(c.h, ca, sum.h * cs);
     c.r = up ? sum.r : rd;
 }
 
-__device__ __forceinline__ RevCarry rfollow(RevCarry c, const RevCarry &sum, double len_w2,
-                                            float len) {
-    rfold(c, sum, len_w2, len);
+__device__ __forceinline__ RevCarry rfollow(RevCarry c, const RevCarry &sum, double len_w2) {
+    rfold(c, sum, len_w2);
     return c;
 }
 
-// Rescale so that the largest |mantissa| lies in [1, 2) (exact), making r the magnitude.
+// Rescale so that the larger |mantissa| lies in [1, 2) (exact), making r the magnitude.
 __device__ __forceinline__ void rnormalize(RevCarry &c) {
-    const float m = fmaxf(fmaxf(fabsf(c.g), fabsf(c.h)), fmaxf(fabsf(c.gp), fabsf(c.hp)));
-    if (m > 0.0f && m <= 3.0e38f) {
-        const int e = __builtin_amdgcn_frexp_expf(m) - 1;
-        c.g = ldexpf(c.g, -e);
-        c.h = ldexpf(c.h, -e);
-        c.gp = ldexpf(c.gp, -e);
-        c.hp = ldexpf(c.hp, -e);
+    const double m = fmax(fabs(c.g), fabs(c.h));
+    if (m > 0.0 && m <= 1.0e300) {
+        const int e = __builtin_amdgcn_frexp_exp(m) - 1;
+        c.g = ldexp(c.g, -e);
+        c.h = ldexp(c.h, -e);
         c.r += (double)e;
     }
 }
 
-__device__ __forceinline__ uint64_t pack2(float x, float y) {
-    return ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32) |
-           (uint64_t)__builtin_bit_cast(uint32_t, x);
-}
-__device__ __forceinline__ float lo32(uint64_t v) {
-    return __builtin_bit_cast(float, (uint32_t)(v & 0xffffffffu));
-}
-__device__ __forceinline__ float hi32(uint64_t v) {
-    return __builtin_bit_cast(float, (uint32_t)(v >> 32));
-}
-
 __device__ __forceinline__ void put_rrec(RevRec *p, const RevCarry &c) {
-    __hip_atomic_store(&p->gh, pack2(c.g, c.h), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p->gphp, pack2(c.gp, c.hp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p->r, __builtin_bit_cast(uint64_t, c.r), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    put_u64(&p->g, c.g);
+    put_u64(&p->h, c.h);
+    put_u64(&p->r, c.r);
 }
 __device__ __forceinline__ RevCarry get_rrec(const RevRec *p) {
-    const uint64_t gh = __hip_atomic_load(&p->gh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t gphp = __hip_atomic_load(&p->gphp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t r = __hip_atomic_load(&p->r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return RevCarry{lo32(gh), hi32(gh), lo32(gphp), hi32(gphp), __builtin_bit_cast(double, r)};
+    return RevCarry{get_u64(&p->g), get_u64(&p->h), get_u64(&p->r)};
 }
 
 // ---------------------------------------------------------------------------------
 // Exact per-token backward of one lane's chunk (tokens [0, Lv)), for chunks whose fixed
-// frame would under- or overflow. On entry kc, vc, gc hold the raw k, v, dy; they and yc
-// are clobbered. `fin` is the forward carry entering the chunk, `rin` the future sums at
-// the chunk's nominal end (CH tokens after its start). The chunk is done in two halves:
-// the forward recursion is rerun from `fin` for each half and its per-token quantities
-// (k - ref, v, y, dy / den, log-scale of D) are kept only for that half, which is then
-// swept backwards. With OUT, dk and dv are stored and the du, dw contributions added.
-// Returns the future sums at the chunk start.
+// frame would under- or overflow (a dominant key next to much smaller ones, extreme u).
+// Everything is fp64 with library exponentials. On entry kc, vc, gc hold the raw k, v,
+// dy; gc and yc are clobbered. `fin` is the forward carry entering the chunk, `rin` the
+// future sums at the chunk's nominal end. The chunk is swept in quarters from the last
+// one: for each quarter the forward recursion is rerun from `fin` (adding the dw, du
+// terms of the quarter's tokens if FG) and that quarter's per-token y and log-scale of D
+// (each as a float pair, about 48 bits) and dy / den are kept in yc and gc; then the
+// quarter is swept backwards (storing dk, dv if OUT). Returns the future sums at the
+// chunk start.
 // ---------------------------------------------------------------------------------
-struct RevState {  // (R, Q, X, Y) = (g, h, gp, hp) e^r, natural scale relative to e^{ref}
-    float g, h, gp, hp, r;
+struct RevState64 {  // (G, H) = (g, h) e^{r - ref}
+    double g, h, r;
 };
 
-template <int CH, int J0, int J1, bool STORE>
-__device__ __forceinline__ void exact_fwd_steps(float (&kc)[CH], float (&vc)[CH],
-                                                float (&gc)[CH], float (&yc)[CH], int Lv,
-                                                float ref, float uc, const Decay &dc, Rs &st) {
-    constexpr int H = CH / 2;
+template <int CH, int QS, bool OUT, bool FG>
+__device__ __forceinline__ void exact_quarter(const float (&kc)[CH], const float (&vc)[CH],
+                                              float (&gc)[CH], float (&yc)[CH], int Lv,
+                                              double ref, double uc, double wc,
+                                              const Rs64 &st0, RevState64 &rs, rsrc_t rdk,
+                                              rsrc_t rdv, int voff, int stride, bool st_ok,
+                                              double &du_acc, double &dw_acc) {
+    constexpr int Q = CH / 4;  // tokens per quarter
+    constexpr int J0 = QS * Q;
+    static_assert(4 * Q <= CH, "yc holds y and M of one quarter, each as a float pair");
+    Rs64 st = st0;
 #pragma unroll
-    for (int j = J0; j < J1; ++j) {
+    for (int j = 0; j < J0; ++j)
+        if (j < Lv) rs64_push(st, (double)kc[j] - ref, (double)vc[j], wc);
+#pragma unroll
+    for (int j = J0; j < J0 + Q; ++j) {
         if (j < Lv) {
-            const float kr = kc[j] - ref;
-            const float vv = vc[j];
-            if (STORE) {
-                const float uk = uc + kr;
-                const float d = st.p - uk;
-                const float e = expn(-fabsf(d));
-                const bool sp = d >= 0.0f;
-                const float e1 = sp ? 1.0f : e;
-                const float e2 = sp ? e : 1.0f;
-                const float den = fmaf(e1, st.b, e2);
-                kc[j] = kr;
-                yc[j] = fmaf(e1, st.a, e2 * vv) / den;
-                gc[j] = gc[j] / den;
-                yc[(j + H) % CH] = sp ? st.p : uk;
+            const double kr = (double)kc[j] - ref, vv = (double)vc[j];
+            const double uk = uc + kr;
+            const double m = fmax(st.p, uk);
+            const double e1 = exp(st.p - m), e2 = exp(uk - m);
+            const double rden = 1.0 / fma(e1, st.b, e2);
+            const double yv = fma(e1, st.a, e2 * vv) * rden;
+            const double sg = (double)gc[j] * rden;  // dy / D in units of e^{-(m + ref)}
+            if (FG) {
+                // s (A' - y B') and s e^{u+k} (v - y), with A' = a' e^{p+ref}
+                dw_acc = fma(sg * e1, fma(-yv, st.bp, st.ap), dw_acc);
+                du_acc = fma(sg * e2, vv - yv, du_acc);
             }
-            rs_push(st, kr, vv, dc);
+            const float yh = (float)yv;
+            yc[j - J0] = yh;
+            yc[3 * Q + j - J0] = (float)(yv - (double)yh);
+            gc[j] = (float)sg;
+            const float mh = (float)m;
+            yc[Q + j - J0] = mh;
+            yc[2 * Q + j - J0] = (float)(m - (double)mh);
+            rs64_push(st, kr, vv, wc);
         }
     }
-}
-
-template <int CH, int J0, int J1, bool OUT>
-__device__ __forceinline__ void exact_rev_steps(const float (&kc)[CH], const float (&vc)[CH],
-                                                const float (&gc)[CH], const float (&yc)[CH],
-                                                int Lv, float uc, const Decay &dc, RevState &rs,
-                                                rsrc_t rdk, rsrc_t rdv, int voff, int stride,
-                                                bool st_ok, float &du_acc, float &dw_acc) {
-    constexpr int H = CH / 2;
 #pragma unroll
-    for (int j = J1 - 1; j >= J0; --j) {
+    for (int j = J0 + Q - 1; j >= J0; --j) {
         if (j < Lv) {
-            const float kr = kc[j], vv = vc[j], yy = yc[j], sg = gc[j];
-            const float M = yc[(j + H) % CH];
+            const double kr = (double)kc[j] - ref, vv = (double)vc[j];
+            const double yy = (double)yc[j - J0] + (double)yc[3 * Q + j - J0];
+            const double sg = (double)gc[j];
+            const double M = (double)yc[Q + j - J0] + (double)yc[2 * Q + j - J0];
             if (OUT) {
-                const float ekr = expn(kr + rs.r);
-                const float cpi = sg * expn(uc + kr - M);
-                const float dd = vv - yy;
+                const double ekr = exp(kr + rs.r);
+                const double cpi = sg * exp(uc + kr - M);
                 if (st_ok) {
-                    bstore(rdv, fmaf(ekr, rs.g, cpi), voff, j * stride);
-                    bstore(rdk, fmaf(cpi, dd, ekr * fmaf(vv, rs.g, -rs.h)), voff, j * stride);
+                    bstore(rdv, (float)fma(ekr, rs.g, cpi), voff, j * stride);
+                    bstore(rdk, (float)fma(cpi, vv - yy, ekr * fma(vv, rs.g, -rs.h)), voff,
+                           j * stride);
                 }
-                du_acc = fmaf(cpi, dd, du_acc);
-                dw_acc = fmaf(ekr, fmaf(vv, rs.gp, -rs.hp), dw_acc);
             }
-            const float a = rs.r - dc.w;
-            const float b = -M;
-            const float e = expn(-fabsf(a - b));
-            const bool keep = a >= b;
-            const float fa = keep ? 1.0f : e;
-            const float fb = keep ? e : 1.0f;
-            rs.gp = (rs.gp + rs.g) * fa;
-            rs.hp = (rs.hp + rs.h) * fa;
-            rs.g = fmaf(rs.g, fa, sg * fb);
-            rs.h = fmaf(rs.h, fa, sg * yy * fb);
-            rs.r = keep ? a : b;
+            const double a = rs.r - wc, b = -M;
+            const double rn = fmax(a, b);
+            const double fa = exp(a - rn), fb = exp(b - rn);
+            rs.g = fma(rs.g, fa, sg * fb);
+            rs.h = fma(rs.h, fa, sg * yy * fb);
+            rs.r = rn;
         } else {
-            rs.gp = rs.gp + rs.g;  // a padded token past T: pure decay (its s is 0)
-            rs.hp = rs.hp + rs.h;
-            rs.r -= dc.w;
+            rs.r -= wc;  // a padded token past T: pure decay (its s is 0)
         }
     }
 }
 
-template <int CH, bool OUT>
-__device__ RevCarry exact_chunk_bwd(float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
-                                    float (&yc)[CH], int Lv, float ref, const Carry &fin,
-                                    const RevCarry &rin, float uc, const Decay &dc, rsrc_t rdk,
-                                    rsrc_t rdv, int voff, int stride, bool st_ok, float &du_acc,
-                                    float &dw_acc) {
-    constexpr int H = CH / 2;
-    const double ref2 = (double)(ref * kLog2e);
-    const Rs st0{fin.a, fin.b, (float)((fin.P - ref2) * kLn2D)};
-    RevState rs{rin.g, rin.h, rin.gp, rin.hp, (float)((rin.r + ref2) * kLn2D)};
-    // second half: forward to the middle, then forward over the half keeping its tokens
-    {
-        Rs st = st0;
-        exact_fwd_steps<CH, 0, H, false>(kc, vc, gc, yc, Lv, ref, uc, dc, st);
-        exact_fwd_steps<CH, H, CH, true>(kc, vc, gc, yc, Lv, ref, uc, dc, st);
-        exact_rev_steps<CH, H, CH, OUT>(kc, vc, gc, yc, Lv, uc, dc, rs, rdk, rdv, voff, stride,
-                                        st_ok, du_acc, dw_acc);
-    }
-    // first half
-    {
-        Rs st = st0;
-        exact_fwd_steps<CH, 0, H, true>(kc, vc, gc, yc, Lv, ref, uc, dc, st);
-        exact_rev_steps<CH, 0, H, OUT>(kc, vc, gc, yc, Lv, uc, dc, rs, rdk, rdv, voff, stride,
-                                       st_ok, du_acc, dw_acc);
-    }
-    return RevCarry{rs.g, rs.h, rs.gp, rs.hp, (double)rs.r * kLog2eD - ref2};
+template <int CH, bool OUT, bool FG>
+__device__ RevCarry exact_chunk(const float (&kc)[CH], const float (&vc)[CH], float (&gc)[CH],
+                                float (&yc)[CH], int Lv, float ref, const Carry &fin,
+                                RevCarry rin, float uc, float wc, rsrc_t rdk, rsrc_t rdv,
+                                int voff, int stride, bool st_ok, double &du_acc,
+                                double &dw_acc) {
+    const double refd = (double)ref;
+    const double ref2 = refd * kLog2eD;  // the frame 2^{ref2} the carries refer to
+    rnormalize(rin);
+    // the carries are relative to 2^{ref2}; the per-token path works relative to e^{ref}
+    const double shift = ref2 * kLn2D - refd;
+    const Rs64 st0{fin.a, fin.b, fin.ap, fin.bp, (fin.P - ref2) * kLn2D + shift};
+    RevState64 rs{rin.g, rin.h, (rin.r + ref2) * kLn2D - shift};
+    const double u = (double)uc, w = (double)wc;
+    exact_quarter<CH, 3, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
+                                  stride, st_ok, du_acc, dw_acc);
+    exact_quarter<CH, 2, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
+                                  stride, st_ok, du_acc, dw_acc);
+    exact_quarter<CH, 1, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
+                                  stride, st_ok, du_acc, dw_acc);
+    exact_quarter<CH, 0, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
+                                  stride, st_ok, du_acc, dw_acc);
+    // G = g e^{r - ref} at the chunk start
+    return RevCarry{rs.g, rs.h, (rs.r - refd) * kLog2eD};
 }
 
-// LDS staging shared by the waves of a backward unit (forward summaries use a, b, r).
+// LDS staging shared by the waves of a backward unit (forward summaries use all five
+// arrays, reverse summaries three, the dw, du partials two).
 template <int NW>
 struct BwdShared {
-    float a[NW][64];
-    float b[NW][64];
-    float c[NW][64];
-    float d[NW][64];
+    double a[NW][64];
+    double b[NW][64];
+    double c[NW][64];
+    double d[NW][64];
     double r[NW][64];
     int status[2];
 };
 
+// Per-channel constants of a backward lane.
+struct BwdConst {
+    double w;       // the decay rate
+    double dwf;     // e^{-w}
+    double eu;      // e^{u}
+    double w2;      // w log2 e
+    float uc;
+    bool slow_wave; // some lane has |u| > 60: exact path throughout
+};
+
 // Everything a unit needs about one lane's chunk of window jw, up to its reverse summary:
-// the forward recomputation (F1/F3) and the reverse summary from a zero future (R1).
-// Called by all waves of the workgroup together (it contains a barrier; the caller makes
-// sure nobody still reads the staging arrays). On return with exact == false, kc, vc, gc,
-// yc hold e_j, v_j, sigma_j, y_j; with exact == true they are clobbered and the chunk must
-// take the per-token path again from raw data. Deterministic: the owner of a window and
-// a helper recomputing it get identical bits.
+// the forward recomputation with the chunk's dw, du terms (F1/F3) and the reverse summary
+// from a zero future (R1). Called by all waves of the workgroup together (it contains a
+// barrier; the caller makes sure nobody still reads the staging arrays). On return with
+// fx == false, kc, vc, gc, yc hold e_j, v_j, sigma_j, y_j; with fx == true (the forward
+// frame failed) they are clobbered and the chunk must take the per-token path again from
+// raw data. Deterministic: the owner of a window and a helper recomputing it get identical
+// bits.
 template <int NW, int CH>
 __device__ __forceinline__ RevCarry chunk_pass(
     BwdShared<NW> &sh, int64_t jw, int q, int lane, int64_t T, int64_t C, int64_t nseg,
     int64_t bidx, int64_t row0, int cl, int voff, int stride, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ dy, const Rec *__restrict__ fincl,
-    const Decay &dc, float uc, float eu, double w2, bool slow_wave, float (&kc)[CH],
-    float (&vc)[CH], float (&gc)[CH], float (&yc)[CH], bool &exact, Carry &mine, float &ref,
-    int &Lv) {
+    const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH], float (&yc)[CH],
+    bool &fx, Carry &mine, float &ref, int &Lv, double &du_acc, double &dw_acc) {
     const int64_t t0 = jw * (int64_t)(NW * CH) + (int64_t)q * CH;
     Lv = chunk_len(t0, T, CH);
     load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
@@ -251,75 +244,82 @@ __device__ __forceinline__ RevCarry chunk_pass(
 
     // F1: forward summary of the chunk, and the carry entering it
     ref = chunk_ref<CH>(kc, Lv);
-    const float ref2 = ref * kLog2e;
-    float S, Z;
-    double sc;
-    exact = chunk_summary<CH, true>(kc, vc, Lv, ref, slow_wave, dc, S, Z, sc);
-    if (exact) {
-        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        exact_summary<CH>(kc, vc, Lv, ref, dc, S, Z, sc);
-    }
-    sh.a[q][lane] = S;
-    sh.b[q][lane] = Z;
-    sh.r[q][lane] = sc;
+    const double refd = (double)ref;
+    const double ref2 = refd * kLog2eD;
+    Carry sum;
+    fx = chunk_summary<CH, true>(kc, vc, Lv, ref, K.slow_wave, K.dwf, sum);
+    if (fx) exact_summary<CH>(kc, vc, Lv, ref, K.w, sum);
+    sh.a[q][lane] = sum.a;
+    sh.b[q][lane] = sum.b;
+    sh.c[q][lane] = sum.ap;
+    sh.d[q][lane] = sum.bp;
+    sh.r[q][lane] = sum.P;
     __syncthreads();
-    mine = Carry{0.0f, 0.0f, kNegBigD};
-    if (jw > 0) {
-        const Rec *fr = fincl + (bidx * nseg + (jw - 1)) * C + cl;
-        mine.a = lo32(fr->ab);
-        mine.b = hi32(fr->ab);
-        mine.P = __builtin_bit_cast(double, fr->P);
-    }
+    mine = carry_empty();
+    if (jw > 0) mine = get_rec(fincl + (bidx * nseg + (jw - 1)) * C + cl);
     for (int qq = 0; qq < q; ++qq)
-        fold(mine, sh.a[qq][lane], sh.b[qq][lane], sh.r[qq][lane], (double)CH * w2);
+        fold(mine, Carry{sh.a[qq][lane], sh.b[qq][lane], sh.c[qq][lane], sh.d[qq][lane],
+                         sh.r[qq][lane]},
+             (double)CH * K.w2, (double)CH);
     normalize(mine);
 
-    // F3: y and sigma = dy / den in the chunk frame
-    if (!exact) {
-        const float gap = (float)(mine.P - (double)ref2);
-        bool bad = gap > kCarryGap;
-        const float s0 = ex2(gap);
-        float Sx = mine.a * s0, Zx = mine.b * s0;
+    // F3: y, sigma = dy / den and the dw, du terms in the chunk frame (fp64)
+    du_acc = 0.0;
+    dw_acc = 0.0;
+    if (!fx) {
+        const double gap = mine.P - ref2;
+        bool bad = gap > (double)kCarryGap;
+        const double s0 = exp2_64(gap);
+        double Sx = mine.a * s0, Zx = mine.b * s0, Spx = mine.ap * s0, Zpx = mine.bp * s0;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const float e = kc[j];
-            const float ev = e * vc[j];
-            const float num = fmaf(eu, ev, Sx);
-            const float den = fmaf(eu, e, Zx);
-            const float r = rcpf(den);
+            const double e = (j < Lv) ? exp2_64(((double)kc[j] - refd) * kLog2eD) : 0.0;
+            const double vv = (double)vc[j];
+            const double ev = e * vv;
+            const double num = fma(K.eu, ev, Sx);
+            const double den = fma(K.eu, e, Zx);
             if (j < Lv) {
-                bad |= !(den >= kTinyDen);
-                yc[j] = num * r;
-                gc[j] = gc[j] * r;
+                bad |= !(den >= (double)kTinyDen);
+                const double r = rcpd(den);
+                const double yv = num * r;
+                const double sg = (double)gc[j] * r;
+                dw_acc = fma(sg, fma(-yv, Zpx, Spx), dw_acc);
+                du_acc = fma(sg * (K.eu * e), vv - yv, du_acc);
+                kc[j] = (float)e;
+                yc[j] = (float)yv;
+                gc[j] = (float)sg;
             } else {
+                kc[j] = 0.0f;
                 yc[j] = 0.0f;
                 gc[j] = 0.0f;
             }
-            Sx = fmaf(Sx, dc.dwf, ev);
-            Zx = fmaf(Zx, dc.dwf, e);
+            Spx = K.dwf * (Spx + Sx);
+            Zpx = K.dwf * (Zpx + Zx);
+            Sx = fma(Sx, K.dwf, ev);
+            Zx = fma(Zx, K.dwf, e);
         }
-        exact = wave_any(bad);
+        fx = wave_any(bad);
     }
 
     // R1: reverse summary of the chunk from a zero future
-    if (!exact) {
-        const float dwf = dc.dwf;
-        float R = 0.f, Q = 0.f, X = 0.f, Y = 0.f;
+    if (!fx) {
+        double R = 0.0, Q = 0.0;
 #pragma unroll
         for (int j = CH - 1; j >= 0; --j) {
-            X = dwf * (X + R);
-            Y = dwf * (Y + Q);
-            R = fmaf(R, dwf, gc[j]);
-            Q = fmaf(Q, dwf, gc[j] * yc[j]);
+            const double sg = (double)gc[j];
+            R = fma(R, K.dwf, sg);
+            Q = fma(Q, K.dwf, sg * (double)yc[j]);
         }
-        return RevCarry{R, Q, X, Y, -(double)ref2};
+        return RevCarry{R, Q, -ref2};
     }
     load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
-    float d0 = 0.f, d1 = 0.f;
+    du_acc = 0.0;
+    dw_acc = 0.0;
     const rsrc_t none = make_rsrc(dy);
-    return exact_chunk_bwd<CH, false>(kc, vc, gc, yc, Lv, ref, mine, rev_zero(), uc, dc, none,
-                                      none, voff, stride, false, d0, d1);
+    return exact_chunk<CH, false, true>(kc, vc, gc, yc, Lv, ref, mine, rev_zero(), K.uc,
+                                        (float)K.w, none, none, voff, stride, false, du_acc,
+                                        dw_acc);
 }
 
 // Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
@@ -332,8 +332,6 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW> &sh, const RevCarr
     __syncthreads();
     sh.a[q][lane] = rsum.g;
     sh.b[q][lane] = rsum.h;
-    sh.c[q][lane] = rsum.gp;
-    sh.d[q][lane] = rsum.hp;
     sh.r[q][lane] = rsum.r;
     __syncthreads();
     agg = rev_zero();
@@ -341,9 +339,7 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW> &sh, const RevCarr
 #pragma unroll
     for (int qq = NW - 1; qq >= 0; --qq) {
         if (qq == q) lfut = agg;
-        const RevCarry sm{sh.a[qq][lane], sh.b[qq][lane], sh.c[qq][lane], sh.d[qq][lane],
-                          sh.r[qq][lane]};
-        rfold(agg, sm, (double)CH * w2, (float)CH);
+        rfold(agg, RevCarry{sh.a[qq][lane], sh.b[qq][lane], sh.r[qq][lane]}, (double)CH * w2);
     }
 }
 
@@ -372,25 +368,27 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
     const int stride = (int)(C * 4);
 
     const float wc = w[cl];
-    const float uc = u[cl];
-    const Decay dc = make_decay(wc);
-    const float dwf = dc.dwf;
-    const float eu = expf(uc);
-    const double w2 = (double)wc * kLog2eD;
-    const bool slow_wave = wave_any(!(fabsf(uc) <= 60.0f));
+    BwdConst K;
+    K.uc = u[cl];
+    K.w = (double)wc;
+    K.dwf = exp(-K.w);
+    K.eu = exp((double)K.uc);
+    K.w2 = K.w * kLog2eD;
+    K.slow_wave = wave_any(!(fabsf(K.uc) <= 60.0f));
     const int64_t row0 = bidx * T;
     const int64_t t0 = s * WIN + (int64_t)q * CH;
 
     float kc[CH], vc[CH], gc[CH], yc[CH];
-    bool exact;
+    bool fx;
     Carry mine;
     float ref;
     int Lv;
+    double du_acc, dw_acc;
     RevCarry rsum = chunk_pass<NW, CH>(sh, s, q, lane, T, C, nseg, bidx, row0, cl, voff, stride,
-                                       k, v, dy, fincl, dc, uc, eu, w2, slow_wave, kc, vc, gc,
-                                       yc, exact, mine, ref, Lv);
+                                       k, v, dy, fincl, K, kc, vc, gc, yc, fx, mine, ref, Lv,
+                                       du_acc, dw_acc);
     RevCarry agg, lfut;
-    window_rev_fold<NW, CH>(sh, rsum, q, lane, w2, agg, lfut);
+    window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2, agg, lfut);
     const int64_t rec = (bidx * nseg + s) * C + cl;
     uint64_t *myflag = flags + sidx * nbg + bg;
     if (q == 0) {
@@ -420,15 +418,16 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: recompute window j's reverse aggregate here and
                 // publish it (bitwise what unit j itself publishes)
-                bool ex_j;
+                bool fx_j;
                 Carry m_j;
                 float r_j;
                 int L_j;
+                double du_j, dw_j;
                 const RevCarry rs_j = chunk_pass<NW, CH>(
                     sh, j, q, lane, T, C, nseg, bidx, row0, cl, voff, stride, k, v, dy, fincl,
-                    dc, uc, eu, w2, slow_wave, kc, vc, gc, yc, ex_j, m_j, r_j, L_j);
+                    K, kc, vc, gc, yc, fx_j, m_j, r_j, L_j, du_j, dw_j);
                 RevCarry agg_j, lf_j;
-                window_rev_fold<NW, CH>(sh, rs_j, q, lane, w2, agg_j, lf_j);
+                window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
                 if (q == 0) {
                     if (cval) put_rrec(ragg + (bidx * nseg + j) * C + cl, agg_j);
                     raise_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kAggregate);
@@ -444,73 +443,64 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
         }
         if (j < nseg) fut = get_rrec(rincl + (bidx * nseg + j) * C + cl);
         for (int64_t m = j - 1; m > s; --m)
-            fut = rfollow(fut, get_rrec(ragg + (bidx * nseg + m) * C + cl), (double)WIN * w2,
-                          (float)WIN);
+            fut = rfollow(fut, get_rrec(ragg + (bidx * nseg + m) * C + cl), (double)WIN * K.w2);
         if (redo_own) {
             __syncthreads();
             chunk_pass<NW, CH>(sh, s, q, lane, T, C, nseg, bidx, row0, cl, voff, stride, k, v,
-                               dy, fincl, dc, uc, eu, w2, slow_wave, kc, vc, gc, yc, exact,
-                               mine, ref, Lv);
+                               dy, fincl, K, kc, vc, gc, yc, fx, mine, ref, Lv, du_acc, dw_acc);
         }
     }
     if (q == 0) {
-        if (cval) put_rrec(rincl + rec, rfollow(fut, agg, (double)WIN * w2, (float)WIN));
+        if (cval) put_rrec(rincl + rec, rfollow(fut, agg, (double)WIN * K.w2));
         put_flag(myflag, epoch, kInclusive);
     }
 
-    // ---- R3: gradients of this chunk ----
+    // ---- R3: dk, dv of this chunk ----
     const rsrc_t rdk = make_rsrc(dk + (row0 + (t0 < T ? t0 : 0)) * C);
     const rsrc_t rdv = make_rsrc(dv + (row0 + (t0 < T ? t0 : 0)) * C);
-    float du_acc = 0.0f, dw_acc = 0.0f;
-    RevCarry rc = rfollow(fut, lfut, (double)((NW - 1 - q) * CH) * w2, (float)((NW - 1 - q) * CH));
+    RevCarry rc = rfollow(fut, lfut, (double)((NW - 1 - q) * CH) * K.w2);
     rnormalize(rc);
-    const float ref2 = ref * kLog2e;
-    const float rgap = (float)((double)ref2 + rc.r);
-    if (!exact) exact = wave_any(rgap > kCarryGap);
-    if (!exact) {
-        const float fr = ex2(rgap);
-        float R = rc.g * fr, Q = rc.h * fr, X = rc.gp * fr, Y = rc.hp * fr;
+    const double rgap = (double)ref * kLog2eD + rc.r;
+    const bool rx = fx || wave_any(rgap > (double)kCarryGap);
+    if (!rx) {
+        const double fr = exp2_64(rgap);
+        const double dwf = K.dwf;
+        double R = rc.g * fr, Q = rc.h * fr;
 #pragma unroll
         for (int j = CH - 1; j >= 0; --j) {
-            const float e = kc[j], vv = vc[j], sg = gc[j], yy = yc[j];
-            const float cs = eu * sg;
-            const float t1 = cs * (vv - yy);
-            const float dvj = e * (cs + R);
-            const float dkj = e * (t1 + fmaf(vv, R, -Q));
-            du_acc = fmaf(t1, e, du_acc);
-            dw_acc = fmaf(e, fmaf(vv, X, -Y), dw_acc);
+            const double e = (double)kc[j], vv = (double)vc[j], sg = (double)gc[j];
+            const double yy = (double)yc[j];
+            const double cs = K.eu * sg;
             if (j < Lv && cval) {
-                bstore(rdv, dvj, voff, j * stride);
-                bstore(rdk, dkj, voff, j * stride);
+                bstore(rdv, (float)(e * (cs + R)), voff, j * stride);
+                bstore(rdk, (float)(e * fma(cs, vv - yy, fma(vv, R, -Q))), voff, j * stride);
             }
-            X = dwf * (X + R);
-            Y = dwf * (Y + Q);
-            R = fmaf(R, dwf, sg);
-            Q = fmaf(Q, dwf, sg * yy);
+            R = fma(R, dwf, sg);
+            Q = fma(Q, dwf, sg * yy);
         }
     } else {
         load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
         load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
-        exact_chunk_bwd<CH, true>(kc, vc, gc, yc, Lv, ref, mine, rc, uc, dc, rdk, rdv, voff,
-                                  stride, cval, du_acc, dw_acc);
+        double d0 = 0.0, d1 = 0.0;
+        exact_chunk<CH, true, false>(kc, vc, gc, yc, Lv, ref, mine, rc, K.uc, wc, rdk, rdv,
+                                     voff, stride, cval, d0, d1);
     }
 
     // ---- dw, du partials of this window, summed over its chunks in a fixed order ----
     __syncthreads();
-    sh.r[q][lane] = (double)du_acc;
+    sh.a[q][lane] = du_acc;
+    sh.b[q][lane] = -dw_acc;
     __syncthreads();
     if (q == 0) {
-        double su = 0.0;
-        for (int qq = 0; qq < NW; ++qq) su += sh.r[qq][lane];
-        if (cval) part[rec * 2 + 1] = su;
-    }
-    __syncthreads();
-    sh.r[q][lane] = -(double)dw_acc;
-    __syncthreads();
-    if (q == 0) {
-        double sw = 0.0;
-        for (int qq = 0; qq < NW; ++qq) sw += sh.r[qq][lane];
-        if (cval) part[rec * 2] = sw;
+        double su = 0.0, sw = 0.0;
+        for (int qq = 0; qq < NW; ++qq) {
+            su += sh.a[qq][lane];
+            sw += sh.b[qq][lane];
+        }
+        if (cval) {
+            part[rec * 2] = sw;
+            part[rec * 2 + 1] = su;
+        }
     }
 }
 

@@ -2,12 +2,14 @@
 //
 // Two state representations are used:
 //
-//   Carry (a, b, P): the two sums of the recursive form of formula (8)
+//   Carry (a, b, a', b', P): the two sums of the recursive form of formula (8)
 //     ("RWKV解读：在Transformer的时代的新RNN", section 二.3),
 //       A_t = sum_{i<t} e^{-(t-1-i)w + k_i} v_i,   B_t = sum_{i<t} e^{-(t-1-i)w + k_i},
-//     held as A = a 2^P, B = b 2^P with a, b in fp32 and the base-2 log-scale P in fp64.
-//     Carries move between 32-token chunks; keeping P in fp64 means thousands of decay
-//     steps (P -= L w log2 e) add no rounding drift to the relative weight of old tokens.
+//     and their age-weighted versions, held as A = a 2^P etc. with the base-2 log-scale P,
+//     all fp64. Carries move between 32-token chunks and across whole sequences; in fp64
+//     their rounding cannot build up over thousands of folds, and dw (a sum whose terms
+//     cancel heavily) needs them, and the weights e^{k_i - ref} inside them, far more
+//     accurate than fp32.
 //
 //   Rs (a, b, p): the same sums per token, A = a e^p, B = b e^p, fp32, natural log-scale.
 //     Used by the decode step (whose state the public API exposes) and by the exact
@@ -57,36 +59,88 @@ __device__ __forceinline__ void bstore(rsrc_t r, float x, int voff, int soff) {
 }
 
 // ---------------------------------------------------------------------------------
-// Carry (a, b, P), base 2.
+// fp64 power of two.
 // ---------------------------------------------------------------------------------
+// 2^x for |x| <= 1100 (clamped; 2^-1100 is 0 in fp64). x = n + f with n = rint(x) and
+// |f| <= 1/2, 2^f = e^{f ln 2} by its Taylor series to degree 10 (truncation below
+// (ln2/2)^11/11! = 2.2e-13 relative), then the exponent n is applied exactly.
+__device__ __forceinline__ double exp2_64(double x) {
+    x = fmin(fmax(x, -1100.0), 1100.0);
+    const double n = rint(x);
+    const double f = x - n;  // exact
+    constexpr double l1 = kLn2D;
+    constexpr double l2 = l1 * kLn2D / 2.0;
+    constexpr double l3 = l2 * kLn2D / 3.0;
+    constexpr double l4 = l3 * kLn2D / 4.0;
+    constexpr double l5 = l4 * kLn2D / 5.0;
+    constexpr double l6 = l5 * kLn2D / 6.0;
+    constexpr double l7 = l6 * kLn2D / 7.0;
+    constexpr double l8 = l7 * kLn2D / 8.0;
+    constexpr double l9 = l8 * kLn2D / 9.0;
+    constexpr double l10 = l9 * kLn2D / 10.0;
+    double p = l10;
+    p = fma(p, f, l9);
+    p = fma(p, f, l8);
+    p = fma(p, f, l7);
+    p = fma(p, f, l6);
+    p = fma(p, f, l5);
+    p = fma(p, f, l4);
+    p = fma(p, f, l3);
+    p = fma(p, f, l2);
+    p = fma(p, f, l1);
+    p = fma(p, f, 1.0);
+    return ldexp(p, (int)n);
+}
+
+// ---------------------------------------------------------------------------------
+// Carry (a, b, a', b', P), base 2, fp64.
+// ---------------------------------------------------------------------------------
+// Besides A and B the carry holds the age-weighted sums that w's gradient needs,
+//   A'_t = sum_{i<t} (t-1-i) e^{-(t-1-i)w + k_i} v_i,   B'_t likewise without v_i,
+// which advance as A'_{t+1} = e^{-w} (A'_t + A_t). All four share the scale 2^P.
 struct Carry {
-    float a, b;
+    double a, b, ap, bp;
     double P;
 };
 
-// c <- c decayed by 2^{-dec}, plus a summary (al, be) at scale 2^{sc}. The larger of the
-// two scales becomes the new one, so every factor applied is <= 1.
-__device__ __forceinline__ void fold(Carry &c, float al, float be, double sc, double dec) {
+// c <- c advanced over `len` tokens (decay 2^{-dec}, dec = len w log2 e) plus the summary
+// s of those tokens taken from the empty state. The larger of the two scales becomes the
+// new one, so every factor applied is <= 1.
+__device__ __forceinline__ void fold(Carry &c, const Carry &s, double dec, double len) {
     const double Pd = c.P - dec;
-    const float d = (float)(sc - Pd);
-    const float f = ex2(-fabsf(d));
-    const bool up = d >= 0.0f;
-    const float ca = up ? f : 1.0f;
-    const float cs = up ? 1.0f : f;
-    c.a = fmaf(c.a, ca, al * cs);
-    c.b = fmaf(c.b, ca, be * cs);
-    c.P = up ? sc : Pd;
+    const double d = s.P - Pd;
+    const double f = exp2_64(-fabs(d));
+    const bool up = d >= 0.0;
+    const double ca = up ? f : 1.0;
+    const double cs = up ? 1.0 : f;
+    const double a = c.a, b = c.b;
+    c.a = fma(a, ca, s.a * cs);
+    c.b = fma(b, ca, s.b * cs);
+    c.ap = fma(fma(len, a, c.ap), ca, s.ap * cs);
+    c.bp = fma(fma(len, b, c.bp), ca, s.bp * cs);
+    c.P = up ? s.P : Pd;
 }
+
+__device__ __forceinline__ Carry carry_empty() { return Carry{0.0, 0.0, 0.0, 0.0, kNegBigD}; }
 
 // Move a carry's scale so that b lies in [1, 2) (exact: a power-of-two rescale), so that
 // the scale P says how large the mass is. Empty carries are left alone.
 __device__ __forceinline__ void normalize(Carry &c) {
-    if (c.b > 0.0f) {
-        const int e = __builtin_amdgcn_frexp_expf(c.b) - 1;
-        c.a = ldexpf(c.a, -e);
-        c.b = ldexpf(c.b, -e);
+    if (c.b > 0.0) {
+        const int e = __builtin_amdgcn_frexp_exp(c.b) - 1;
+        c.a = ldexp(c.a, -e);
+        c.b = ldexp(c.b, -e);
+        c.ap = ldexp(c.ap, -e);
+        c.bp = ldexp(c.bp, -e);
         c.P += (double)e;
     }
+}
+
+// 1/x in fp64 from the fp32 reciprocal and one Newton step (relative error ~1e-14 for x
+// in the fp32 normal range, which the callers guarantee).
+__device__ __forceinline__ double rcpd(double x) {
+    const double r0 = (double)rcpf((float)x);
+    return fma(r0, fma(-x, r0, 1.0), r0);
 }
 
 // ---------------------------------------------------------------------------------

@@ -15,8 +15,9 @@
 //
 // Per chunk, with frame ref = max_j k_j of the lane's chunk and e_j = e^{k_j - ref} <= 1:
 //   phase 1  summary from the empty state: S = sum_j e^{-(CH-1-j)w} e_j v_j, Z likewise
-//            without v (Horner with the fp32 factor e^{-w}: at most CH steps, so its
-//            rounding cannot compound); the chunk adds S 2^{ref log2 e} to A and Z to B.
+//            without v, and the age-weighted S', Z' (Horner, fp64, e_j from an fp64 exp2:
+//            the carries also serve the backward pass, whose dw needs them that exact);
+//            the chunk adds S 2^{ref log2 e} to A, Z to B and S', Z' to A', B'.
 //   window   summaries go to LDS; after one barrier every wave folds the NW summaries in
 //            order from the empty state (identical arithmetic in every wave), giving its own
 //            chunk's local incoming carry and the window aggregate. Carries keep their
@@ -27,9 +28,9 @@
 //            aggregate recomputed from k, v here, so no unit ever blocks on another). The
 //            window's inclusive carry is published for its successors and kept for the
 //            backward pass.
-//   phase 3  outputs from the incoming carry put into the chunk frame:
+//   phase 3  outputs from the incoming carry put into the chunk frame, in fp32:
 //            y_j = (S_j + e^u e_j v_j) / (Z_j + e^u e_j),  S_{j+1} = e^{-w} S_j + e_j v_j.
-// One exp2 per element in each phase, one reciprocal in phase 3.
+// One fp64 exp2 per element in phase 1, one fp32 reciprocal per element in phase 3.
 //
 // The fixed frame is exact in real arithmetic but can underflow when k varies by more
 // than ~70 inside one chunk, or overflow when the incoming carry exceeds the chunk frame
@@ -40,6 +41,27 @@
 
 namespace wkvdev {
 
+// Window staging of chunk summaries (one per wave) for the in-window fold.
+template <int NW>
+struct FwdShared {
+    double a[NW][64], b[NW][64], ap[NW][64], bp[NW][64], P[NW][64];
+    int status[2];
+};
+
+template <int NW>
+__device__ __forceinline__ void stage(FwdShared<NW> &sh, int q, int lane, const Carry &c) {
+    sh.a[q][lane] = c.a;
+    sh.b[q][lane] = c.b;
+    sh.ap[q][lane] = c.ap;
+    sh.bp[q][lane] = c.bp;
+    sh.P[q][lane] = c.P;
+}
+
+template <int NW>
+__device__ __forceinline__ Carry staged(const FwdShared<NW> &sh, int q, int lane) {
+    return Carry{sh.a[q][lane], sh.b[q][lane], sh.ap[q][lane], sh.bp[q][lane], sh.P[q][lane]};
+}
+
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
@@ -47,10 +69,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
     Rec *__restrict__ agg, Rec *__restrict__ incl) {
     constexpr int WIN = NW * CH;
-    __shared__ float s_al[NW][64];
-    __shared__ float s_be[NW][64];
-    __shared__ double s_sc[NW][64];
-    __shared__ int s_status[2];
+    __shared__ FwdShared<NW> sh;
 
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -66,37 +85,37 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const float wc = w[cl];
     const float uc = u[cl];
     const Decay dc = make_decay(wc);
+    const double wd = (double)wc;
+    const double dwfd = exp(-wd);
     const float eu = expf(uc);
-    const double w2 = (double)wc * kLog2eD;
+    const double cw2 = (double)CH * wd * kLog2eD;
+    const double ww2 = (double)WIN * wd * kLog2eD;
     const bool slow_wave = wave_any(!(fabsf(uc) <= 60.0f));
 
     const int64_t row0 = bidx * T;
     const int64_t t0 = s * WIN + (int64_t)q * CH;
-    const int Lv = (int)(t0 >= T ? 0 : (T - t0 < CH ? T - t0 : CH));
+    const int Lv = chunk_len(t0, T, CH);
 
     // ---- phase 1: frame and summary of this wave's chunk ----
     float kc[CH], vc[CH];
     load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     const float ref = chunk_ref<CH>(kc, Lv);
-    float S, Z;
-    double sc;
-    bool exact = chunk_summary<CH>(kc, vc, Lv, ref, slow_wave, dc, S, Z, sc);
+    Carry sum;
+    bool exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, sum);
     if (exact) {
         load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        exact_summary<CH>(kc, vc, Lv, ref, dc, S, Z, sc);
+        exact_summary<CH>(kc, vc, Lv, ref, wd, sum);
     }
 
     // ---- window: local carries and aggregate ----
-    s_al[q][lane] = S;
-    s_be[q][lane] = Z;
-    s_sc[q][lane] = sc;
+    stage(sh, q, lane, sum);
     __syncthreads();
-    Carry run{0.0f, 0.0f, kNegBigD};
+    Carry run = carry_empty();
     Carry lexcl = run;
 #pragma unroll
     for (int qq = 0; qq < NW; ++qq) {
         if (qq == q) lexcl = run;
-        fold(run, s_al[qq][lane], s_be[qq][lane], s_sc[qq][lane], (double)CH * w2);
+        fold(run, staged(sh, qq, lane), cw2, (double)CH);
     }
     const int64_t rec = (bidx * nseg + s) * C + cl;
     uint64_t *myflag = flags + s * nbg + bg;
@@ -110,7 +129,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // start), making sure every window in between has its aggregate in memory; then fold
     // those aggregates forward in order. The result is bitwise the sequential chain
     // incl[s] = fold(incl[s-1], agg[s]) whatever the timing, so every run is deterministic.
-    Carry prefix{0.0f, 0.0f, kNegBigD};
+    Carry prefix = carry_empty();
     bool own_clobbered = false;
     if (s > 0) {
         int64_t j = s - 1;
@@ -118,10 +137,10 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         for (;;) {
             if (q == 0) {
                 const int st = poll_flag(flags + j * nbg + bg, epoch, kPollTries);
-                if (lane == 0) s_status[it & 1] = st;
+                if (lane == 0) sh.status[it & 1] = st;
             }
             __syncthreads();
-            const int st = s_status[it & 1];
+            const int st = sh.status[it & 1];
             ++it;
             if (st == (int)kInclusive) break;
             if (st != (int)kAggregate) {
@@ -132,21 +151,17 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
                 load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
                 own_clobbered = true;
                 const float rj = chunk_ref<CH>(kc, Lj);
-                float Sj, Zj;
-                double scj;
-                if (chunk_summary<CH>(kc, vc, Lj, rj, slow_wave, dc, Sj, Zj, scj)) {
+                Carry sj;
+                if (chunk_summary<CH, false>(kc, vc, Lj, rj, slow_wave, dwfd, sj)) {
                     load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
-                    exact_summary<CH>(kc, vc, Lj, rj, dc, Sj, Zj, scj);
+                    exact_summary<CH>(kc, vc, Lj, rj, wd, sj);
                 }
                 __syncthreads();
-                s_al[q][lane] = Sj;
-                s_be[q][lane] = Zj;
-                s_sc[q][lane] = scj;
+                stage(sh, q, lane, sj);
                 __syncthreads();
-                Carry X{0.0f, 0.0f, kNegBigD};
+                Carry X = carry_empty();
 #pragma unroll
-                for (int qq = 0; qq < NW; ++qq)
-                    fold(X, s_al[qq][lane], s_be[qq][lane], s_sc[qq][lane], (double)CH * w2);
+                for (int qq = 0; qq < NW; ++qq) fold(X, staged(sh, qq, lane), cw2, (double)CH);
                 if (q == 0) {
                     if (cval) put_rec(agg + (bidx * nseg + j) * C + cl, X);
                     raise_flag(flags + j * nbg + bg, epoch, kAggregate);
@@ -162,35 +177,34 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         // j is the window with a published inclusive carry, or -1
         if (j >= 0) prefix = get_rec(incl + (bidx * nseg + j) * C + cl);
         for (int64_t m = j + 1; m < s; ++m)
-            prefix = follow(prefix, get_rec(agg + (bidx * nseg + m) * C + cl), (double)WIN * w2);
+            prefix = follow(prefix, get_rec(agg + (bidx * nseg + m) * C + cl), ww2, (double)WIN);
     }
     if (q == 0) {
-        if (cval) put_rec(incl + rec, follow(prefix, run, (double)WIN * w2));
+        if (cval) put_rec(incl + rec, follow(prefix, run, ww2, (double)WIN));
         put_flag(myflag, epoch, kInclusive);
     }
     if (y == nullptr) return;
 
     // ---- phase 3: outputs ----
-    Carry mine = follow(prefix, lexcl, (double)(q * CH) * w2);
+    Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
     if (own_clobbered) {
         load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
         if (!exact) {
-            float S2, Z2;
-            double sc2;
-            exact = chunk_summary<CH>(kc, vc, Lv, ref, slow_wave, dc, S2, Z2, sc2);
+            Carry s2;
+            exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, s2);
             if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
         }
     }
+    const double ref2 = (double)ref * kLog2eD;
     if (!exact) {
-        const float ref2 = ref * kLog2e;
-        const float gap = (float)(mine.P - (double)ref2);
-        bool bad = gap > kCarryGap;
-        const float s0 = ex2(gap);
-        float Sx = mine.a * s0, Zx = mine.b * s0;
+        const double gap = mine.P - ref2;
+        bool bad = gap > (double)kCarryGap;
+        const double s0 = exp2_64(gap);
+        float Sx = (float)(mine.a * s0), Zx = (float)(mine.b * s0);
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const float e = kc[j], ev = vc[j];
+            const float e = kc[j], ev = e * vc[j];
             const float num = fmaf(eu, ev, Sx);
             const float den = fmaf(eu, e, Zx);
             if (j < Lv) bad |= !(den >= kTinyDen);
@@ -202,8 +216,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     }
     if (exact) {
-        const float ref2 = ref * kLog2e;
-        Rs st{mine.a, mine.b, (float)((mine.P - (double)ref2) * kLn2D)};
+        Rs st{(float)mine.a, (float)mine.b, (float)((mine.P - ref2) * kLn2D)};
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             if (j < Lv) {

@@ -16,10 +16,11 @@ constexpr uint64_t kAggregate = 1;
 constexpr uint64_t kInclusive = 2;
 constexpr int kPollTries = 2000;  // bounded wait before a missing aggregate is recomputed
 
-// A carry or window summary as published: A = a 2^P, B = b 2^P (a, b packed in `ab`).
+// A carry or window summary as published: A = a 2^P, B = b 2^P and the age-weighted
+// A' = a' 2^P, B' = b' 2^P (fp64 bits each).
 struct Rec {
-    uint64_t ab;
-    uint64_t P;  // fp64 bits
+    uint64_t a, b, ap, bp;
+    uint64_t P;
 };
 
 // Forward workspace, carved out of the caller's buffer (see wkv_api.hip):
@@ -34,14 +35,11 @@ struct FwdLayout {
 };
 
 // A reverse carry or reverse window summary as published: the future sums
-//   G = sum_{t>=t0} e^{-(t-t0)w} s_t,  H = same with s_t y_t,
-//   G' = sum_{t>=t0} (t-t0) e^{-(t-t0)w} s_t,  H' = same with s_t y_t
-// (s_t = dy_t / D_t), held as (g, h, gp, hp) 2^r with fp32 mantissas and an fp64 scale.
+//   G = sum_{t>=t0} e^{-(t-t0)w} s_t,  H = same with s_t y_t
+// (s_t = dy_t / D_t), held as (g, h) 2^r (fp64 bits each).
 struct RevRec {
-    uint64_t gh;    // g, h (fp32 bits)
-    uint64_t gphp;  // gp, hp (fp32 bits)
-    uint64_t r;     // fp64 bits
-    uint64_t pad;
+    uint64_t g, h;
+    uint64_t r;
 };
 
 // Backward workspace:

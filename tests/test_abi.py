@@ -49,9 +49,9 @@ def test_sizes(pkg):
     lib = pkg.load_library()
     B, T, C = 8, 4096, 2560
     nseg, ngrp = 16, 40
-    fwd = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 16)
+    fwd = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 40)
     assert lib.wkv_forward_workspace_size(B, T, C) == fwd
-    own = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 32) + _r256(B * nseg * C * 16)
+    own = _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 24) + _r256(B * nseg * C * 16)
     assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
     assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
     assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 256
