@@ -1,0 +1,315 @@
+"""Throughput of the WKV operator (RWKV-4 time mixing) on one MI355X.
+
+A step is one forward and one backward pass over one batch of the 3B-class layer shape
+(B=8, T=4096, C=2560, fp32): wkv_forward fills y and its workspace, wkv_backward reads
+that workspace and writes dk, dv, dw, du. Inputs are synthetic and seeded (the
+distributions of the 3B-class layer workload in wkv_inputs.py) and resident in HBM
+before timing starts; the step reuses preallocated outputs and workspaces.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
+`roofline` describes the kernel that takes most of the step, with its algorithmic bytes
+(20 B per element for the backward: k, v, dy read, dk, dv written; 12 B for the
+forward: k, v read, y written) over its mean duration from HIP events on the stream the
+library launches on. `traffic` comes from a committed rocprofv3 counter summary and is
+reported only while the kernel sources still hash to the value recorded there.
+`cpu_baseline` times the fp64 CPU oracle (test infrastructure, OpenMP over all host
+threads) on the same workload. `decode` reports the batched decode step separately
+(B=256, C=5120, 40 layer states, 36 B per element per call).
+
+Helpers for the counter summaries:
+    python bench.py --with-copy ...        also runs a 1 GiB device copy (known bytes)
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR
+        reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` output folders of a
+        `--with-copy` run and prints the summary JSON (per-dispatch KiB, copy scaling).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG_DIR = os.path.join(HERE, "rwkv_linear_attention_forward_amd")
+CSRC = os.path.join(PKG_DIR, "csrc")
+COUNTERS = os.path.join(HERE, "profiles", "wkv_l3b_counters.json")
+METRIC = ("WKV fwd+bwd elements/sec (B·T·C) and achieved HBM GB/s vs peak, "
+          "T=4096 C=2560")
+PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30
+KERNELS = {"forward": "wkv_forward_kernel", "backward": "wkv_backward_kernel"}
+BYTES_PER_ELEM = {"forward": 12, "backward": 20}
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources (csrc/*.hip, *.h), in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# ---------------------------------------------------------------------------------------
+# counter summaries
+# ---------------------------------------------------------------------------------------
+def _read_counter_rows(folder):
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit("no *counter_collection.csv under %s" % folder)
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel_name: [value per dispatch]} for one counter (values summed per dispatch)."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r.get("Dispatch_Id"), r.get("Kernel_Name"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (_, name), val in per.items():
+        out.setdefault(name, []).append(val)
+    return out
+
+
+def _match(per, needle):
+    vals = [v for name, vs in per.items() if needle in name for v in vs]
+    return statistics.median(vals) if vals else None
+
+
+def summarize_counters(fetch_dir, write_dir):
+    fetch = _per_dispatch(_read_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_read_counter_rows(write_dir), "WRITE_SIZE")
+    # the copy kernel: the dispatch whose counters are closest to 1 GiB each way
+    copy_f = max(v for vs in fetch.values() for v in vs)
+    copy_w = max(v for vs in write.values() for v in vs)
+    out = {"source_sha256": source_hash(),
+           "copy_kib_expected": COPY_BYTES / 1024,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "fetch_scale": (COPY_BYTES / 1024) / copy_f,
+           "write_scale": (COPY_BYTES / 1024) / copy_w,
+           "kernels": {}}
+    for op, name in KERNELS.items():
+        f, w = _match(fetch, name), _match(write, name)
+        if f is not None and w is not None:
+            out["kernels"][op] = {"fetch_kib": f, "write_kib": w,
+                                  "traffic_bytes": 1024 * (f * out["fetch_scale"]
+                                                           + w * out["write_scale"])}
+    return out
+
+
+def counter_traffic(op):
+    """HBM bytes per launch of `op` from the committed counter summary, or None if absent or
+    taken on different kernel sources."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(op)
+    return None if k is None else k["traffic_bytes"]
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the same workload
+# ---------------------------------------------------------------------------------------
+def cpu_baseline(x, budget_s=10.0, max_runs=3):
+    import oracle
+    B, T, C = x["k"].shape
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs:
+        t0 = time.perf_counter()
+        oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
+        oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    t = statistics.median(times)
+    return {"value": B * T * C / t, "unit": "elem/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "full workload B=%d T=%d C=%d, fp64 plain recurrence forward + linear-time "
+                      "backward (OpenMP over b, c), median of %d runs" % (B, T, C, len(times))}
+
+
+# ---------------------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------------------
+def bench_step(wkv, torch, dev, x, steps, warmup):
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v", "dy")}
+    B, T, C = t["k"].shape
+    fws = wkv.forward_workspace(B, T, C, dev)
+    bws = torch.empty(max(16, wkv.backward_workspace_size(B, T, C, True)), dtype=torch.uint8,
+                      device=dev)
+    y = torch.empty_like(t["k"])
+    outs = (torch.empty_like(t["k"]), torch.empty_like(t["k"]), torch.empty_like(t["w"]),
+            torch.empty_like(t["u"]))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wkv.forward(t["w"], t["u"], t["k"], t["v"], workspace=fws, out=y)
+        if ev is not None:
+            ev[1].record()
+        wkv.backward(t["w"], t["u"], t["k"], t["v"], t["dy"], fwd_workspace=fws, workspace=bws,
+                     out=outs)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    span_ms = evs[0][0].elapsed_time(evs[-1][2])
+    ok = all(bool(torch.isfinite(a).all()) for a in (y,) + outs)
+    return {"B": B, "T": T, "C": C, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "span_ms": span_ms,
+            "wall_s": wall, "finite": ok}
+
+
+def bench_copy(torch, dev, reps=3):
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        ms.append(e0.elapsed_time(e1))
+    return {"bytes": 2 * COPY_BYTES, "ms": statistics.median(ms),
+            "gbps": 2 * COPY_BYTES / (statistics.median(ms) * 1e-3) / 1e9}
+
+
+def bench_decode(wkv, torch, dev, steps=20, warmup=3):
+    import wkv_inputs
+    cfg = wkv_inputs.DECODE
+    B, C, L = cfg["B"], cfg["C"], cfg["layers"]
+    params = [wkv_inputs.decode_layer_params(l) for l in range(L)]
+    w = [torch.from_numpy(pw).to(dev) for pw, _ in params]
+    u = [torch.from_numpy(pu).to(dev) for _, pu in params]
+    st = [tuple(torch.from_numpy(a).to(dev) for a in wkv_inputs.empty_decode_state(B, C))
+          for _ in range(L)]
+    y = torch.empty(B, C, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+    ms = []
+    for s in range(warmup + steps):
+        kv = torch.randn(L, 2, B, C, dtype=torch.float32, device=dev, generator=gen)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(L):
+            a, b, p = st[l]
+            wkv.decode_step(w[l], u[l], kv[l, 0], kv[l, 1], a, b, p, out=y)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        if s >= warmup:
+            ms.append(e0.elapsed_time(e1))
+    per_call_us = statistics.median(ms) * 1e3 / L
+    gbps = 36 * B * C / (per_call_us * 1e-6) / 1e9
+    return {"workload": "batched decode B=%d C=%d, %d layer states, k, v ~ N(0,1)" % (B, C, L),
+            "us_per_call": per_call_us, "elem_per_s": B * C / (per_call_us * 1e-6),
+            "algorithmic_gbps": gbps, "frac_of_peak": gbps / PEAK_GBPS, "steps": steps,
+            "calls_per_step": L}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the WKV path here runs on a single device "
+              "(--gpus %d, WORLD_SIZE %d requested); run with --gpus 1" % (args.gpus, world),
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    sys.path.insert(0, HERE)
+    import numpy as np  # noqa: F401
+    import torch
+    import rwkv_linear_attention_forward_amd as wkv
+    import wkv_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    x = wkv_inputs.generate("l3b", with_dy=True)
+    r = bench_step(wkv, torch, dev, x, args.steps, args.warmup)
+    B, T, C = r["B"], r["T"], r["C"]
+    n = B * T * C
+    ms_per_step = r["span_ms"] / args.steps
+    fwd = statistics.mean(r["fwd_ms"])
+    bwd = statistics.mean(r["bwd_ms"])
+    op = "backward" if bwd >= fwd else "forward"
+    dur_ms = bwd if op == "backward" else fwd
+    alg = BYTES_PER_ELEM[op] * n
+    achieved = alg / (dur_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": n / (ms_per_step * 1e-3), "unit": "elem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "3B-class layer WKV forward+backward", "B": B, "T": T, "C": C,
+                   "dist": "k,v,dy ~ N(0,1); w = exp(U(-8,2)); u ~ U(-1,1)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": KERNELS[op], "achieved": achieved,
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": achieved / PEAK_GBPS,
+                     "traffic": counter_traffic(op), "algorithmic_bytes": alg,
+                     "mean_launch_us": dur_ms * 1e3},
+        "step_gbps": 32 * n / (ms_per_step * 1e-3) / 1e9,
+        "kernels_us": {"forward_mean": fwd * 1e3, "forward_min": min(r["fwd_ms"]) * 1e3,
+                       "backward_mean": bwd * 1e3, "backward_min": min(r["bwd_ms"]) * 1e3},
+        "forward_frac_of_peak": 12 * n / (fwd * 1e-3) / 1e9 / PEAK_GBPS,
+        "outputs_finite": r["finite"],
+    }
+    if args.with_copy:
+        out["copy_1gib"] = bench_copy(torch, dev)
+    if not args.no_decode:
+        out["decode"] = bench_decode(wkv, torch, dev)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

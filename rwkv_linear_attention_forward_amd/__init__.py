@@ -160,9 +160,10 @@ def backward_workspace_size(B: int, T: int, C: int, have_fwd_workspace: bool) ->
     return int(load_library().wkv_backward_workspace_size(B, T, C, 1 if have_fwd_workspace else 0))
 
 
-def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None):
+def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
     """(dk, dv, dw, du) of sum(dy * y). `fwd_workspace` is the workspace forward() filled for
-    the same inputs (optional: without it the window states are recomputed)."""
+    the same inputs (optional: without it the window states are recomputed). `out` may hold
+    preallocated (dk, dv, dw, du)."""
     B, T, C, dev = _check_btc(w, u, k, v)
     _need(dy, "dy", 3, dev)
     if dy.shape != k.shape:
@@ -174,10 +175,15 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None):
     if workspace is None or workspace.numel() < wsz:
         workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
     _check_ws(workspace, dev, "workspace")
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(k)
-    dw = torch.empty_like(w)
-    du = torch.empty_like(u)
+    if out is None:
+        dk, dv, dw, du = torch.empty_like(k), torch.empty_like(k), torch.empty_like(w), \
+            torch.empty_like(u)
+    else:
+        dk, dv, dw, du = out
+        for t, n, ref in ((dk, "dk", k), (dv, "dv", k), (dw, "dw", w), (du, "du", u)):
+            _need(t, n, ref.dim(), dev)
+            if t.shape != ref.shape:
+                raise ValueError("%s has the wrong shape" % n)
     _check(lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
                             _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
                             _ptr(workspace), workspace.numel(), _stream(dev)))

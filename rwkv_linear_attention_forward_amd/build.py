@@ -19,9 +19,13 @@ LIB = os.path.join(PKG, "librwkv_wkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 out of scalar fp32 code.
+# -ffp-contract=off: fused multiply-adds only where the source writes fma(), so that the same
+# expression gives the same bits wherever it is inlined (a look-back helper must reproduce
+# a unit's published summary exactly).
 # The host pass prints that it does not know the feature; that warning is harmless.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

@@ -113,12 +113,16 @@ int check_device(const char *fn) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
+int64_t nchunk_of(int64_t T) { return (T + wkvdev::kFwdChunk - 1) / wkvdev::kFwdChunk; }
+int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
-// Forward workspace: flags, aggregates, inclusive carries (see wkv_launch.h).
+// Forward workspace: flags, aggregates, inclusive carries, chunk carries (see wkv_launch.h).
 size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
-    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256);
+    const size_t cin = (size_t)B * (size_t)nchunk_of(T) * (size_t)C * 5u * sizeof(double);
+    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256) +
+           round_up(cin, 256);
 }
 
 wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
@@ -127,26 +131,31 @@ wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
     char *p = static_cast<char *>(ws);
     L.nseg = (int64_t)nseg;
+    L.nchunk = nchunk_of(T);
     L.flags = reinterpret_cast<uint64_t *>(p);
     p += round_up((size_t)B * ngrp * nseg * 8u, 256);
     L.agg = reinterpret_cast<wkvdev::Rec *>(p);
     p += round_up(recs, 256);
     L.incl = reinterpret_cast<wkvdev::Rec *>(p);
+    p += round_up(recs, 256);
+    L.cin = reinterpret_cast<double *>(p);
     return L;
 }
 
 // Backward workspace: flags, reverse aggregates, reverse inclusive carries, per-window dw/du
-// partials, then (without a forward workspace) a forward workspace of its own.
+// partials, arrival counters, then (without a forward workspace) a forward workspace of
+// its own.
 size_t bwd_own_bytes(int64_t B, int64_t T, int64_t C) {
-    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t nseg = (size_t)bseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t n = (size_t)B * nseg * (size_t)C;
-    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(n * sizeof(wkvdev::RevRec), 256) +
-           round_up(n * 2 * sizeof(double), 256);
+    return round_up((size_t)B * ngrp * nseg * 8u, 256) +
+           2 * round_up(n * sizeof(wkvdev::RevRec), 256) + round_up(n * 2 * sizeof(double), 256) +
+           round_up(ngrp * 8u, 256);
 }
 
 wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     wkvdev::BwdLayout L;
-    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t nseg = (size_t)bseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t n = (size_t)B * nseg * (size_t)C;
     char *p = static_cast<char *>(ws);
     L.nseg = (int64_t)nseg;
@@ -156,7 +165,9 @@ wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     p += round_up(n * sizeof(wkvdev::RevRec), 256);
     L.rincl = reinterpret_cast<wkvdev::RevRec *>(p);
     p += round_up(n * sizeof(wkvdev::RevRec), 256);
-    L.part = reinterpret_cast<double *>(p);
+    L.part = reinterpret_cast<uint64_t *>(p);
+    p += round_up(n * 2 * sizeof(double), 256);
+    L.ctr = reinterpret_cast<uint64_t *>(p);
     return L;
 }
 
@@ -179,6 +190,18 @@ bool grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
     const int64_t units = B * ((C + 63) / 64) * nseg_of(T);
     if (units > INT32_MAX) {
         fail(WKV_ERR_INVALID_ARG, "%s: %lld workgroups exceed 2^31-1", fn, (long long)units);
+        return false;
+    }
+    return true;
+}
+
+// The backward's arrival counters count B * ceil(T / window) units per channel group.
+bool bwd_grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
+    if (!grid_ok(B, T, C, fn)) return false;
+    const int64_t per_group = B * bseg_of(T);
+    if (per_group >= (int64_t(1) << wkvdev::kCountBits)) {
+        fail(WKV_ERR_INVALID_ARG, "%s: B*ceil(T/%d)=%lld exceeds 2^%d-1", fn, wkvdev::kBwdWindow,
+             (long long)per_group, wkvdev::kCountBits);
         return false;
     }
     return true;
@@ -269,7 +292,7 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
         if (e != hipSuccess) return fail_hip(e, fn);
         return WKV_OK;
     }
-    if (!grid_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (!bwd_grid_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     const void *ptrs[9] = {w, u, k, v, dy, dk, dv, workspace, nullptr};
     const char *names[9] = {"w", "u", "k", "v", "dy", "dk", "dv", "workspace", ""};
     for (int i = 0; i < 8; ++i)
@@ -308,7 +331,7 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
         hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, F, next_epoch(), st);
         if (e != hipSuccess) return fail_hip(e, fn);
     }
-    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, F.incl, dk, dv, dw, du,
+    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, F, dk, dv, dw, du,
                                            bwd_layout(B, T, C, own), next_epoch(), st);
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;

@@ -92,241 +92,240 @@ __device__ __forceinline__ RevCarry get_rrec(const RevRec *p) {
 }
 
 // ---------------------------------------------------------------------------------
-// Exact per-token backward of one lane's chunk (tokens [0, Lv)), for chunks whose fixed
-// frame would under- or overflow (a dominant key next to much smaller ones, extreme u).
-// Everything is fp64 with library exponentials. On entry kc, vc, gc hold the raw k, v,
-// dy; gc and yc are clobbered. `fin` is the forward carry entering the chunk, `rin` the
-// future sums at the chunk's nominal end. The chunk is swept in quarters from the last
-// one: for each quarter the forward recursion is rerun from `fin` (adding the dw, du
-// terms of the quarter's tokens if FG) and that quarter's per-token y and log-scale of D
-// (each as a float pair, about 48 bits) and dy / den are kept in yc and gc; then the
-// quarter is swept backwards (storing dk, dv if OUT). Returns the future sums at the
-// chunk start.
+// Exact per-token backward of one lane's chunk (tokens [0, Lv) from t0), for chunks whose
+// fixed frame would under- or overflow (a dominant key next to much smaller ones, extreme
+// u). Everything is fp64 with library exponentials. It reads k, v, dy straight from
+// memory in loops that are not unrolled (per-token values of the forward sweep go to
+// private arrays), so that this rare path holds few registers wherever it is inlined. `fin` is the forward carry
+// entering the chunk, `rin` the future sums at the chunk's nominal end (CH tokens on).
+// The forward sweep adds the chunk's dw, du terms if FG; the reverse sweep stores dk, dv
+// if OUT. Returns the future sums at the chunk start.
 // ---------------------------------------------------------------------------------
 struct RevState64 {  // (G, H) = (g, h) e^{r - ref}
     double g, h, r;
 };
 
-template <int CH, int QS, bool OUT, bool FG>
-__device__ __forceinline__ void exact_quarter(const float (&kc)[CH], const float (&vc)[CH],
-                                              float (&gc)[CH], float (&yc)[CH], int Lv,
-                                              double ref, double uc, double wc,
-                                              const Rs64 &st0, RevState64 &rs, rsrc_t rdk,
-                                              rsrc_t rdv, int voff, int stride, bool st_ok,
-                                              double &du_acc, double &dw_acc) {
-    constexpr int Q = CH / 4;  // tokens per quarter
-    constexpr int J0 = QS * Q;
-    static_assert(4 * Q <= CH, "yc holds y and M of one quarter, each as a float pair");
-    Rs64 st = st0;
-#pragma unroll
-    for (int j = 0; j < J0; ++j)
-        if (j < Lv) rs64_push(st, (double)kc[j] - ref, (double)vc[j], wc);
-#pragma unroll
-    for (int j = J0; j < J0 + Q; ++j) {
-        if (j < Lv) {
-            const double kr = (double)kc[j] - ref, vv = (double)vc[j];
-            const double uk = uc + kr;
-            const double m = fmax(st.p, uk);
-            const double e1 = exp(st.p - m), e2 = exp(uk - m);
-            const double rden = 1.0 / fma(e1, st.b, e2);
-            const double yv = fma(e1, st.a, e2 * vv) * rden;
-            const double sg = (double)gc[j] * rden;  // dy / D in units of e^{-(m + ref)}
-            if (FG) {
-                // s (A' - y B') and s e^{u+k} (v - y), with A' = a' e^{p+ref}
-                dw_acc = fma(sg * e1, fma(-yv, st.bp, st.ap), dw_acc);
-                du_acc = fma(sg * e2, vv - yv, du_acc);
-            }
-            const float yh = (float)yv;
-            yc[j - J0] = yh;
-            yc[3 * Q + j - J0] = (float)(yv - (double)yh);
-            gc[j] = (float)sg;
-            const float mh = (float)m;
-            yc[Q + j - J0] = mh;
-            yc[2 * Q + j - J0] = (float)(m - (double)mh);
-            rs64_push(st, kr, vv, wc);
-        }
-    }
-#pragma unroll
-    for (int j = J0 + Q - 1; j >= J0; --j) {
-        if (j < Lv) {
-            const double kr = (double)kc[j] - ref, vv = (double)vc[j];
-            const double yy = (double)yc[j - J0] + (double)yc[3 * Q + j - J0];
-            const double sg = (double)gc[j];
-            const double M = (double)yc[Q + j - J0] + (double)yc[2 * Q + j - J0];
-            if (OUT) {
-                const double ekr = exp(kr + rs.r);
-                const double cpi = sg * exp(uc + kr - M);
-                if (st_ok) {
-                    bstore(rdv, (float)fma(ekr, rs.g, cpi), voff, j * stride);
-                    bstore(rdk, (float)fma(cpi, vv - yy, ekr * fma(vv, rs.g, -rs.h)), voff,
-                           j * stride);
-                }
-            }
-            const double a = rs.r - wc, b = -M;
-            const double rn = fmax(a, b);
-            const double fa = exp(a - rn), fb = exp(b - rn);
-            rs.g = fma(rs.g, fa, sg * fb);
-            rs.h = fma(rs.h, fa, sg * yy * fb);
-            rs.r = rn;
-        } else {
-            rs.r -= wc;  // a padded token past T: pure decay (its s is 0)
-        }
-    }
-}
-
 template <int CH, bool OUT, bool FG>
-__device__ RevCarry exact_chunk(const float (&kc)[CH], const float (&vc)[CH], float (&gc)[CH],
-                                float (&yc)[CH], int Lv, float ref, const Carry &fin,
-                                RevCarry rin, float uc, float wc, rsrc_t rdk, rsrc_t rdv,
-                                int voff, int stride, bool st_ok, double &du_acc,
-                                double &dw_acc) {
+__device__ __forceinline__ RevCarry exact_chunk(
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
+    float *__restrict__ dk, float *__restrict__ dv, int64_t row0, int64_t t0, int Lv,
+    int64_t C, int cl, bool st_ok, float ref, const Carry &fin, RevCarry rin, float uc,
+    float wc, double &du_acc, double &dw_acc) {
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;  // the frame 2^{ref2} the carries refer to
-    rnormalize(rin);
     // the carries are relative to 2^{ref2}; the per-token path works relative to e^{ref}
     const double shift = ref2 * kLn2D - refd;
-    const Rs64 st0{fin.a, fin.b, fin.ap, fin.bp, (fin.P - ref2) * kLn2D + shift};
-    RevState64 rs{rin.g, rin.h, (rin.r + ref2) * kLn2D - shift};
     const double u = (double)uc, w = (double)wc;
-    exact_quarter<CH, 3, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
-                                  stride, st_ok, du_acc, dw_acc);
-    exact_quarter<CH, 2, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
-                                  stride, st_ok, du_acc, dw_acc);
-    exact_quarter<CH, 1, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
-                                  stride, st_ok, du_acc, dw_acc);
-    exact_quarter<CH, 0, OUT, FG>(kc, vc, gc, yc, Lv, refd, u, w, st0, rs, rdk, rdv, voff,
-                                  stride, st_ok, du_acc, dw_acc);
+    double ys[CH], ss[CH], ms[CH];
+    Rs64 st{fin.a, fin.b, fin.ap, fin.bp, (fin.P - ref2) * kLn2D + shift};
+#pragma unroll 1
+    for (int j = 0; j < Lv; ++j) {
+        const int64_t i = (row0 + t0 + j) * C + cl;
+        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double uk = u + kr;
+        const double m = fmax(st.p, uk);
+        const double e1 = exp(st.p - m), e2 = exp(uk - m);
+        const double rden = 1.0 / fma(e1, st.b, e2);
+        const double yv = fma(e1, st.a, e2 * vv) * rden;
+        const double sg = (double)dy[i] * rden;  // dy / D in units of e^{-(m + ref)}
+        if (FG) {
+            // s (A' - y B') and s e^{u+k} (v - y), with A' = a' e^{p+ref}
+            dw_acc = fma(sg * e1, fma(-yv, st.bp, st.ap), dw_acc);
+            du_acc = fma(sg * e2, vv - yv, du_acc);
+        }
+        ys[j] = yv;
+        ss[j] = sg;
+        ms[j] = m;
+        rs64_push(st, kr, vv, w);
+    }
+    rnormalize(rin);
+    RevState64 rs{rin.g, rin.h, (rin.r + ref2) * kLn2D - shift};
+    rs.r -= (double)(CH - Lv) * w;  // padded tokens past T: pure decay (their s is 0)
+#pragma unroll 1
+    for (int j = Lv - 1; j >= 0; --j) {
+        const int64_t i = (row0 + t0 + j) * C + cl;
+        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double yy = ys[j], sg = ss[j], M = ms[j];
+        if (OUT) {
+            const double ekr = exp(kr + rs.r);
+            const double cpi = sg * exp(u + kr - M);
+            if (st_ok) {
+                dv[i] = (float)fma(ekr, rs.g, cpi);
+                dk[i] = (float)fma(cpi, vv - yy, ekr * fma(vv, rs.g, -rs.h));
+            }
+        }
+        const double a = rs.r - w, b = -M;
+        const double rn = fmax(a, b);
+        const double fa = exp(a - rn), fb = exp(b - rn);
+        rs.g = fma(rs.g, fa, sg * fb);
+        rs.h = fma(rs.h, fa, sg * yy * fb);
+        rs.r = rn;
+    }
     // G = g e^{r - ref} at the chunk start
     return RevCarry{rs.g, rs.h, (rs.r - refd) * kLog2eD};
 }
 
-// LDS staging shared by the waves of a backward unit (forward summaries use all five
-// arrays, reverse summaries three, the dw, du partials two).
-template <int NW>
+// LDS of a backward unit: staging for the window's reverse summaries and the dw/du
+// partials, and each wave's per-token (sigma_j, y_j) from F3 until its reverse sweep.
+template <int NW, int CH>
 struct BwdShared {
     double a[NW][64];
     double b[NW][64];
-    double c[NW][64];
-    double d[NW][64];
     double r[NW][64];
+    float2 sy[NW][CH][64];
     int status[2];
 };
 
 // Per-channel constants of a backward lane.
 struct BwdConst {
-    double w;       // the decay rate
-    double dwf;     // e^{-w}
-    double eu;      // e^{u}
-    double w2;      // w log2 e
+    double w;        // the decay rate
+    double dwf;      // e^{-w}
+    double eu;       // e^{u}
+    double w2;       // w log2 e
     float uc;
-    bool slow_wave; // some lane has |u| > 60: exact path throughout
+    bool slow_wave;  // some lane has |u| > 60: exact path throughout
 };
 
-// Everything a unit needs about one lane's chunk of window jw, up to its reverse summary:
-// the forward recomputation with the chunk's dw, du terms (F1/F3) and the reverse summary
-// from a zero future (R1). Called by all waves of the workgroup together (it contains a
-// barrier; the caller makes sure nobody still reads the staging arrays). On return with
-// fx == false, kc, vc, gc, yc hold e_j, v_j, sigma_j, y_j; with fx == true (the forward
-// frame failed) they are clobbered and the chunk must take the per-token path again from
-// raw data. Deterministic: the owner of a window and a helper recomputing it get identical
-// bits.
-template <int NW, int CH>
+// One lane's chunk ci (tokens t0 = ci*CH ...): the forward recomputation from the chunk's
+// entering carry (read from the forward's workspace) and, in the same sweep, the chunk's
+// reverse summary from a zero future (R1):
+//   R = sum_j e^{-j w} sigma_j,  Q = sum_j e^{-j w} sigma_j y_j   (future sums at the
+// chunk start, in the chunk frame).
+// Also the chunk's dw, du terms; e_j, v_j are left in kc, vc and (sigma_j, y_j) in `sy`
+// (fp32) for the reverse sweep, unless fx (the fixed frame failed for some lane of the
+// wave; the chunk then takes the per-token path). helper_summary repeats the summary
+// arithmetic op for op, so a helper publishes the bits the owner would (every fused
+// multiply-add is written out; the build does not contract).
+template <int CH>
 __device__ __forceinline__ RevCarry chunk_pass(
-    BwdShared<NW> &sh, int64_t jw, int q, int lane, int64_t T, int64_t C, int64_t nseg,
-    int64_t bidx, int64_t row0, int cl, int voff, int stride, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ dy, const Rec *__restrict__ fincl,
-    const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH], float (&yc)[CH],
-    bool &fx, Carry &mine, float &ref, int &Lv, double &du_acc, double &dw_acc) {
-    const int64_t t0 = jw * (int64_t)(NW * CH) + (int64_t)q * CH;
+    int64_t ci, int64_t T, int64_t C, int64_t nchunk, const double *__restrict__ cin,
+    int64_t ncin, int64_t bidx, int64_t row0, int cl, int voff, int stride,
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
+    const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
+    float2 (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
+    double &dw_acc) {
+    const int64_t t0 = ci * CH;
     Lv = chunk_len(t0, T, CH);
     load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
-
-    // F1: forward summary of the chunk, and the carry entering it
     ref = chunk_ref<CH>(kc, Lv);
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
-    Carry sum;
-    fx = chunk_summary<CH, true>(kc, vc, Lv, ref, K.slow_wave, K.dwf, sum);
-    if (fx) exact_summary<CH>(kc, vc, Lv, ref, K.w, sum);
-    sh.a[q][lane] = sum.a;
-    sh.b[q][lane] = sum.b;
-    sh.c[q][lane] = sum.ap;
-    sh.d[q][lane] = sum.bp;
-    sh.r[q][lane] = sum.P;
-    __syncthreads();
-    mine = carry_empty();
-    if (jw > 0) mine = get_rec(fincl + (bidx * nseg + (jw - 1)) * C + cl);
-    for (int qq = 0; qq < q; ++qq)
-        fold(mine, Carry{sh.a[qq][lane], sh.b[qq][lane], sh.c[qq][lane], sh.d[qq][lane],
-                         sh.r[qq][lane]},
-             (double)CH * K.w2, (double)CH);
-    normalize(mine);
-
-    // F3: y, sigma = dy / den and the dw, du terms in the chunk frame (fp64)
     du_acc = 0.0;
     dw_acc = 0.0;
+    if (Lv == 0) {  // past the sequence end
+        fx = false;
+        return rev_zero();
+    }
+    const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
+    const double gap = fin.P - ref2;
+    fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
+    double R = 0.0, Q = 0.0;
     if (!fx) {
-        const double gap = mine.P - ref2;
-        bool bad = gap > (double)kCarryGap;
         const double s0 = exp2_64(gap);
-        double Sx = mine.a * s0, Zx = mine.b * s0, Spx = mine.ap * s0, Zpx = mine.bp * s0;
+        double Sx = fin.a * s0, Zx = fin.b * s0, Spx = fin.ap * s0, Zpx = fin.bp * s0;
+        double pw = 1.0;
+        bool bad = false;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const double e = (j < Lv) ? exp2_64(((double)kc[j] - refd) * kLog2eD) : 0.0;
+            // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0
+            const double e = exp2_64(((double)kc[j] - refd) * kLog2eD);
             const double vv = (double)vc[j];
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            if (j < Lv) {
-                bad |= !(den >= (double)kTinyDen);
-                const double r = rcpd(den);
-                const double yv = num * r;
-                const double sg = (double)gc[j] * r;
-                dw_acc = fma(sg, fma(-yv, Zpx, Spx), dw_acc);
-                du_acc = fma(sg * (K.eu * e), vv - yv, du_acc);
-                kc[j] = (float)e;
-                yc[j] = (float)yv;
-                gc[j] = (float)sg;
-            } else {
-                kc[j] = 0.0f;
-                yc[j] = 0.0f;
-                gc[j] = 0.0f;
-            }
+            bad |= !(den >= (double)kTinyDen) & (j < Lv);
+            const double r = rcpd(fmax(den, 0x1p-120));
+            const double yv = num * r;
+            const double sg = (double)gc[j] * r;
+            // dw term s (A' - y B'), du term s e^{u+k} (v - y), both in the frame
+            dw_acc = fma(sg, fma(-yv, Zpx, Spx), dw_acc);
+            du_acc = fma(sg * (K.eu * e), vv - yv, du_acc);
+            const double ps = pw * sg;
+            R += ps;
+            Q = fma(ps, yv, Q);
+            kc[j] = (float)e;
+            sy[j][lane] = make_float2((float)sg, (float)yv);
+            pw *= K.dwf;
+            Spx = K.dwf * (Spx + Sx);
+            Zpx = K.dwf * (Zpx + Zx);
+            Sx = fma(Sx, K.dwf, ev);
+            Zx = fma(Zx, K.dwf, e);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fx = wave_any(bad);
+    }
+    if (!fx) return RevCarry{R, Q, -ref2};
+    du_acc = 0.0;
+    dw_acc = 0.0;
+    return exact_chunk<CH, false, true>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
+                                       ref, fin, rev_zero(), K.uc, (float)K.w, du_acc, dw_acc);
+}
+
+// Reverse summary of another unit's chunk, for the look-back's recomputation of a window
+// whose aggregate was not published in time: the summary arithmetic of chunk_pass, op
+// for op and in the same order (so the bits are those the owner publishes), but streaming
+// k, v, dy from memory in a loop that is not unrolled, so that the unit's own chunk stays
+// in registers across the look-back.
+template <int CH>
+__device__ __forceinline__ RevCarry helper_summary(
+    int64_t ci, int64_t T, int64_t C, int64_t nchunk, const double *__restrict__ cin,
+    int64_t ncin, int64_t bidx, int64_t row0, int cl, const float *__restrict__ k,
+    const float *__restrict__ v, const float *__restrict__ dy, const BwdConst &K) {
+    const int64_t t0 = ci * CH;
+    const int Lv = chunk_len(t0, T, CH);
+    if (Lv == 0) return rev_zero();
+    const float *kp = k + (row0 + t0) * C + cl;
+    const float *vp = v + (row0 + t0) * C + cl;
+    const float *gp = dy + (row0 + t0) * C + cl;
+    float ref = kNegBig;
+#pragma unroll 1
+    for (int j = 0; j < Lv; ++j) ref = fmaxf(ref, kp[(int64_t)j * C]);
+    const double refd = (double)ref;
+    const double ref2 = refd * kLog2eD;
+    const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
+    const double gap = fin.P - ref2;
+    bool fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
+    if (!fx) {
+        const double s0 = exp2_64(gap);
+        double Sx = fin.a * s0, Zx = fin.b * s0, Spx = fin.ap * s0, Zpx = fin.bp * s0;
+        double pw = 1.0, R = 0.0, Q = 0.0;
+        bool bad = false;
+#pragma unroll 1
+        for (int j = 0; j < CH; ++j) {
+            const bool in = j < Lv;
+            const float kj = in ? kp[(int64_t)j * C] : -__builtin_inff();
+            const double e = exp2_64(((double)kj - refd) * kLog2eD);
+            const double vv = in ? (double)vp[(int64_t)j * C] : 0.0;
+            const double ev = e * vv;
+            const double num = fma(K.eu, ev, Sx);
+            const double den = fma(K.eu, e, Zx);
+            bad |= !(den >= (double)kTinyDen) & in;
+            const double r = rcpd(fmax(den, 0x1p-120));
+            const double yv = num * r;
+            const double sg = (in ? (double)gp[(int64_t)j * C] : 0.0) * r;
+            const double ps = pw * sg;
+            R += ps;
+            Q = fma(ps, yv, Q);
+            pw *= K.dwf;
             Spx = K.dwf * (Spx + Sx);
             Zpx = K.dwf * (Zpx + Zx);
             Sx = fma(Sx, K.dwf, ev);
             Zx = fma(Zx, K.dwf, e);
         }
         fx = wave_any(bad);
+        if (!fx) return RevCarry{R, Q, -ref2};
     }
-
-    // R1: reverse summary of the chunk from a zero future
-    if (!fx) {
-        double R = 0.0, Q = 0.0;
-#pragma unroll
-        for (int j = CH - 1; j >= 0; --j) {
-            const double sg = (double)gc[j];
-            R = fma(R, K.dwf, sg);
-            Q = fma(Q, K.dwf, sg * (double)yc[j]);
-        }
-        return RevCarry{R, Q, -ref2};
-    }
-    load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-    load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
-    du_acc = 0.0;
-    dw_acc = 0.0;
-    const rsrc_t none = make_rsrc(dy);
-    return exact_chunk<CH, false, true>(kc, vc, gc, yc, Lv, ref, mine, rev_zero(), K.uc,
-                                        (float)K.w, none, none, voff, stride, false, du_acc,
-                                        dw_acc);
+    double du, dw;
+    return exact_chunk<CH, false, false>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
+                                         ref, fin, rev_zero(), K.uc, (float)K.w, du, dw);
 }
 
 // Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
 // first) from a zero future: `agg` is the window's reverse aggregate, `lfut` the part of it
 // that lies after this wave's chunk. Contains barriers (all waves call it together).
 template <int NW, int CH>
-__device__ __forceinline__ void window_rev_fold(BwdShared<NW> &sh, const RevCarry &rsum, int q,
+__device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const RevCarry &rsum, int q,
                                                 int lane, double w2, RevCarry &agg,
                                                 RevCarry &lfut) {
     __syncthreads();
@@ -343,16 +342,34 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW> &sh, const RevCarr
     }
 }
 
+// Count this unit's arrival in its channel group's counter and return the count. The
+// counter holds (epoch << kCountBits) | count; a value from another call (other epoch)
+// restarts the count. The caller's partials are stored (device scope) and complete before
+// it arrives, and the unit that sees the final count reads them only afterwards.
+__device__ __forceinline__ uint64_t arrive(uint64_t *ctr, uint64_t epoch) {
+    const uint64_t tag = epoch & ((uint64_t(1) << (64 - kCountBits)) - 1);
+    uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint64_t nv = ((old >> kCountBits) == tag) ? old + 1 : ((tag << kCountBits) | 1u);
+        if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            consume_fence();
+            return nv & ((uint64_t(1) << kCountBits) - 1);
+        }
+    }
+}
+
 template <int NW, int CH>
-__global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
-    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
-    const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ dy, const Rec *__restrict__ fincl,
-    float *__restrict__ dk, float *__restrict__ dv, uint64_t *__restrict__ flags,
-    RevRec *__restrict__ ragg, RevRec *__restrict__ rincl, double *__restrict__ part) {
+__global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
+    int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk,
+    uint64_t epoch, const float *__restrict__ w, const float *__restrict__ u,
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
+    const double *__restrict__ cin, int64_t ncin, float *__restrict__ dk,
+    float *__restrict__ dv, float *__restrict__ dw, float *__restrict__ du,
+    uint64_t *__restrict__ flags, RevRec *__restrict__ ragg, RevRec *__restrict__ rincl,
+    uint64_t *__restrict__ part, uint64_t *__restrict__ ctr) {
     constexpr int WIN = NW * CH;
-    static_assert(WIN == kFwdWindow, "backward windows must match the forward's carries");
-    __shared__ BwdShared<NW> sh;
+    __shared__ BwdShared<NW, CH> sh;
 
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,17 +393,17 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
     K.w2 = K.w * kLog2eD;
     K.slow_wave = wave_any(!(fabsf(K.uc) <= 60.0f));
     const int64_t row0 = bidx * T;
-    const int64_t t0 = s * WIN + (int64_t)q * CH;
+    const int64_t ci = s * NW + q;
+    const int64_t t0 = ci * CH;
 
-    float kc[CH], vc[CH], gc[CH], yc[CH];
+    float kc[CH], vc[CH], gc[CH];
     bool fx;
-    Carry mine;
     float ref;
     int Lv;
     double du_acc, dw_acc;
-    RevCarry rsum = chunk_pass<NW, CH>(sh, s, q, lane, T, C, nseg, bidx, row0, cl, voff, stride,
-                                       k, v, dy, fincl, K, kc, vc, gc, yc, fx, mine, ref, Lv,
-                                       du_acc, dw_acc);
+    RevCarry rsum = chunk_pass<CH>(ci, T, C, nchunk, cin, ncin, bidx, row0, cl, voff, stride,
+                                         k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref, Lv,
+                                         du_acc, dw_acc);
     RevCarry agg, lfut;
     window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2, agg, lfut);
     const int64_t rec = (bidx * nseg + s) * C + cl;
@@ -405,7 +422,6 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
     if (s < nseg - 1) {
         int64_t j = s + 1;
         int it = 0;
-        bool redo_own = false;
         for (;;) {
             if (q == 0) {
                 const int st = poll_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kPollTries);
@@ -418,22 +434,14 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: recompute window j's reverse aggregate here and
                 // publish it (bitwise what unit j itself publishes)
-                bool fx_j;
-                Carry m_j;
-                float r_j;
-                int L_j;
-                double du_j, dw_j;
-                const RevCarry rs_j = chunk_pass<NW, CH>(
-                    sh, j, q, lane, T, C, nseg, bidx, row0, cl, voff, stride, k, v, dy, fincl,
-                    K, kc, vc, gc, yc, fx_j, m_j, r_j, L_j, du_j, dw_j);
+                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, nchunk, cin, ncin,
+                                                         bidx, row0, cl, k, v, dy, K);
                 RevCarry agg_j, lf_j;
                 window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
                 if (q == 0) {
                     if (cval) put_rrec(ragg + (bidx * nseg + j) * C + cl, agg_j);
                     raise_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kAggregate);
                 }
-                __syncthreads();
-                redo_own = true;
             }
             if (j == nseg - 1) {
                 j = nseg;
@@ -444,11 +452,6 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
         if (j < nseg) fut = get_rrec(rincl + (bidx * nseg + j) * C + cl);
         for (int64_t m = j - 1; m > s; --m)
             fut = rfollow(fut, get_rrec(ragg + (bidx * nseg + m) * C + cl), (double)WIN * K.w2);
-        if (redo_own) {
-            __syncthreads();
-            chunk_pass<NW, CH>(sh, s, q, lane, T, C, nseg, bidx, row0, cl, voff, stride, k, v,
-                               dy, fincl, K, kc, vc, gc, yc, fx, mine, ref, Lv, du_acc, dw_acc);
-        }
     }
     if (q == 0) {
         if (cval) put_rrec(rincl + rec, rfollow(fut, agg, (double)WIN * K.w2));
@@ -462,14 +465,17 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
     rnormalize(rc);
     const double rgap = (double)ref * kLog2eD + rc.r;
     const bool rx = fx || wave_any(rgap > (double)kCarryGap);
-    if (!rx) {
+    if (Lv == 0) {
+        // past the sequence end: nothing to store
+    } else if (!rx) {
         const double fr = exp2_64(rgap);
         const double dwf = K.dwf;
         double R = rc.g * fr, Q = rc.h * fr;
 #pragma unroll
         for (int j = CH - 1; j >= 0; --j) {
-            const double e = (double)kc[j], vv = (double)vc[j], sg = (double)gc[j];
-            const double yy = (double)yc[j];
+            const float2 p = sh.sy[q][j][lane];
+            const double e = (double)kc[j], vv = (double)vc[j], sg = (double)p.x;
+            const double yy = (double)p.y;
             const double cs = K.eu * sg;
             if (j < Lv && cval) {
                 bstore(rdv, (float)(e * (cs + R)), voff, j * stride);
@@ -479,17 +485,17 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
             Q = fma(Q, dwf, sg * yy);
         }
     } else {
-        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
+        const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
         double d0 = 0.0, d1 = 0.0;
-        exact_chunk<CH, true, false>(kc, vc, gc, yc, Lv, ref, mine, rc, K.uc, wc, rdk, rdv,
-                                     voff, stride, cval, d0, d1);
+        exact_chunk<CH, true, false>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
+                                     K.uc, wc, d0, d1);
     }
 
-    // ---- dw, du partials of this window, summed over its chunks in a fixed order ----
+    // ---- dw, du: this window's partial (its chunks summed in a fixed order), then the
+    // last unit of the channel group to arrive sums all partials in a fixed order ----
     __syncthreads();
     sh.a[q][lane] = du_acc;
-    sh.b[q][lane] = -dw_acc;
+    sh.b[q][lane] = dw_acc;
     __syncthreads();
     if (q == 0) {
         double su = 0.0, sw = 0.0;
@@ -498,26 +504,32 @@ __global__ __launch_bounds__(NW * 64) void wkv_backward_kernel(
             sw += sh.b[qq][lane];
         }
         if (cval) {
-            part[rec * 2] = sw;
-            part[rec * 2 + 1] = su;
+            put_u64(part + rec * 2, -sw);
+            put_u64(part + rec * 2 + 1, su);
         }
+        publish_fence();
+        if (lane == 0) sh.status[0] = (arrive(ctr + grp, epoch) == (uint64_t)(B * nseg)) ? 1 : 0;
     }
-}
-
-// dw[c], du[c] = sums of the per-window partials over b and windows, in a fixed order.
-__global__ __launch_bounds__(256) void wkv_reduce_kernel(int64_t n_bs, int64_t C,
-                                                         const double *__restrict__ part,
-                                                         float *__restrict__ dw,
-                                                         float *__restrict__ du) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= C) return;
+    __syncthreads();
+    if (sh.status[0] == 0) return;
+    consume_fence();
     double sw = 0.0, su = 0.0;
-    for (int64_t i = 0; i < n_bs; ++i) {
-        sw += part[(i * C + c) * 2];
-        su += part[(i * C + c) * 2 + 1];
+    for (int64_t i = q; i < B * nseg; i += NW) {
+        sw += get_u64(part + (i * C + cl) * 2);
+        su += get_u64(part + (i * C + cl) * 2 + 1);
     }
-    dw[c] = (float)sw;
-    du[c] = (float)su;
+    sh.a[q][lane] = sw;
+    sh.b[q][lane] = su;
+    __syncthreads();
+    if (q == 0 && cval) {
+        double tw = 0.0, tu = 0.0;
+        for (int qq = 0; qq < NW; ++qq) {
+            tw += sh.a[qq][lane];
+            tu += sh.b[qq][lane];
+        }
+        dw[c] = (float)tw;
+        du[c] = (float)tu;
+    }
 }
 
 __global__ __launch_bounds__(256) void wkv_zero2_kernel(float *__restrict__ a,
@@ -530,19 +542,16 @@ __global__ __launch_bounds__(256) void wkv_zero2_kernel(float *__restrict__ a,
 }
 
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const Rec *fincl,
+                           const float *k, const float *v, const float *dy, const FwdLayout &F,
                            float *dk, float *dv, float *dw, float *du, const BwdLayout &L,
                            uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
-    hipLaunchKernelGGL((wkv_backward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
-                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
-                       k, v, dy, fincl, dk, dv, L.flags, L.ragg, L.rincl, L.part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0,
-                       stream, B * L.nseg, C, L.part, dw, du);
+    hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kFwdChunk>), dim3((unsigned)units),
+                       dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, F.nchunk,
+                       epoch, w, u, k, v, dy, F.cin, B * F.nchunk * C, dk, dv, dw, du, L.flags,
+                       L.ragg, L.rincl, L.part, L.ctr);
     return hipGetLastError();
 }
 

@@ -8,7 +8,10 @@
 
 namespace wkvdev {
 
-// Load a CH-token chunk of one lane's channel starting at token t0 (rows past T are 0).
+// Load a CH-token chunk of one lane's channel starting at token t0. Tokens past T are
+// padding: k = -inf (weight e^{k - ref} = 0 in every frame), v = 0. The loads carry no
+// branches (a padded token re-reads the last valid row), so the unrolled chunk stays in
+// straight-line code.
 template <int CH>
 __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
                                            const float *__restrict__ k,
@@ -17,7 +20,7 @@ __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
     if (t0 >= T) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            kc[j] = 0.0f;
+            kc[j] = -__builtin_inff();
             vc[j] = 0.0f;
         }
         return;
@@ -25,15 +28,20 @@ __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
     const rsrc_t rk = make_rsrc(k + (row0 + t0) * C);
     const rsrc_t rv = make_rsrc(v + (row0 + t0) * C);
     const int stride = (int)(C * 4);
-    const int Lv = (int)(T - t0 < CH ? T - t0 : CH);
+    const int last = (int)(T - t0 < CH ? T - t0 : CH) - 1;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        if (j < Lv) {
-            kc[j] = bload(rk, voff, j * stride);
-            vc[j] = bload(rv, voff, j * stride);
-        } else {
-            kc[j] = 0.0f;
-            vc[j] = 0.0f;
+        const int soff = (j < last ? j : last) * stride;
+        kc[j] = bload(rk, voff, soff);
+        vc[j] = bload(rv, voff, soff);
+    }
+    if (last < CH - 1) {
+#pragma unroll
+        for (int j = 1; j < CH; ++j) {
+            if (j > last) {
+                kc[j] = -__builtin_inff();
+                vc[j] = 0.0f;
+            }
         }
     }
 }
@@ -42,20 +50,25 @@ __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
 // ref = max_j k_j and e_j = 2^{(k_j - ref) log2 e} <= 1 (fp64), the sums A, B, A', B'
 // after the CH tokens, at scale 2^{ref log2 e}. Horner from the first token:
 //   A'_{j+1} = e^{-w} (A'_j + A_j),   A_{j+1} = e^{-w} A_j + e_j v_j   (B, B' alike).
-// Unless KEEPK, kc receives e_j rounded to fp32 (for outputs that need only fp32). Returns
-// true (wave-uniform) if the exact form is needed instead (forced, or the fixed frame
-// underflows for some lane); the caller then uses exact_summary on the raw chunk.
+// Padded tokens (k = -inf) have e_j = 0. Unless KEEPK, kc receives e_j rounded to fp32
+// (for outputs that need only fp32). Returns true (wave-uniform) if the exact form is
+// needed instead (forced, or the fp64 sums would underflow for some lane, which takes keys
+// some 600 apart within one chunk); the caller then uses exact_summary.
 template <int CH, bool KEEPK>
 __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)[CH], int Lv,
                                               float ref, bool force_exact, double dwf,
                                               Carry &sum) {
     const double refd = (double)ref;
     sum = Carry{0.0, 0.0, 0.0, 0.0, refd * kLog2eD};
+    if (Lv == 0) {
+        sum.P = kNegBigD;
+        return false;
+    }
     if (force_exact) return true;
     double S = 0.0, Z = 0.0, Sp = 0.0, Zp = 0.0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const double e = (j < Lv) ? exp2_64(((double)kc[j] - refd) * kLog2eD) : 0.0;
+        const double e = exp2_64(((double)kc[j] - refd) * kLog2eD);
         if (!KEEPK) kc[j] = (float)e;
         Sp = dwf * (Sp + S);
         Zp = dwf * (Zp + Z);
@@ -66,10 +79,10 @@ __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)
     sum.b = Z;
     sum.ap = Sp;
     sum.bp = Zp;
-    return wave_any(Lv > 0 && !(Z >= (double)kTinyDen));
+    return wave_any(!(Z >= kTinySum));
 }
 
-// Load one tensor's CH-token chunk (rows past T are 0).
+// Load one tensor's CH-token chunk (tokens past T are 0), branch-free as load_chunk.
 template <int CH>
 __device__ __forceinline__ void load_chunk1(float (&gc)[CH], const float *__restrict__ g,
                                             int64_t row0, int64_t t0, int64_t T, int64_t C,
@@ -81,9 +94,14 @@ __device__ __forceinline__ void load_chunk1(float (&gc)[CH], const float *__rest
     }
     const rsrc_t rg = make_rsrc(g + (row0 + t0) * C);
     const int stride = (int)(C * 4);
-    const int Lv = (int)(T - t0 < CH ? T - t0 : CH);
+    const int last = (int)(T - t0 < CH ? T - t0 : CH) - 1;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) gc[j] = (j < Lv) ? bload(rg, voff, j * stride) : 0.0f;
+    for (int j = 0; j < CH; ++j) gc[j] = bload(rg, voff, (j < last ? j : last) * stride);
+    if (last < CH - 1) {
+#pragma unroll
+        for (int j = 1; j < CH; ++j)
+            if (j > last) gc[j] = 0.0f;
+    }
 }
 
 // Valid tokens of the chunk starting at t0.
@@ -120,33 +138,48 @@ __device__ __forceinline__ void rs64_skip(Rs64 &s, double w) {
     s.p -= w;
 }
 
-// Chunk summary in the per-token form (fp64), same meaning as chunk_summary's.
+// Chunk summary in the per-token form (fp64), same meaning as chunk_summary's, for the
+// rare chunks the fixed frame cannot take. Reads k, v straight from memory in a loop that
+// is not unrolled: few registers wherever it is inlined.
 template <int CH>
-__device__ __forceinline__ void exact_summary(const float (&kc)[CH], const float (&vc)[CH],
-                                              int Lv, float ref, double w, Carry &sum) {
+__device__ __forceinline__ Carry exact_summary(const float *__restrict__ k,
+                                            const float *__restrict__ v, int64_t row0,
+                                            int64_t t0, int Lv, int64_t C, int cl, float ref,
+                                            double w) {
     const double refd = (double)ref;
     Rs64 s{0.0, 0.0, 0.0, 0.0, kNegBigD};
-#pragma unroll
+#pragma unroll 1
     for (int j = 0; j < CH; ++j) {
-        if (j < Lv)
-            rs64_push(s, (double)kc[j] - refd, (double)vc[j], w);
-        else
+        if (j < Lv) {
+            const int64_t i = (row0 + t0 + j) * C + cl;
+            rs64_push(s, (double)k[i] - refd, (double)v[i], w);
+        } else {
             rs64_skip(s, w);
+        }
     }
     // A = a e^{p + ref}; the carry scale is base 2: 2^{P} = e^{p + ref}
-    sum = Carry{s.a, s.b, s.ap, s.bp, (s.p + refd) * kLog2eD};
+    return Carry{s.a, s.b, s.ap, s.bp, (s.p + refd) * kLog2eD};
 }
 
+// Frame of a chunk: its largest key (padding is -inf; a chunk of padding only gets kNegBig).
 template <int CH>
 __device__ __forceinline__ float chunk_ref(const float (&kc)[CH], int Lv) {
     float ref = kNegBig;
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
-        if (j < Lv) ref = fmaxf(ref, kc[j]);
+    for (int j = 0; j < CH; ++j) ref = fmaxf(ref, kc[j]);
     return ref;
 }
 
 // ---- publication records (device-scope, see wkv_launch.h for the layout) ----
+// Everything one workgroup publishes for another (records, flags, partials) is written
+// and read only with device-scope atomic loads and stores (sc1: coherent across the XCDs'
+// separate L2 caches without flushing them). Ordering is explicit: a producer waits for
+// its record stores to complete before it stores the flag (publish_fence), and a consumer
+// issues its record loads only after the flag value it polled has returned. A C++
+// release/acquire would instead write back or invalidate the whole L2 of the XCD
+// (buffer_wbl2 / buffer_inv), which costs microseconds per publication here.
+__device__ __forceinline__ void publish_fence() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void consume_fence() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void put_u64(uint64_t *p, double x) {
     __hip_atomic_store(p, __builtin_bit_cast(uint64_t, x), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -167,12 +200,14 @@ __device__ __forceinline__ Carry get_rec(const Rec *r) {
                  get_u64(&r->P)};
 }
 __device__ __forceinline__ void put_flag(uint64_t *f, uint64_t epoch, uint64_t status) {
-    __hip_atomic_store(f, (epoch << 2) | status, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    publish_fence();
+    __hip_atomic_store(f, (epoch << 2) | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Publish `status` unless a higher status of this call is already there (a helper that
 // recomputed an aggregate must not hide the owner's inclusive carry).
 __device__ __forceinline__ void raise_flag(uint64_t *f, uint64_t epoch, uint64_t status) {
-    __hip_atomic_fetch_max(f, (epoch << 2) | status, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    publish_fence();
+    __hip_atomic_fetch_max(f, (epoch << 2) | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Status of a unit's publication for this call: 1 aggregate, 2 inclusive carry, or 0 if
@@ -180,11 +215,26 @@ __device__ __forceinline__ void raise_flag(uint64_t *f, uint64_t epoch, uint64_t
 // waits without bound).
 __device__ __forceinline__ int poll_flag(const uint64_t *f, uint64_t epoch, int tries) {
     for (int i = 0;; ++i) {
-        const uint64_t x = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        if ((x >> 2) == epoch && (x & 3u) != 0u) return (int)(x & 3u);
+        const uint64_t x = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((x >> 2) == epoch && (x & 3u) != 0u) {
+            consume_fence();
+            return (int)(x & 3u);
+        }
         if (i >= tries) return 0;
         __builtin_amdgcn_s_sleep(4);
     }
+}
+
+// Chunk carries, one fp64 array per field (stride n between fields).
+__device__ __forceinline__ void put_cin(double *f, int64_t n, int64_t i, const Carry &c) {
+    f[i] = c.a;
+    f[n + i] = c.b;
+    f[2 * n + i] = c.ap;
+    f[3 * n + i] = c.bp;
+    f[4 * n + i] = c.P;
+}
+__device__ __forceinline__ Carry get_cin(const double *f, int64_t n, int64_t i) {
+    return Carry{f[i], f[n + i], f[2 * n + i], f[3 * n + i], f[4 * n + i]};
 }
 
 // c <- fold of a carry and a summary (the summary follows c in time, `len` tokens,

@@ -34,6 +34,7 @@ constexpr float kNegBig = -1e30f;   // "no mass yet" log-scale: finite, so no in
 constexpr double kNegBigD = -1e30;
 constexpr float kTinyDen = 0x1p-100f;  // smallest in-frame denominator the fast path accepts
 constexpr float kCarryGap = 64.0f;     // largest log2 gap (carry above chunk frame) accepted
+constexpr double kTinySum = 0x1p-900;  // smallest fp64 chunk summary the fast path accepts
 constexpr float kRenorm = 0x1p-40f;    // Rs renormalization threshold on b
 constexpr float kRenormUp = 0x1p40f;
 constexpr float kRenormLn = 27.725887222397812f;  // 40 ln 2

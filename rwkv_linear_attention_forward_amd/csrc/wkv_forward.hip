@@ -41,6 +41,26 @@
 
 namespace wkvdev {
 
+// Outputs of one lane's chunk by the per-token rescaled recursion (Rs, fp32), from the
+// carry entering the chunk; for chunks whose fixed frame would under- or overflow. Reads
+// k, v straight from memory in a loop that is not unrolled: few registers.
+template <int CH>
+__device__ __forceinline__ void exact_outputs(const float *__restrict__ k,
+                                           const float *__restrict__ v, float *__restrict__ y,
+                                           int64_t row0, int64_t t0, int Lv, int64_t C, int cl,
+                                           float ref, const Carry &mine, float uc,
+                                           const Decay &dc) {
+    const double ref2 = (double)ref * kLog2eD;
+    Rs st{(float)mine.a, (float)mine.b, (float)((mine.P - ref2) * kLn2D)};
+#pragma unroll 1
+    for (int j = 0; j < Lv; ++j) {
+        const int64_t i = (row0 + t0 + j) * C + cl;
+        const float kr = k[i] - ref, vv = v[i];
+        y[i] = rs_out(st, kr, vv, uc);
+        rs_push(st, kr, vv, dc);
+    }
+}
+
 // Window staging of chunk summaries (one per wave) for the in-window fold.
 template <int NW>
 struct FwdShared {
@@ -62,12 +82,67 @@ __device__ __forceinline__ Carry staged(const FwdShared<NW> &sh, int q, int lane
     return Carry{sh.a[q][lane], sh.b[q][lane], sh.ap[q][lane], sh.bp[q][lane], sh.P[q][lane]};
 }
 
+// Aggregate of window j (its NW chunk summaries folded from the empty state), for the
+// look-back's recomputation of a window whose aggregate was not published in time. Called
+// by all waves together (it contains barriers). Each wave streams its chunk from memory in
+// a loop that is not unrolled, repeating chunk_summary's arithmetic op for op and in the
+// same order (bitwise what unit j computes itself), so the unit's own chunk stays in
+// registers.
+template <int NW, int CH>
+__device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, int q, int lane,
+                                                  int64_t T, int64_t C, int64_t row0, int cl,
+                                                  const float *__restrict__ k,
+                                                  const float *__restrict__ v, bool slow_wave,
+                                                  double dwfd, double wd, double cw2) {
+    const int64_t tj = j * (NW * CH) + (int64_t)q * CH;
+    const int Lj = chunk_len(tj, T, CH);
+    Carry sj = carry_empty();
+    if (Lj > 0) {
+        const float *kp = k + (row0 + tj) * C + cl;
+        const float *vp = v + (row0 + tj) * C + cl;
+        float rj = kNegBig;
+#pragma unroll 1
+        for (int i = 0; i < Lj; ++i) rj = fmaxf(rj, kp[(int64_t)i * C]);
+        const double refd = (double)rj;
+        sj.P = refd * kLog2eD;
+        if (slow_wave) {
+            sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
+        } else {
+            double S = 0.0, Z = 0.0, Sp = 0.0, Zp = 0.0;
+#pragma unroll 1
+            for (int i = 0; i < CH; ++i) {
+                const bool in = i < Lj;
+                const float ki = in ? kp[(int64_t)i * C] : -__builtin_inff();
+                const double e = exp2_64(((double)ki - refd) * kLog2eD);
+                const double vi = in ? (double)vp[(int64_t)i * C] : 0.0;
+                Sp = dwfd * (Sp + S);
+                Zp = dwfd * (Zp + Z);
+                S = fma(S, dwfd, e * vi);
+                Z = fma(Z, dwfd, e);
+            }
+            sj.a = S;
+            sj.b = Z;
+            sj.ap = Sp;
+            sj.bp = Zp;
+            if (wave_any(!(Z >= kTinySum))) sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
+        }
+    }
+    __syncthreads();
+    stage(sh, q, lane, sj);
+    __syncthreads();
+    Carry X = carry_empty();
+#pragma unroll
+    for (int qq = 0; qq < NW; ++qq) fold(X, staged(sh, qq, lane), cw2, (double)CH);
+    __syncthreads();
+    return X;
+}
+
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
-    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
+    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk, uint64_t epoch,
     const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
     const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
-    Rec *__restrict__ agg, Rec *__restrict__ incl) {
+    Rec *__restrict__ agg, Rec *__restrict__ incl, double *__restrict__ cin, int64_t ncin) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
 
@@ -102,10 +177,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const float ref = chunk_ref<CH>(kc, Lv);
     Carry sum;
     bool exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, sum);
-    if (exact) {
-        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        exact_summary<CH>(kc, vc, Lv, ref, wd, sum);
-    }
+    if (exact) sum = exact_summary<CH>(k, v, row0, t0, Lv, C, cl, ref, wd);
 
     // ---- window: local carries and aggregate ----
     stage(sh, q, lane, sum);
@@ -130,7 +202,6 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // those aggregates forward in order. The result is bitwise the sequential chain
     // incl[s] = fold(incl[s-1], agg[s]) whatever the timing, so every run is deterministic.
     Carry prefix = carry_empty();
-    bool own_clobbered = false;
     if (s > 0) {
         int64_t j = s - 1;
         int it = 0;
@@ -146,27 +217,12 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: compute window j's aggregate here and publish it
                 // (bitwise what unit j itself publishes)
-                const int64_t tj = j * WIN + (int64_t)q * CH;
-                const int Lj = chunk_len(tj, T, CH);
-                load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
-                own_clobbered = true;
-                const float rj = chunk_ref<CH>(kc, Lj);
-                Carry sj;
-                if (chunk_summary<CH, false>(kc, vc, Lj, rj, slow_wave, dwfd, sj)) {
-                    load_chunk<CH>(kc, vc, k, v, row0, tj, T, C, voff);
-                    exact_summary<CH>(kc, vc, Lj, rj, wd, sj);
-                }
-                __syncthreads();
-                stage(sh, q, lane, sj);
-                __syncthreads();
-                Carry X = carry_empty();
-#pragma unroll
-                for (int qq = 0; qq < NW; ++qq) fold(X, staged(sh, qq, lane), cw2, (double)CH);
+                const Carry X = window_aggregate<NW, CH>(sh, j, q, lane, T, C, row0, cl, k, v,
+                                                         slow_wave, dwfd, wd, cw2);
                 if (q == 0) {
                     if (cval) put_rec(agg + (bidx * nseg + j) * C + cl, X);
                     raise_flag(flags + j * nbg + bg, epoch, kAggregate);
                 }
-                __syncthreads();
             }
             if (j == 0) {
                 j = -1;
@@ -183,19 +239,13 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         if (cval) put_rec(incl + rec, follow(prefix, run, ww2, (double)WIN));
         put_flag(myflag, epoch, kInclusive);
     }
-    if (y == nullptr) return;
-
-    // ---- phase 3: outputs ----
+    // ---- the carry entering this wave's chunk, kept for the backward pass ----
     Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
-    if (own_clobbered) {
-        load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        if (!exact) {
-            Carry s2;
-            exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, s2);
-            if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-        }
-    }
+    if (Lv > 0 && cval) put_cin(cin, ncin, (bidx * nchunk + s * NW + q) * C + cl, mine);
+    if (y == nullptr || Lv == 0) return;
+
+    // ---- phase 3: outputs ----
     const double ref2 = (double)ref * kLog2eD;
     if (!exact) {
         const double gap = mine.P - ref2;
@@ -207,27 +257,18 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             const float e = kc[j], ev = e * vc[j];
             const float num = fmaf(eu, ev, Sx);
             const float den = fmaf(eu, e, Zx);
-            if (j < Lv) bad |= !(den >= kTinyDen);
+            bad |= !(den >= kTinyDen) & (j < Lv);
             kc[j] = num * rcpf(den);
             Sx = fmaf(Sx, dc.dwf, ev);
             Zx = fmaf(Zx, dc.dwf, e);
         }
         exact = wave_any(bad);
-        if (exact) load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     }
     if (exact) {
-        Rs st{(float)mine.a, (float)mine.b, (float)((mine.P - ref2) * kLn2D)};
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            if (j < Lv) {
-                const float kr = kc[j] - ref;
-                const float yj = rs_out(st, kr, vc[j], uc);
-                rs_push(st, kr, vc[j], dc);
-                kc[j] = yj;
-            }
-        }
+        if (cval) exact_outputs<CH>(k, v, y, row0, t0, Lv, C, cl, ref, mine, uc, dc);
+        return;
     }
-    if (Lv > 0 && cval) {
+    if (cval) {
         const rsrc_t ry = make_rsrc(y + (row0 + t0) * C);
         const int stride = (int)(C * 4);
 #pragma unroll
@@ -243,8 +284,8 @@ hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
-                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
-                       k, v, y, L.flags, L.agg, L.incl);
+                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, L.nchunk, epoch,
+                       w, u, k, v, y, L.flags, L.agg, L.incl, L.cin, B * L.nchunk * C);
     return hipGetLastError();
 }
 

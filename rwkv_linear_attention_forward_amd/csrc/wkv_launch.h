@@ -7,7 +7,7 @@
 namespace wkvdev {
 
 // Forward geometry: a unit is 64 channels x one window of kFwdWaves * kFwdChunk tokens.
-constexpr int kFwdWaves = 8;
+constexpr int kFwdWaves = 4;
 constexpr int kFwdChunk = 32;
 constexpr int kFwdWindow = kFwdWaves * kFwdChunk;
 
@@ -27,11 +27,17 @@ struct Rec {
 //   flags[nseg][B * ngrp]   uint64 publication flags
 //   agg[B][nseg][C]         window aggregates (from the empty state)
 //   incl[B][nseg][C]        inclusive carries: the state after window s, i.e. entering s+1
+//   cin[5][B][nchunk][C]    the carry entering every kFwdChunk-token chunk, normalized,
+//                           one fp64 array per field (a, b, a', b', P) so that a wave's
+//                           64 channels read and write 512 contiguous bytes per field;
+//                           the backward pass starts each of its chunks from these.
 struct FwdLayout {
     int64_t nseg;
+    int64_t nchunk;
     uint64_t *flags;
     Rec *agg;
     Rec *incl;
+    double *cin;
 };
 
 // A reverse carry or reverse window summary as published: the future sums
@@ -42,26 +48,37 @@ struct RevRec {
     uint64_t r;
 };
 
+// Backward geometry: a unit is 64 channels x kBwdWaves chunks of kFwdChunk tokens (the
+// chunks must coincide with the forward's, whose entering carries they start from).
+constexpr int kBwdWaves = 4;
+constexpr int kBwdWindow = kBwdWaves * kFwdChunk;
+
 // Backward workspace:
 //   flags[nseg][B * ngrp]    uint64 publication flags (reverse direction)
 //   ragg[B][nseg][C]         reverse window aggregates (from a zero future)
 //   rincl[B][nseg][C]        reverse inclusive carries: the future sums entering window s
-//   part[B][nseg][C][2]      per-window dw, du partials (fp64), summed by a second kernel
+//   part[B][nseg][C][2]      per-window dw, du partials (fp64)
+//   ctr[ngrp]                per channel group: arrivals of this call's units, tagged with
+//                            the call epoch; the last unit to arrive sums the partials
 struct BwdLayout {
     int64_t nseg;
     uint64_t *flags;
     RevRec *ragg;
     RevRec *rincl;
-    double *part;
+    uint64_t *part;  // fp64 bits
+    uint64_t *ctr;
 };
+
+// Units per channel group (B * nseg) must fit the arrival counter's 24-bit count.
+constexpr int kCountBits = 24;
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                           const float *k, const float *v, float *y, const FwdLayout &L,
                           uint64_t epoch, hipStream_t stream);
 
-// `fincl` is the forward workspace's inclusive-carry array for the same inputs.
+// `F` is the forward workspace filled for the same inputs (its chunk carries are read).
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const Rec *fincl,
+                           const float *k, const float *v, const float *dy, const FwdLayout &F,
                            float *dk, float *dv, float *dw, float *du, const BwdLayout &L,
                            uint64_t epoch, hipStream_t stream);
 
