@@ -191,8 +191,8 @@ struct BwdConst {
 // reverse summary from a zero future (R1):
 //   R = sum_j e^{-j w} sigma_j,  Q = sum_j e^{-j w} sigma_j y_j   (future sums at the
 // chunk start, in the chunk frame).
-// Also the chunk's dw, du terms; e_j, v_j are left in kc, vc and (sigma_j, y_j) in `sy`
-// (fp32) for the reverse sweep, unless fx (the fixed frame failed for some lane of the
+// Also the chunk's dw, du terms; e_j, v_j are left in kc, vc and (sigma_j, sigma_j y_j) in
+// `sy` (fp32) for the reverse sweep, unless fx (the fixed frame failed for some lane of the
 // wave; the chunk then takes the per-token path). helper_summary repeats the summary
 // arithmetic op for op, so a helper publishes the bits the owner would (every fused
 // multiply-add is written out; the build does not contract).
@@ -223,9 +223,16 @@ __device__ __forceinline__ RevCarry chunk_pass(
     double R = 0.0, Q = 0.0;
     if (!fx) {
         const double s0 = exp2_64(gap);
-        double Sx = fin.a * s0, Zx = fin.b * s0, Spx = fin.ap * s0, Zpx = fin.bp * s0;
+        double Sx = fin.a * s0, Zx = fin.b * s0;
+        // A'_j = d P_j with P_{j+1} = d P_j + A_j (d = e^{-w}; A'_{j+1} = d (A'_j + A_j));
+        // the dw terms are summed without the common factor d, applied at the end
+        double Ps = 0.0, Pz = 0.0;
+        if (K.dwf > 0.0) {
+            Ps = fin.ap * s0 / K.dwf;
+            Pz = fin.bp * s0 / K.dwf;
+        }
         double pw = 1.0;
-        bool bad = false;
+        double dmin = __builtin_inf();
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0
@@ -234,26 +241,26 @@ __device__ __forceinline__ RevCarry chunk_pass(
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            bad |= !(den >= (double)kTinyDen) & (j < Lv);
+            dmin = (j < Lv) ? fmin(dmin, den) : dmin;
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
             const double sg = (double)gc[j] * r;
-            // dw term s (A' - y B'), du term s e^{u+k} (v - y), both in the frame
-            dw_acc = fma(sg, fma(-yv, Zpx, Spx), dw_acc);
+            const double sgy = sg * yv;
+            // dw term s (A' - y B') / d, du term s e^{u+k} (v - y), both in the frame
+            dw_acc = fma(sg, fma(-yv, Pz, Ps), dw_acc);
             du_acc = fma(sg * (K.eu * e), vv - yv, du_acc);
-            const double ps = pw * sg;
-            R += ps;
-            Q = fma(ps, yv, Q);
+            R = fma(pw, sg, R);
+            Q = fma(pw, sgy, Q);
             kc[j] = (float)e;
-            sy[j][lane] = make_float2((float)sg, (float)yv);
+            sy[j][lane] = make_float2((float)sg, (float)sgy);
             pw *= K.dwf;
-            Spx = K.dwf * (Spx + Sx);
-            Zpx = K.dwf * (Zpx + Zx);
+            Ps = fma(Ps, K.dwf, Sx);
+            Pz = fma(Pz, K.dwf, Zx);
             Sx = fma(Sx, K.dwf, ev);
             Zx = fma(Zx, K.dwf, e);
-            __builtin_amdgcn_sched_barrier(0);
         }
-        fx = wave_any(bad);
+        dw_acc *= K.dwf;
+        fx = wave_any(!(dmin >= (double)kTinyDen));
     }
     if (!fx) return RevCarry{R, Q, -ref2};
     du_acc = 0.0;
@@ -288,9 +295,9 @@ __device__ __forceinline__ RevCarry helper_summary(
     bool fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
     if (!fx) {
         const double s0 = exp2_64(gap);
-        double Sx = fin.a * s0, Zx = fin.b * s0, Spx = fin.ap * s0, Zpx = fin.bp * s0;
+        double Sx = fin.a * s0, Zx = fin.b * s0;
         double pw = 1.0, R = 0.0, Q = 0.0;
-        bool bad = false;
+        double dmin = __builtin_inf();
 #pragma unroll 1
         for (int j = 0; j < CH; ++j) {
             const bool in = j < Lv;
@@ -300,20 +307,18 @@ __device__ __forceinline__ RevCarry helper_summary(
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            bad |= !(den >= (double)kTinyDen) & in;
+            dmin = in ? fmin(dmin, den) : dmin;
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
             const double sg = (in ? (double)gp[(int64_t)j * C] : 0.0) * r;
-            const double ps = pw * sg;
-            R += ps;
-            Q = fma(ps, yv, Q);
+            const double sgy = sg * yv;
+            R = fma(pw, sg, R);
+            Q = fma(pw, sgy, Q);
             pw *= K.dwf;
-            Spx = K.dwf * (Spx + Sx);
-            Zpx = K.dwf * (Zpx + Zx);
             Sx = fma(Sx, K.dwf, ev);
             Zx = fma(Zx, K.dwf, e);
         }
-        fx = wave_any(bad);
+        fx = wave_any(!(dmin >= (double)kTinyDen));
         if (!fx) return RevCarry{R, Q, -ref2};
     }
     double du, dw;
@@ -473,16 +478,18 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
         double R = rc.g * fr, Q = rc.h * fr;
 #pragma unroll
         for (int j = CH - 1; j >= 0; --j) {
+            // dv = e (e^u s + R),  dk = e (e^u s (v - y) + v R - Q) = v dv - e (e^u s y + Q)
             const float2 p = sh.sy[q][j][lane];
-            const double e = (double)kc[j], vv = (double)vc[j], sg = (double)p.x;
-            const double yy = (double)p.y;
-            const double cs = K.eu * sg;
+            const double e = (double)kc[j], vv = (double)vc[j];
+            const double sg = (double)p.x, sgy = (double)p.y;
+            const double dvv = e * fma(K.eu, sg, R);
+            const double dkk = fma(vv, dvv, -(e * fma(K.eu, sgy, Q)));
             if (j < Lv && cval) {
-                bstore(rdv, (float)(e * (cs + R)), voff, j * stride);
-                bstore(rdk, (float)(e * fma(cs, vv - yy, fma(vv, R, -Q))), voff, j * stride);
+                bstore(rdv, (float)dvv, voff, j * stride);
+                bstore(rdk, (float)dkk, voff, j * stride);
             }
             R = fma(R, dwf, sg);
-            Q = fma(Q, dwf, sg * yy);
+            Q = fma(Q, dwf, sgy);
         }
     } else {
         const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);

@@ -48,8 +48,10 @@ __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
 
 // Summary of one lane's chunk from the empty state, in the chunk frame: with
 // ref = max_j k_j and e_j = 2^{(k_j - ref) log2 e} <= 1 (fp64), the sums A, B, A', B'
-// after the CH tokens, at scale 2^{ref log2 e}. Horner from the first token:
-//   A'_{j+1} = e^{-w} (A'_j + A_j),   A_{j+1} = e^{-w} A_j + e_j v_j   (B, B' alike).
+// after the CH tokens, at scale 2^{ref log2 e}. Horner from the first token,
+//   A_{j+1} = d A_j + e_j v_j   (d = e^{-w}),
+// and A' = d dA/dd by the derivative recursion Q_{j+1} = d Q_j + A_j, A' = d Q (one fused
+// multiply-add per token; A'_{j+1} = d (A'_j + A_j) term by term). B, B' alike.
 // Padded tokens (k = -inf) have e_j = 0. Unless KEEPK, kc receives e_j rounded to fp32
 // (for outputs that need only fp32). Returns true (wave-uniform) if the exact form is
 // needed instead (forced, or the fp64 sums would underflow for some lane, which takes keys
@@ -65,20 +67,20 @@ __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)
         return false;
     }
     if (force_exact) return true;
-    double S = 0.0, Z = 0.0, Sp = 0.0, Zp = 0.0;
+    double S = 0.0, Z = 0.0, Qs = 0.0, Qz = 0.0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const double e = exp2_64(((double)kc[j] - refd) * kLog2eD);
         if (!KEEPK) kc[j] = (float)e;
-        Sp = dwf * (Sp + S);
-        Zp = dwf * (Zp + Z);
+        Qs = fma(Qs, dwf, S);
+        Qz = fma(Qz, dwf, Z);
         S = fma(S, dwf, e * (double)vc[j]);
         Z = fma(Z, dwf, e);
     }
     sum.a = S;
     sum.b = Z;
-    sum.ap = Sp;
-    sum.bp = Zp;
+    sum.ap = dwf * Qs;
+    sum.bp = dwf * Qz;
     return wave_any(!(Z >= kTinySum));
 }
 

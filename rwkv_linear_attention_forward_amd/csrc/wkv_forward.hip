@@ -108,22 +108,22 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
         if (slow_wave) {
             sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
         } else {
-            double S = 0.0, Z = 0.0, Sp = 0.0, Zp = 0.0;
+            double S = 0.0, Z = 0.0, Qs = 0.0, Qz = 0.0;
 #pragma unroll 1
             for (int i = 0; i < CH; ++i) {
                 const bool in = i < Lj;
                 const float ki = in ? kp[(int64_t)i * C] : -__builtin_inff();
                 const double e = exp2_64(((double)ki - refd) * kLog2eD);
                 const double vi = in ? (double)vp[(int64_t)i * C] : 0.0;
-                Sp = dwfd * (Sp + S);
-                Zp = dwfd * (Zp + Z);
+                Qs = fma(Qs, dwfd, S);
+                Qz = fma(Qz, dwfd, Z);
                 S = fma(S, dwfd, e * vi);
                 Z = fma(Z, dwfd, e);
             }
             sj.a = S;
             sj.b = Z;
-            sj.ap = Sp;
-            sj.bp = Zp;
+            sj.ap = dwfd * Qs;
+            sj.bp = dwfd * Qz;
             if (wave_any(!(Z >= kTinySum))) sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
         }
     }
@@ -250,6 +250,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     if (!exact) {
         const double gap = mine.P - ref2;
         bool bad = gap > (double)kCarryGap;
+        float dmin = __builtin_inff();
         const double s0 = exp2_64(gap);
         float Sx = (float)(mine.a * s0), Zx = (float)(mine.b * s0);
 #pragma unroll
@@ -257,12 +258,12 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             const float e = kc[j], ev = e * vc[j];
             const float num = fmaf(eu, ev, Sx);
             const float den = fmaf(eu, e, Zx);
-            bad |= !(den >= kTinyDen) & (j < Lv);
+            dmin = (j < Lv) ? fminf(dmin, den) : dmin;
             kc[j] = num * rcpf(den);
             Sx = fmaf(Sx, dc.dwf, ev);
             Zx = fmaf(Zx, dc.dwf, e);
         }
-        exact = wave_any(bad);
+        exact = wave_any(bad || !(dmin >= kTinyDen));
     }
     if (exact) {
         if (cval) exact_outputs<CH>(k, v, y, row0, t0, Lv, C, cl, ref, mine, uc, dc);
