@@ -91,11 +91,16 @@ def _match(per, needle):
 
 
 def summarize_counters(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the WKV kernels, each scaled by what the
+    same counter reads for the 1 GiB device copy of a --with-copy run (the runtime's
+    copyBuffer kernel: reads and writes exactly COPY_BYTES)."""
     fetch = _per_dispatch(_read_counter_rows(fetch_dir), "FETCH_SIZE")
     write = _per_dispatch(_read_counter_rows(write_dir), "WRITE_SIZE")
-    # the copy kernel: the dispatch whose counters are closest to 1 GiB each way
-    copy_f = max(v for vs in fetch.values() for v in vs)
-    copy_w = max(v for vs in write.values() for v in vs)
+    big = COPY_BYTES / 1024 / 4  # the copy's dispatches, not the runtime's small blits
+    copy_f = statistics.median(v for n, vs in fetch.items() if "copyBuffer" in n for v in vs
+                               if v > big)
+    copy_w = statistics.median(v for n, vs in write.items() if "copyBuffer" in n for v in vs
+                               if v > big)
     out = {"source_sha256": source_hash(),
            "copy_kib_expected": COPY_BYTES / 1024,
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,

@@ -113,13 +113,13 @@ int check_device(const char *fn) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
-int64_t nchunk_of(int64_t T) { return (T + wkvdev::kFwdChunk - 1) / wkvdev::kFwdChunk; }
+int64_t nchunk_of(int64_t T) { return (T + wkvdev::kCinChunk - 1) / wkvdev::kCinChunk; }
 int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
 // Forward workspace: flags, aggregates, inclusive carries, chunk carries (see wkv_launch.h).
 size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
-    const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
+    const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
     const size_t cin = (size_t)B * (size_t)nchunk_of(T) * (size_t)C * 5u * sizeof(double);
     return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256) +
            round_up(cin, 256);
@@ -128,15 +128,15 @@ size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
 wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     wkvdev::FwdLayout L;
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
-    const size_t recs = (size_t)B * nseg * (size_t)C * sizeof(wkvdev::Rec);
+    const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
     char *p = static_cast<char *>(ws);
     L.nseg = (int64_t)nseg;
     L.nchunk = nchunk_of(T);
     L.flags = reinterpret_cast<uint64_t *>(p);
     p += round_up((size_t)B * ngrp * nseg * 8u, 256);
-    L.agg = reinterpret_cast<wkvdev::Rec *>(p);
+    L.agg = reinterpret_cast<double *>(p);
     p += round_up(recs, 256);
-    L.incl = reinterpret_cast<wkvdev::Rec *>(p);
+    L.incl = reinterpret_cast<double *>(p);
     p += round_up(recs, 256);
     L.cin = reinterpret_cast<double *>(p);
     return L;
@@ -149,7 +149,7 @@ size_t bwd_own_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)bseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t n = (size_t)B * nseg * (size_t)C;
     return round_up((size_t)B * ngrp * nseg * 8u, 256) +
-           2 * round_up(n * sizeof(wkvdev::RevRec), 256) + round_up(n * 2 * sizeof(double), 256) +
+           2 * round_up(n * (wkvdev::kRevFields * sizeof(double)), 256) + round_up(n * 2 * sizeof(double), 256) +
            round_up(ngrp * 8u, 256);
 }
 
@@ -161,11 +161,11 @@ wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     L.nseg = (int64_t)nseg;
     L.flags = reinterpret_cast<uint64_t *>(p);
     p += round_up((size_t)B * ngrp * nseg * 8u, 256);
-    L.ragg = reinterpret_cast<wkvdev::RevRec *>(p);
-    p += round_up(n * sizeof(wkvdev::RevRec), 256);
-    L.rincl = reinterpret_cast<wkvdev::RevRec *>(p);
-    p += round_up(n * sizeof(wkvdev::RevRec), 256);
-    L.part = reinterpret_cast<uint64_t *>(p);
+    L.ragg = reinterpret_cast<double *>(p);
+    p += round_up(n * (wkvdev::kRevFields * sizeof(double)), 256);
+    L.rincl = reinterpret_cast<double *>(p);
+    p += round_up(n * (wkvdev::kRevFields * sizeof(double)), 256);
+    L.part = reinterpret_cast<double *>(p);
     p += round_up(n * 2 * sizeof(double), 256);
     L.ctr = reinterpret_cast<uint64_t *>(p);
     return L;

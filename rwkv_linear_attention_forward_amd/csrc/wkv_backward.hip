@@ -82,13 +82,14 @@ __device__ __forceinline__ void rnormalize(RevCarry &c) {
     }
 }
 
-__device__ __forceinline__ void put_rrec(RevRec *p, const RevCarry &c) {
-    put_u64(&p->g, c.g);
-    put_u64(&p->h, c.h);
-    put_u64(&p->r, c.r);
+// Reverse record i of n (fields g, h, r at stride n).
+__device__ __forceinline__ void put_rrec(double *p, int64_t n, int64_t i, const RevCarry &c) {
+    put_u64(p + i, c.g);
+    put_u64(p + n + i, c.h);
+    put_u64(p + 2 * n + i, c.r);
 }
-__device__ __forceinline__ RevCarry get_rrec(const RevRec *p) {
-    return RevCarry{get_u64(&p->g), get_u64(&p->h), get_u64(&p->r)};
+__device__ __forceinline__ RevCarry get_rrec(const double *p, int64_t n, int64_t i) {
+    return RevCarry{get_u64(p + i), get_u64(p + n + i), get_u64(p + 2 * n + i)};
 }
 
 // ---------------------------------------------------------------------------------
@@ -371,8 +372,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
     const double *__restrict__ cin, int64_t ncin, float *__restrict__ dk,
     float *__restrict__ dv, float *__restrict__ dw, float *__restrict__ du,
-    uint64_t *__restrict__ flags, RevRec *__restrict__ ragg, RevRec *__restrict__ rincl,
-    uint64_t *__restrict__ part, uint64_t *__restrict__ ctr) {
+    uint64_t *__restrict__ flags, double *__restrict__ ragg, double *__restrict__ rincl,
+    double *__restrict__ part, uint64_t *__restrict__ ctr) {
     constexpr int WIN = NW * CH;
     __shared__ BwdShared<NW, CH> sh;
 
@@ -412,9 +413,10 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     RevCarry agg, lfut;
     window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2, agg, lfut);
     const int64_t rec = (bidx * nseg + s) * C + cl;
+    const int64_t nrec = B * nseg * C;
     uint64_t *myflag = flags + sidx * nbg + bg;
     if (q == 0) {
-        if (cval) put_rrec(ragg + rec, agg);
+        if (cval) put_rrec(ragg, nrec, rec, agg);
         put_flag(myflag, epoch, kAggregate);
     }
 
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
                 RevCarry agg_j, lf_j;
                 window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
                 if (q == 0) {
-                    if (cval) put_rrec(ragg + (bidx * nseg + j) * C + cl, agg_j);
+                    if (cval) put_rrec(ragg, nrec, (bidx * nseg + j) * C + cl, agg_j);
                     raise_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kAggregate);
                 }
             }
@@ -454,12 +456,13 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             }
             ++j;
         }
-        if (j < nseg) fut = get_rrec(rincl + (bidx * nseg + j) * C + cl);
+        if (j < nseg) fut = get_rrec(rincl, nrec, (bidx * nseg + j) * C + cl);
         for (int64_t m = j - 1; m > s; --m)
-            fut = rfollow(fut, get_rrec(ragg + (bidx * nseg + m) * C + cl), (double)WIN * K.w2);
+            fut = rfollow(fut, get_rrec(ragg, nrec, (bidx * nseg + m) * C + cl),
+                          (double)WIN * K.w2);
     }
     if (q == 0) {
-        if (cval) put_rrec(rincl + rec, rfollow(fut, agg, (double)WIN * K.w2));
+        if (cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2));
         put_flag(myflag, epoch, kInclusive);
     }
 
@@ -511,8 +514,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             sw += sh.b[qq][lane];
         }
         if (cval) {
-            put_u64(part + rec * 2, -sw);
-            put_u64(part + rec * 2 + 1, su);
+            put_u64(part + rec, -sw);
+            put_u64(part + nrec + rec, su);
         }
         publish_fence();
         if (lane == 0) sh.status[0] = (arrive(ctr + grp, epoch) == (uint64_t)(B * nseg)) ? 1 : 0;
@@ -522,8 +525,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     consume_fence();
     double sw = 0.0, su = 0.0;
     for (int64_t i = q; i < B * nseg; i += NW) {
-        sw += get_u64(part + (i * C + cl) * 2);
-        su += get_u64(part + (i * C + cl) * 2 + 1);
+        sw += get_u64(part + i * C + cl);
+        su += get_u64(part + nrec + i * C + cl);
     }
     sh.a[q][lane] = sw;
     sh.b[q][lane] = su;
@@ -555,7 +558,7 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, cons
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
-    hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kFwdChunk>), dim3((unsigned)units),
+    hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk>), dim3((unsigned)units),
                        dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, F.nchunk,
                        epoch, w, u, k, v, dy, F.cin, B * F.nchunk * C, dk, dv, dw, du, L.flags,
                        L.ragg, L.rincl, L.part, L.ctr);

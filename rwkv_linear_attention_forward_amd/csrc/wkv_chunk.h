@@ -182,24 +182,26 @@ __device__ __forceinline__ float chunk_ref(const float (&kc)[CH], int Lv) {
 // (buffer_wbl2 / buffer_inv), which costs microseconds per publication here.
 __device__ __forceinline__ void publish_fence() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void consume_fence() { asm volatile("" ::: "memory"); }
-__device__ __forceinline__ void put_u64(uint64_t *p, double x) {
-    __hip_atomic_store(p, __builtin_bit_cast(uint64_t, x), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void put_u64(double *p, double x) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, x),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ double get_u64(const uint64_t *p) {
-    return __builtin_bit_cast(double,
-                              __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ double get_u64(const double *p) {
+    return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const uint64_t *>(p),
+                                                        __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT));
 }
-__device__ __forceinline__ void put_rec(Rec *r, const Carry &c) {
-    put_u64(&r->a, c.a);
-    put_u64(&r->b, c.b);
-    put_u64(&r->ap, c.ap);
-    put_u64(&r->bp, c.bp);
-    put_u64(&r->P, c.P);
+// Forward record i of n (fields a, b, a', b', P at stride n).
+__device__ __forceinline__ void put_rec(double *r, int64_t n, int64_t i, const Carry &c) {
+    put_u64(r + i, c.a);
+    put_u64(r + n + i, c.b);
+    put_u64(r + 2 * n + i, c.ap);
+    put_u64(r + 3 * n + i, c.bp);
+    put_u64(r + 4 * n + i, c.P);
 }
-__device__ __forceinline__ Carry get_rec(const Rec *r) {
-    return Carry{get_u64(&r->a), get_u64(&r->b), get_u64(&r->ap), get_u64(&r->bp),
-                 get_u64(&r->P)};
+__device__ __forceinline__ Carry get_rec(const double *r, int64_t n, int64_t i) {
+    return Carry{get_u64(r + i), get_u64(r + n + i), get_u64(r + 2 * n + i),
+                 get_u64(r + 3 * n + i), get_u64(r + 4 * n + i)};
 }
 __device__ __forceinline__ void put_flag(uint64_t *f, uint64_t epoch, uint64_t status) {
     publish_fence();

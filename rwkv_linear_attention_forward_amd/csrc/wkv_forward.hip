@@ -142,7 +142,8 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk, uint64_t epoch,
     const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
     const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
-    Rec *__restrict__ agg, Rec *__restrict__ incl, double *__restrict__ cin, int64_t ncin) {
+    double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
+    int64_t ncin) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
 
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const int64_t rec = (bidx * nseg + s) * C + cl;
     uint64_t *myflag = flags + s * nbg + bg;
     if (q == 0) {
-        if (cval) put_rec(agg + rec, run);
+        if (cval) put_rec(agg, nrec, rec, run);
         put_flag(myflag, epoch, kAggregate);
     }
 
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
                 const Carry X = window_aggregate<NW, CH>(sh, j, q, lane, T, C, row0, cl, k, v,
                                                          slow_wave, dwfd, wd, cw2);
                 if (q == 0) {
-                    if (cval) put_rec(agg + (bidx * nseg + j) * C + cl, X);
+                    if (cval) put_rec(agg, nrec, (bidx * nseg + j) * C + cl, X);
                     raise_flag(flags + j * nbg + bg, epoch, kAggregate);
                 }
             }
@@ -231,18 +232,24 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             --j;
         }
         // j is the window with a published inclusive carry, or -1
-        if (j >= 0) prefix = get_rec(incl + (bidx * nseg + j) * C + cl);
+        if (j >= 0) prefix = get_rec(incl, nrec, (bidx * nseg + j) * C + cl);
         for (int64_t m = j + 1; m < s; ++m)
-            prefix = follow(prefix, get_rec(agg + (bidx * nseg + m) * C + cl), ww2, (double)WIN);
+            prefix = follow(prefix, get_rec(agg, nrec, (bidx * nseg + m) * C + cl), ww2,
+                            (double)WIN);
     }
     if (q == 0) {
-        if (cval) put_rec(incl + rec, follow(prefix, run, ww2, (double)WIN));
+        if (cval) put_rec(incl, nrec, rec, follow(prefix, run, ww2, (double)WIN));
         put_flag(myflag, epoch, kInclusive);
     }
     // ---- the carry entering this wave's chunk, kept for the backward pass ----
     Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
-    if (Lv > 0 && cval) put_cin(cin, ncin, (bidx * nchunk + s * NW + q) * C + cl, mine);
+    {
+        // the carry entering every kCinChunk tokens (every CPC-th chunk) is kept
+        constexpr int CPC = kCinChunk / CH;
+        const int64_t gq = s * NW + q;
+        if (Lv > 0 && cval && gq % CPC == 0) put_cin(cin, ncin, (bidx * nchunk + gq / CPC) * C + cl, mine);
+    }
     if (y == nullptr || Lv == 0) return;
 
     // ---- phase 3: outputs ----
@@ -286,7 +293,8 @@ hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const
     const int64_t units = nbg * L.nseg;
     hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
                        dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, L.nchunk, epoch,
-                       w, u, k, v, y, L.flags, L.agg, L.incl, L.cin, B * L.nchunk * C);
+                       w, u, k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin,
+                       B * L.nchunk * C);
     return hipGetLastError();
 }
 

@@ -11,23 +11,28 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdChunk = 32;
 constexpr int kFwdWindow = kFwdWaves * kFwdChunk;
 
+// The forward keeps the carry entering every kCinChunk tokens; the backward's chunks are
+// exactly these spans.
+constexpr int kCinChunk = 32;
+static_assert(kCinChunk % kFwdChunk == 0 && kFwdWindow % kCinChunk == 0,
+              "carry chunks must be whole forward chunks and tile the forward window");
+
 // Publication status of a unit (low 2 bits of its flag; the high bits hold the call epoch).
 constexpr uint64_t kAggregate = 1;
 constexpr uint64_t kInclusive = 2;
 constexpr int kPollTries = 2000;  // bounded wait before a missing aggregate is recomputed
 
-// A carry or window summary as published: A = a 2^P, B = b 2^P and the age-weighted
-// A' = a' 2^P, B' = b' 2^P (fp64 bits each).
-struct Rec {
-    uint64_t a, b, ap, bp;
-    uint64_t P;
-};
+// Published carries and summaries are stored one fp64 array per field (field f of
+// record i at f * n + i, n records), so that a wave's 64 channels write and read 512
+// contiguous bytes per field. A forward record has the fields (a, b, a', b', P):
+// A = a 2^P, B = b 2^P and the age-weighted A' = a' 2^P, B' = b' 2^P.
+constexpr int kRecFields = 5;
 
 // Forward workspace, carved out of the caller's buffer (see wkv_api.hip):
 //   flags[nseg][B * ngrp]   uint64 publication flags
-//   agg[B][nseg][C]         window aggregates (from the empty state)
-//   incl[B][nseg][C]        inclusive carries: the state after window s, i.e. entering s+1
-//   cin[5][B][nchunk][C]    the carry entering every kFwdChunk-token chunk, normalized,
+//   agg[5][B][nseg][C]      window aggregates (from the empty state)
+//   incl[5][B][nseg][C]     inclusive carries: the state after window s, i.e. entering s+1
+//   cin[5][B][nchunk][C]    the carry entering every kCinChunk-token chunk, normalized,
 //                           one fp64 array per field (a, b, a', b', P) so that a wave's
 //                           64 channels read and write 512 contiguous bytes per field;
 //                           the backward pass starts each of its chunks from these.
@@ -35,37 +40,34 @@ struct FwdLayout {
     int64_t nseg;
     int64_t nchunk;
     uint64_t *flags;
-    Rec *agg;
-    Rec *incl;
+    double *agg;
+    double *incl;
     double *cin;
 };
 
-// A reverse carry or reverse window summary as published: the future sums
-//   G = sum_{t>=t0} e^{-(t-t0)w} s_t,  H = same with s_t y_t
-// (s_t = dy_t / D_t), held as (g, h) 2^r (fp64 bits each).
-struct RevRec {
-    uint64_t g, h;
-    uint64_t r;
-};
+// A reverse record has the fields (g, h, r): the future sums
+//   G = sum_{t>=t0} e^{-(t-t0)w} s_t,  H = same with s_t y_t   (s_t = dy_t / D_t)
+// held as (g, h) 2^r.
+constexpr int kRevFields = 3;
 
-// Backward geometry: a unit is 64 channels x kBwdWaves chunks of kFwdChunk tokens (the
-// chunks must coincide with the forward's, whose entering carries they start from).
+// Backward geometry: a unit is 64 channels x kBwdWaves chunks of kCinChunk tokens (each
+// starts from the carry the forward kept for it).
 constexpr int kBwdWaves = 4;
-constexpr int kBwdWindow = kBwdWaves * kFwdChunk;
+constexpr int kBwdWindow = kBwdWaves * kCinChunk;
 
 // Backward workspace:
 //   flags[nseg][B * ngrp]    uint64 publication flags (reverse direction)
-//   ragg[B][nseg][C]         reverse window aggregates (from a zero future)
-//   rincl[B][nseg][C]        reverse inclusive carries: the future sums entering window s
-//   part[B][nseg][C][2]      per-window dw, du partials (fp64)
+//   ragg[3][B][nseg][C]      reverse window aggregates (from a zero future)
+//   rincl[3][B][nseg][C]     reverse inclusive carries: the future sums entering window s
+//   part[2][B][nseg][C]      per-window dw, du partials (fp64)
 //   ctr[ngrp]                per channel group: arrivals of this call's units, tagged with
 //                            the call epoch; the last unit to arrive sums the partials
 struct BwdLayout {
     int64_t nseg;
     uint64_t *flags;
-    RevRec *ragg;
-    RevRec *rincl;
-    uint64_t *part;  // fp64 bits
+    double *ragg;
+    double *rincl;
+    double *part;
     uint64_t *ctr;
 };
 
