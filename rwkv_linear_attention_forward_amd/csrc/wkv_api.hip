@@ -143,14 +143,13 @@ wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
 }
 
 // Backward workspace: flags, reverse aggregates, reverse inclusive carries, per-window dw/du
-// partials, arrival counters, then (without a forward workspace) a forward workspace of
-// its own.
+// partials, then (without a forward workspace) a forward workspace of its own.
 size_t bwd_own_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)bseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t n = (size_t)B * nseg * (size_t)C;
     return round_up((size_t)B * ngrp * nseg * 8u, 256) +
-           2 * round_up(n * (wkvdev::kRevFields * sizeof(double)), 256) + round_up(n * 2 * sizeof(double), 256) +
-           round_up(ngrp * 8u, 256);
+           2 * round_up(n * (wkvdev::kRevFields * sizeof(double)), 256) +
+           round_up(n * 2 * sizeof(double), 256);
 }
 
 wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
@@ -166,8 +165,6 @@ wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     L.rincl = reinterpret_cast<double *>(p);
     p += round_up(n * (wkvdev::kRevFields * sizeof(double)), 256);
     L.part = reinterpret_cast<double *>(p);
-    p += round_up(n * 2 * sizeof(double), 256);
-    L.ctr = reinterpret_cast<uint64_t *>(p);
     return L;
 }
 
@@ -195,19 +192,56 @@ bool grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
     return true;
 }
 
-// The backward's arrival counters count B * ceil(T / window) units per channel group.
+// The backward's grid: B * ceil(C/64) * ceil(T / window) workgroups.
 bool bwd_grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
-    if (!grid_ok(B, T, C, fn)) return false;
-    const int64_t per_group = B * bseg_of(T);
-    if (per_group >= (int64_t(1) << wkvdev::kCountBits)) {
-        fail(WKV_ERR_INVALID_ARG, "%s: B*ceil(T/%d)=%lld exceeds 2^%d-1", fn, wkvdev::kBwdWindow,
-             (long long)per_group, wkvdev::kCountBits);
+    const int64_t units = B * ((C + 63) / 64) * bseg_of(T);
+    if (units > INT32_MAX) {
+        fail(WKV_ERR_INVALID_ARG, "%s: %lld workgroups exceed 2^31-1", fn, (long long)units);
         return false;
     }
-    return true;
+    return grid_ok(B, T, C, fn);
 }
 
 }  // namespace
+
+namespace wkvdev {
+
+hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out) {
+    struct Entry {
+        int dev;
+        const void *kernel;
+        int threads;
+        int64_t n;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int ncache = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (int i = 0; i < ncache; ++i)
+            if (cache[i].dev == dev && cache[i].kernel == kernel && cache[i].threads == threads) {
+                *out = cache[i].n;
+                return hipSuccess;
+            }
+    }
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (ncache < 64) cache[ncache++] = Entry{dev, kernel, threads, n};
+    }
+    *out = n;
+    return hipSuccess;
+}
+
+}  // namespace wkvdev
 
 extern "C" {
 

@@ -348,23 +348,6 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const Rev
     }
 }
 
-// Count this unit's arrival in its channel group's counter and return the count. The
-// counter holds (epoch << kCountBits) | count; a value from another call (other epoch)
-// restarts the count. The caller's partials are stored (device scope) and complete before
-// it arrives, and the unit that sees the final count reads them only afterwards.
-__device__ __forceinline__ uint64_t arrive(uint64_t *ctr, uint64_t epoch) {
-    const uint64_t tag = epoch & ((uint64_t(1) << (64 - kCountBits)) - 1);
-    uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const uint64_t nv = ((old >> kCountBits) == tag) ? old + 1 : ((tag << kCountBits) | 1u);
-        if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            consume_fence();
-            return nv & ((uint64_t(1) << kCountBits) - 1);
-        }
-    }
-}
-
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk,
@@ -373,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     const double *__restrict__ cin, int64_t ncin, float *__restrict__ dk,
     float *__restrict__ dv, float *__restrict__ dw, float *__restrict__ du,
     uint64_t *__restrict__ flags, double *__restrict__ ragg, double *__restrict__ rincl,
-    double *__restrict__ part, uint64_t *__restrict__ ctr) {
+    double *__restrict__ part) {
     constexpr int WIN = NW * CH;
     __shared__ BwdShared<NW, CH> sh;
 
@@ -501,41 +484,63 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
                                      K.uc, wc, d0, d1);
     }
 
-    // ---- dw, du: this window's partial (its chunks summed in a fixed order), then the
-    // last unit of the channel group to arrive sums all partials in a fixed order ----
+    // ---- dw, du: this window's partial, its chunks summed in a fixed order ----
     __syncthreads();
     sh.a[q][lane] = du_acc;
     sh.b[q][lane] = dw_acc;
     __syncthreads();
-    if (q == 0) {
+    if (q == 0 && cval) {
         double su = 0.0, sw = 0.0;
         for (int qq = 0; qq < NW; ++qq) {
             su += sh.a[qq][lane];
             sw += sh.b[qq][lane];
         }
-        if (cval) {
-            put_u64(part + rec, -sw);
-            put_u64(part + nrec + rec, su);
-        }
-        publish_fence();
-        if (lane == 0) sh.status[0] = (arrive(ctr + grp, epoch) == (uint64_t)(B * nseg)) ? 1 : 0;
+        part[rec] = -sw;
+        part[nrec + rec] = su;
     }
-    __syncthreads();
-    if (sh.status[0] == 0) return;
-    consume_fence();
+}
+
+// dw[c], du[c]: the sums of the B * nseg window partials of each channel, in a fixed order.
+// One workgroup per 64 channels; wave q sums partials q, q + RW, q + 2 RW, ... (loads
+// issued in batches), then wave 0 adds the RW wave sums in order.
+constexpr int kReduceWaves = 16;
+
+__global__ __launch_bounds__(kReduceWaves * 64) void wkv_reduce_kernel(
+    int64_t npart, int64_t C, const double *__restrict__ part, float *__restrict__ dw,
+    float *__restrict__ du) {
+    constexpr int RW = kReduceWaves, RB = 8;
+    __shared__ double sw_[RW][64], su_[RW][64];
+    const int lane = threadIdx.x & 63;
+    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t cl = c < C ? c : C - 1;
+    const int64_t nrec = npart * C;
     double sw = 0.0, su = 0.0;
-    for (int64_t i = q; i < B * nseg; i += NW) {
-        sw += get_u64(part + i * C + cl);
-        su += get_u64(part + nrec + i * C + cl);
+    for (int64_t i0 = q; i0 < npart; i0 += (int64_t)RW * RB) {
+        double a[RB], b[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t i = i0 + (int64_t)r * RW;
+            const int64_t ic = i < npart ? i : npart - 1;
+            a[r] = part[ic * C + cl];
+            b[r] = part[nrec + ic * C + cl];
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (i0 + (int64_t)r * RW < npart) {
+                sw += a[r];
+                su += b[r];
+            }
+        }
     }
-    sh.a[q][lane] = sw;
-    sh.b[q][lane] = su;
+    sw_[q][lane] = sw;
+    su_[q][lane] = su;
     __syncthreads();
-    if (q == 0 && cval) {
+    if (q == 0 && c < C) {
         double tw = 0.0, tu = 0.0;
-        for (int qq = 0; qq < NW; ++qq) {
-            tw += sh.a[qq][lane];
-            tu += sh.b[qq][lane];
+        for (int qq = 0; qq < RW; ++qq) {
+            tw += sw_[qq][lane];
+            tu += su_[qq][lane];
         }
         dw[c] = (float)tw;
         du[c] = (float)tu;
@@ -561,7 +566,11 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, cons
     hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk>), dim3((unsigned)units),
                        dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, F.nchunk,
                        epoch, w, u, k, v, dy, F.cin, B * F.nchunk * C, dk, dv, dw, du, L.flags,
-                       L.ragg, L.rincl, L.part, L.ctr);
+                       L.ragg, L.rincl, L.part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)ngrp), dim3(kReduceWaves * 64), 0,
+                       stream, B * L.nseg, C, L.part, dw, du);
     return hipGetLastError();
 }
 

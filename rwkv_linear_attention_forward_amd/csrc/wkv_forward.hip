@@ -237,10 +237,9 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             prefix = follow(prefix, get_rec(agg, nrec, (bidx * nseg + m) * C + cl), ww2,
                             (double)WIN);
     }
-    if (q == 0) {
-        if (cval) put_rec(incl, nrec, rec, follow(prefix, run, ww2, (double)WIN));
-        put_flag(myflag, epoch, kInclusive);
-    }
+    // The inclusive record is stored now; wave 0 stores its flag after the output sweep
+    // below, so that the wait for the record's stores to complete overlaps the sweep.
+    if (q == 0 && cval) put_rec(incl, nrec, rec, follow(prefix, run, ww2, (double)WIN));
     // ---- the carry entering this wave's chunk, kept for the backward pass ----
     Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
@@ -250,7 +249,10 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         const int64_t gq = s * NW + q;
         if (Lv > 0 && cval && gq % CPC == 0) put_cin(cin, ncin, (bidx * nchunk + gq / CPC) * C + cl, mine);
     }
-    if (y == nullptr || Lv == 0) return;
+    if (y == nullptr || Lv == 0) {
+        if (q == 0) put_flag(myflag, epoch, kInclusive);
+        return;
+    }
 
     // ---- phase 3: outputs ----
     const double ref2 = (double)ref * kLog2eD;
@@ -272,6 +274,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         }
         exact = wave_any(bad || !(dmin >= kTinyDen));
     }
+    if (q == 0) put_flag(myflag, epoch, kInclusive);
     if (exact) {
         if (cval) exact_outputs<CH>(k, v, y, row0, t0, Lv, C, cl, ref, mine, uc, dc);
         return;

@@ -7,7 +7,7 @@
 namespace wkvdev {
 
 // Forward geometry: a unit is 64 channels x one window of kFwdWaves * kFwdChunk tokens.
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 2;
 constexpr int kFwdChunk = 32;
 constexpr int kFwdWindow = kFwdWaves * kFwdChunk;
 
@@ -52,27 +52,25 @@ constexpr int kRevFields = 3;
 
 // Backward geometry: a unit is 64 channels x kBwdWaves chunks of kCinChunk tokens (each
 // starts from the carry the forward kept for it).
-constexpr int kBwdWaves = 4;
+constexpr int kBwdWaves = 2;
 constexpr int kBwdWindow = kBwdWaves * kCinChunk;
 
 // Backward workspace:
 //   flags[nseg][B * ngrp]    uint64 publication flags (reverse direction)
 //   ragg[3][B][nseg][C]      reverse window aggregates (from a zero future)
 //   rincl[3][B][nseg][C]     reverse inclusive carries: the future sums entering window s
-//   part[2][B][nseg][C]      per-window dw, du partials (fp64)
-//   ctr[ngrp]                per channel group: arrivals of this call's units, tagged with
-//                            the call epoch; the last unit to arrive sums the partials
+//   part[2][B][nseg][C]      per-window dw, du partials (fp64), summed by a second kernel
 struct BwdLayout {
     int64_t nseg;
     uint64_t *flags;
     double *ragg;
     double *rincl;
     double *part;
-    uint64_t *ctr;
 };
 
-// Units per channel group (B * nseg) must fit the arrival counter's 24-bit count.
-constexpr int kCountBits = 24;
+// Workgroups of `kernel` (block of `threads`, static LDS only) that the current device holds
+// at once: its occupancy per CU times the CU count (cached per device and kernel).
+hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out);
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                           const float *k, const float *v, float *y, const FwdLayout &L,

@@ -45,7 +45,7 @@ def _r256(x):
     return (x + 255) // 256 * 256
 
 
-def _fwd_bytes(B, T, C, window=128, chunk=32):
+def _fwd_bytes(B, T, C, window=64, chunk=32):
     """Forward workspace: flags, window aggregates and inclusive carries (40 B records), and
     the carry entering every chunk (5 fp64 fields)."""
     nseg, nchunk, ngrp = -(-T // window), -(-T // chunk), -(-C // 64)
@@ -53,12 +53,11 @@ def _fwd_bytes(B, T, C, window=128, chunk=32):
             + _r256(B * nchunk * C * 40))
 
 
-def _bwd_bytes(B, T, C, window=128):
+def _bwd_bytes(B, T, C, window=64):
     """Backward workspace: flags, reverse aggregates and inclusive carries (24 B records),
-    dw/du partials (2 fp64), arrival counters (one per channel group)."""
+    dw/du partials (2 fp64)."""
     nseg, ngrp = -(-T // window), -(-C // 64)
-    return (_r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 24) + _r256(B * nseg * C * 16)
-            + _r256(ngrp * 8))
+    return _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 24) + _r256(B * nseg * C * 16)
 
 
 def test_sizes(pkg):
@@ -69,7 +68,7 @@ def test_sizes(pkg):
         own = _bwd_bytes(B, T, C)
         assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
         assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
-    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 512 + 1280
+    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 1280
     assert lib.wkv_forward_workspace_size(-1, 4, 4) == 0
     assert lib.wkv_forward_workspace_size(1, 4, (1 << 24) + 1) == 0
 
