@@ -398,8 +398,12 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     const int64_t rec = (bidx * nseg + s) * C + cl;
     const int64_t nrec = B * nseg * C;
     uint64_t *myflag = flags + sidx * nbg + bg;
+    // the next window's flag is read before this unit's flag store, so that one wait
+    // covers the aggregate's stores and that read
+    uint64_t next = 0;
     if (q == 0) {
         if (cval) put_rrec(ragg, nrec, rec, agg);
+        if (s < nseg - 1) next = peek_flag(myflag - nbg);
         put_flag(myflag, epoch, kAggregate);
     }
 
@@ -414,7 +418,11 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
         int it = 0;
         for (;;) {
             if (q == 0) {
-                const int st = poll_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kPollTries);
+                int st = it == 0 ? flag_status(next, epoch) : 0;
+                if (st != 0)
+                    consume_fence();
+                else
+                    st = poll_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kPollTries);
                 if (lane == 0) sh.status[it & 1] = st;
             }
             __syncthreads();
@@ -444,10 +452,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             fut = rfollow(fut, get_rrec(ragg, nrec, (bidx * nseg + m) * C + cl),
                           (double)WIN * K.w2);
     }
-    if (q == 0) {
-        if (cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2));
-        put_flag(myflag, epoch, kInclusive);
-    }
+    if (q == 0 && cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2));
 
     // ---- R3: dk, dv of this chunk ----
     const rsrc_t rdk = make_rsrc(dk + (row0 + (t0 < T ? t0 : 0)) * C);
@@ -456,9 +461,10 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     rnormalize(rc);
     const double rgap = (double)ref * kLog2eD + rc.r;
     const bool rx = fx || wave_any(rgap > (double)kCarryGap);
-    if (Lv == 0) {
-        // past the sequence end: nothing to store
-    } else if (!rx) {
+    // The sweep's arithmetic runs before wave 0 stores the inclusive flag, so that the wait
+    // for the record's stores overlaps it; dv, dk replace e, v in kc, vc and are stored
+    // after the flag.
+    if (Lv != 0 && !rx) {
         const double fr = exp2_64(rgap);
         const double dwf = K.dwf;
         double R = rc.g * fr, Q = rc.h * fr;
@@ -470,12 +476,22 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             const double sg = (double)p.x, sgy = (double)p.y;
             const double dvv = e * fma(K.eu, sg, R);
             const double dkk = fma(vv, dvv, -(e * fma(K.eu, sgy, Q)));
-            if (j < Lv && cval) {
-                bstore(rdv, (float)dvv, voff, j * stride);
-                bstore(rdk, (float)dkk, voff, j * stride);
-            }
+            kc[j] = (float)dvv;
+            vc[j] = (float)dkk;
             R = fma(R, dwf, sg);
             Q = fma(Q, dwf, sgy);
+        }
+    }
+    if (q == 0) put_flag(myflag, epoch, kInclusive);
+    if (Lv == 0) {
+        // past the sequence end: nothing to store
+    } else if (!rx) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (j < Lv && cval) {
+                bstore(rdv, kc[j], voff, j * stride);
+                bstore(rdk, vc[j], voff, j * stride);
+            }
         }
     } else {
         const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);

@@ -214,6 +214,38 @@ __device__ __forceinline__ void raise_flag(uint64_t *f, uint64_t epoch, uint64_t
     __hip_atomic_fetch_max(f, (epoch << 2) | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One relaxed read of a flag, not yet interpreted: a unit issues it before its own
+// publish_fence, so that the wait for its record stores also covers this read's round
+// trip (the loads and stores of a wave complete in order).
+__device__ __forceinline__ uint64_t peek_flag(const uint64_t *f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The status a peeked flag value shows for this call (0 if none).
+__device__ __forceinline__ int flag_status(uint64_t x, uint64_t epoch) {
+    return (x >> 2) == epoch ? (int)(x & 3u) : 0;
+}
+
+// Look-back read in one batch: lane i < kPeekDepth of the publishing wave peeks the flag of
+// the unit i+1 places before its own in scan order (position p-1-i for a unit at position
+// p of its chain), all lanes in one load instruction.
+constexpr int kPeekDepth = 8;
+
+// Depth d >= 1 when the unit d places back holds an inclusive carry (or d == p: the chain
+// start, an empty carry) and every unit in between has published at least its aggregate;
+// 0 when the batch does not settle the walk (the caller then polls unit by unit). Called
+// by a whole wave, lane i holding the value it peeked.
+__device__ __forceinline__ int peek_depth(uint64_t x, uint64_t epoch, int lane, int64_t p) {
+    const int n = p < kPeekDepth ? (int)p : kPeekDepth;
+    const int st = lane < n ? flag_status(x, epoch) : 0;
+    uint64_t incl = __ballot(st == (int)kInclusive);
+    if (p <= kPeekDepth) incl |= 1ull << p;
+    const uint64_t ok = __ballot(st != 0);
+    if (incl == 0) return 0;
+    const int i = __builtin_ctzll(incl);
+    const uint64_t below = (1ull << i) - 1;
+    return (ok & below) == below ? i + 1 : 0;
+}
+
 // Status of a unit's publication for this call: 1 aggregate, 2 inclusive carry, or 0 if
 // nothing was published within `tries` polls (the caller then recomputes; no unit ever
 // waits without bound).

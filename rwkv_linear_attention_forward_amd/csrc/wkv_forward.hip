@@ -66,6 +66,7 @@ template <int NW>
 struct FwdShared {
     double a[NW][64], b[NW][64], ap[NW][64], bp[NW][64], P[NW][64];
     int status[2];
+    int depth;
 };
 
 template <int NW>
@@ -192,9 +193,17 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     }
     const int64_t rec = (bidx * nseg + s) * C + cl;
     uint64_t *myflag = flags + s * nbg + bg;
+    // the flags of the previous kPeekDepth windows are read before this unit's flag store,
+    // so that one wait covers the aggregate's stores and those reads
     if (q == 0) {
         if (cval) put_rec(agg, nrec, rec, run);
+        uint64_t pk = 0;
+        if (lane < kPeekDepth && lane < s) pk = peek_flag(myflag - (int64_t)(lane + 1) * nbg);
         put_flag(myflag, epoch, kAggregate);
+        if (s > 0) {
+            const int d = peek_depth(pk, epoch, lane, s);
+            if (lane == 0) sh.depth = d;
+        }
     }
 
     // ---- look-back: carry entering this window ----
@@ -204,36 +213,48 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // incl[s] = fold(incl[s-1], agg[s]) whatever the timing, so every run is deterministic.
     Carry prefix = carry_empty();
     if (s > 0) {
-        int64_t j = s - 1;
-        int it = 0;
-        for (;;) {
-            if (q == 0) {
-                const int st = poll_flag(flags + j * nbg + bg, epoch, kPollTries);
-                if (lane == 0) sh.status[it & 1] = st;
-            }
-            __syncthreads();
-            const int st = sh.status[it & 1];
-            ++it;
-            if (st == (int)kInclusive) break;
-            if (st != (int)kAggregate) {
-                // not published in time: compute window j's aggregate here and publish it
-                // (bitwise what unit j itself publishes)
-                const Carry X = window_aggregate<NW, CH>(sh, j, q, lane, T, C, row0, cl, k, v,
-                                                         slow_wave, dwfd, wd, cw2);
+        __syncthreads();
+        const int d = sh.depth;
+        int64_t j = s - d;  // settled by the batch of peeks when d > 0
+        if (d == 0) {
+            j = s - 1;
+            int it = 0;
+            for (;;) {
                 if (q == 0) {
-                    if (cval) put_rec(agg, nrec, (bidx * nseg + j) * C + cl, X);
-                    raise_flag(flags + j * nbg + bg, epoch, kAggregate);
+                    const int st = poll_flag(flags + j * nbg + bg, epoch, kPollTries);
+                    if (lane == 0) sh.status[it & 1] = st;
                 }
+                __syncthreads();
+                const int st = sh.status[it & 1];
+                ++it;
+                if (st == (int)kInclusive) break;
+                if (st != (int)kAggregate) {
+                    // not published in time: compute window j's aggregate here and publish
+                    // it (bitwise what unit j itself publishes)
+                    const Carry X = window_aggregate<NW, CH>(sh, j, q, lane, T, C, row0, cl, k,
+                                                             v, slow_wave, dwfd, wd, cw2);
+                    if (q == 0) {
+                        if (cval) put_rec(agg, nrec, (bidx * nseg + j) * C + cl, X);
+                        raise_flag(flags + j * nbg + bg, epoch, kAggregate);
+                    }
+                }
+                if (j == 0) {
+                    j = -1;
+                    break;
+                }
+                --j;
             }
-            if (j == 0) {
-                j = -1;
-                break;
-            }
-            --j;
         }
-        // j is the window with a published inclusive carry, or -1
+        // j is the window with a published inclusive carry, or -1; the records are read
+        // two at a time so that their round trips overlap
         if (j >= 0) prefix = get_rec(incl, nrec, (bidx * nseg + j) * C + cl);
-        for (int64_t m = j + 1; m < s; ++m)
+        int64_t m = j + 1;
+        for (; m + 1 < s; m += 2) {
+            const Carry a0 = get_rec(agg, nrec, (bidx * nseg + m) * C + cl);
+            const Carry a1 = get_rec(agg, nrec, (bidx * nseg + m + 1) * C + cl);
+            prefix = follow(follow(prefix, a0, ww2, (double)WIN), a1, ww2, (double)WIN);
+        }
+        if (m < s)
             prefix = follow(prefix, get_rec(agg, nrec, (bidx * nseg + m) * C + cl), ww2,
                             (double)WIN);
     }
