@@ -113,14 +113,13 @@ int check_device(const char *fn) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
-int64_t nchunk_of(int64_t T) { return (T + wkvdev::kCinChunk - 1) / wkvdev::kCinChunk; }
 int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
 // Forward workspace: flags, aggregates, inclusive carries, chunk carries (see wkv_launch.h).
 size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
     const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
-    const size_t cin = (size_t)B * (size_t)nchunk_of(T) * (size_t)C * 5u * sizeof(double);
+    const size_t cin = recs * (size_t)wkvdev::kCinCarries;
     return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256) +
            round_up(cin, 256);
 }
@@ -131,7 +130,6 @@ wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
     char *p = static_cast<char *>(ws);
     L.nseg = (int64_t)nseg;
-    L.nchunk = nchunk_of(T);
     L.flags = reinterpret_cast<uint64_t *>(p);
     p += round_up((size_t)B * ngrp * nseg * 8u, 256);
     L.agg = reinterpret_cast<double *>(p);

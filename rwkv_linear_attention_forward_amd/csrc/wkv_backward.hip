@@ -199,8 +199,8 @@ struct BwdConst {
 // multiply-add is written out; the build does not contract).
 template <int CH>
 __device__ __forceinline__ RevCarry chunk_pass(
-    int64_t ci, int64_t T, int64_t C, int64_t nchunk, const double *__restrict__ cin,
-    int64_t ncin, int64_t bidx, int64_t row0, int cl, int voff, int stride,
+    int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
+    int cl, int voff, int stride,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
     const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
     float2 (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
@@ -218,7 +218,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
         fx = false;
         return rev_zero();
     }
-    const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
+    const Carry fin = chunk_carry(F, bidx, ci, C, cl);
     const double gap = fin.P - ref2;
     fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
     double R = 0.0, Q = 0.0;
@@ -277,8 +277,8 @@ __device__ __forceinline__ RevCarry chunk_pass(
 // in registers across the look-back.
 template <int CH>
 __device__ __forceinline__ RevCarry helper_summary(
-    int64_t ci, int64_t T, int64_t C, int64_t nchunk, const double *__restrict__ cin,
-    int64_t ncin, int64_t bidx, int64_t row0, int cl, const float *__restrict__ k,
+    int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
+    int cl, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ dy, const BwdConst &K) {
     const int64_t t0 = ci * CH;
     const int Lv = chunk_len(t0, T, CH);
@@ -291,7 +291,7 @@ __device__ __forceinline__ RevCarry helper_summary(
     for (int j = 0; j < Lv; ++j) ref = fmaxf(ref, kp[(int64_t)j * C]);
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
-    const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
+    const Carry fin = chunk_carry(F, bidx, ci, C, cl);
     const double gap = fin.P - ref2;
     bool fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
     if (!fx) {
@@ -350,10 +350,10 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const Rev
 
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
-    int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk,
+    int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg,
     uint64_t epoch, const float *__restrict__ w, const float *__restrict__ u,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
-    const double *__restrict__ cin, int64_t ncin, float *__restrict__ dk,
+    const FwdCarries F, float *__restrict__ dk,
     float *__restrict__ dv, float *__restrict__ dw, float *__restrict__ du,
     uint64_t *__restrict__ flags, double *__restrict__ ragg, double *__restrict__ rincl,
     double *__restrict__ part) {
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     float ref;
     int Lv;
     double du_acc, dw_acc;
-    RevCarry rsum = chunk_pass<CH>(ci, T, C, nchunk, cin, ncin, bidx, row0, cl, voff, stride,
+    RevCarry rsum = chunk_pass<CH>(ci, T, C, F, bidx, row0, cl, voff, stride,
                                          k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref, Lv,
                                          du_acc, dw_acc);
     RevCarry agg, lfut;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: recompute window j's reverse aggregate here and
                 // publish it (bitwise what unit j itself publishes)
-                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, nchunk, cin, ncin,
+                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, F,
                                                          bidx, row0, cl, k, v, dy, K);
                 RevCarry agg_j, lf_j;
                 window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             }
         }
     } else {
-        const Carry fin = get_cin(cin, ncin, (bidx * nchunk + ci) * C + cl);
+        const Carry fin = chunk_carry(F, bidx, ci, C, cl);
         double d0 = 0.0, d1 = 0.0;
         exact_chunk<CH, true, false>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
                                      K.uc, wc, d0, d1);
@@ -579,10 +579,10 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, cons
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
+    const FwdCarries fc{F.incl, F.cin, B * F.nseg * C, F.nseg};
     hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk>), dim3((unsigned)units),
-                       dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, F.nchunk,
-                       epoch, w, u, k, v, dy, F.cin, B * F.nchunk * C, dk, dv, dw, du, L.flags,
-                       L.ragg, L.rincl, L.part);
+                       dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, epoch, w, u,
+                       k, v, dy, fc, dk, dv, dw, du, L.flags, L.ragg, L.rincl, L.part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)ngrp), dim3(kReduceWaves * 64), 0,

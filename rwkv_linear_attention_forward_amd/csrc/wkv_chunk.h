@@ -273,6 +273,35 @@ __device__ __forceinline__ Carry get_cin(const double *f, int64_t n, int64_t i) 
     return Carry{f[i], f[n + i], f[2 * n + i], f[3 * n + i], f[4 * n + i]};
 }
 
+// Where the backward finds the forward carries: the inclusive records (nrec = B*nseg*C of
+// them per field) and the kept chunk carries of a finished forward launch.
+struct FwdCarries {
+    const double *incl;
+    const double *cin;
+    int64_t nrec;
+    int64_t nseg;
+};
+
+// The forward carry entering kCinChunk-token chunk ci of sequence bidx, channel cl: for a
+// chunk that opens forward window s, the inclusive carry of window s-1 normalized (the
+// empty carry for s = 0) -- bitwise the carry the forward computed for that chunk, since
+// folding in an empty summary over no tokens leaves a carry unchanged -- else the carry
+// the forward kept (plain loads: the records come from an earlier launch).
+__device__ __forceinline__ Carry chunk_carry(const FwdCarries &F, int64_t bidx, int64_t ci,
+                                             int64_t C, int cl) {
+    constexpr int CPW = kCinCarries + 1;
+    const int64_t s = ci / CPW;
+    const int r = (int)(ci - s * CPW);
+    if (r == 0) {
+        if (s == 0) return carry_empty();
+        Carry c = get_cin(F.incl, F.nrec, (bidx * F.nseg + s - 1) * C + cl);
+        normalize(c);
+        return c;
+    }
+    return get_cin(F.cin, F.nrec * kCinCarries,
+                   ((bidx * F.nseg + s) * kCinCarries + (r - 1)) * C + cl);
+}
+
 // c <- fold of a carry and a summary (the summary follows c in time, `len` tokens,
 // len_w2 = len w log2 e).
 __device__ __forceinline__ Carry follow(Carry c, const Carry &sum, double len_w2, double len) {

@@ -140,11 +140,10 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
 
 template <int NW, int CH>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
-    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, int64_t nchunk, uint64_t epoch,
+    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
     const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
     const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
-    double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
-    int64_t ncin) {
+    double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
 
@@ -265,10 +264,13 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
     {
-        // the carry entering every kCinChunk tokens (every CPC-th chunk) is kept
+        // the carry entering each kCinChunk-token chunk of the window but its first (that
+        // one is the previous window's inclusive carry) is kept
         constexpr int CPC = kCinChunk / CH;
-        const int64_t gq = s * NW + q;
-        if (Lv > 0 && cval && gq % CPC == 0) put_cin(cin, ncin, (bidx * nchunk + gq / CPC) * C + cl, mine);
+        const int r = q / CPC;
+        if (Lv > 0 && cval && q % CPC == 0 && r > 0)
+            put_cin(cin, nrec * kCinCarries, ((bidx * nseg + s) * kCinCarries + r - 1) * C + cl,
+                    mine);
     }
     if (y == nullptr || Lv == 0) {
         if (q == 0) put_flag(myflag, epoch, kInclusive);
@@ -316,9 +318,8 @@ hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
-                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, L.nchunk, epoch,
-                       w, u, k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin,
-                       B * L.nchunk * C);
+                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
+                       k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin);
     return hipGetLastError();
 }
 

@@ -11,11 +11,14 @@ constexpr int kFwdWaves = 2;
 constexpr int kFwdChunk = 32;
 constexpr int kFwdWindow = kFwdWaves * kFwdChunk;
 
-// The forward keeps the carry entering every kCinChunk tokens; the backward's chunks are
-// exactly these spans.
+// The backward starts each kCinChunk-token chunk from the forward carry entering it: a
+// chunk that opens a forward window starts from the previous window's inclusive carry
+// (published anyway), the other kCinCarries chunks of a window from a carry the forward
+// keeps for them.
 constexpr int kCinChunk = 32;
 static_assert(kCinChunk % kFwdChunk == 0 && kFwdWindow % kCinChunk == 0,
               "carry chunks must be whole forward chunks and tile the forward window");
+constexpr int kCinCarries = kFwdWindow / kCinChunk - 1;
 
 // Publication status of a unit (low 2 bits of its flag; the high bits hold the call epoch).
 constexpr uint64_t kAggregate = 1;
@@ -32,13 +35,12 @@ constexpr int kRecFields = 5;
 //   flags[nseg][B * ngrp]   uint64 publication flags
 //   agg[5][B][nseg][C]      window aggregates (from the empty state)
 //   incl[5][B][nseg][C]     inclusive carries: the state after window s, i.e. entering s+1
-//   cin[5][B][nchunk][C]    the carry entering every kCinChunk-token chunk, normalized,
-//                           one fp64 array per field (a, b, a', b', P) so that a wave's
-//                           64 channels read and write 512 contiguous bytes per field;
-//                           the backward pass starts each of its chunks from these.
+//   cin[5][B][nseg][kCinCarries][C]  the carry entering each kCinChunk-token chunk of a
+//                           window but its first, normalized, one fp64 array per field
+//                           (a, b, a', b', P) so that a wave's 64 channels read and write
+//                           512 contiguous bytes per field.
 struct FwdLayout {
     int64_t nseg;
-    int64_t nchunk;
     uint64_t *flags;
     double *agg;
     double *incl;

@@ -47,10 +47,11 @@ def _r256(x):
 
 def _fwd_bytes(B, T, C, window=64, chunk=32):
     """Forward workspace: flags, window aggregates and inclusive carries (40 B records), and
-    the carry entering every chunk (5 fp64 fields)."""
-    nseg, nchunk, ngrp = -(-T // window), -(-T // chunk), -(-C // 64)
+    the carry entering each chunk of a window but its first (5 fp64 fields)."""
+    nseg, ngrp = -(-T // window), -(-C // 64)
+    kept = window // chunk - 1
     return (_r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 40)
-            + _r256(B * nchunk * C * 40))
+            + _r256(B * nseg * kept * C * 40))
 
 
 def _bwd_bytes(B, T, C, window=64):
@@ -68,7 +69,7 @@ def test_sizes(pkg):
         own = _bwd_bytes(B, T, C)
         assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
         assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
-    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 1280
+    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 768
     assert lib.wkv_forward_workspace_size(-1, 4, 4) == 0
     assert lib.wkv_forward_workspace_size(1, 4, (1 << 24) + 1) == 0
 
