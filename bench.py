@@ -18,6 +18,11 @@ reported only while the kernel sources still hash to the value recorded there.
 threads) on the same workload. `decode` reports the batched decode step separately
 (B=256, C=5120, 40 layer states, 36 B per element per call).
 
+The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
+load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
+kernels run up to a third slower before they reach a steady rate, and the default timed
+steps (100) are taken there.
+
 Helpers for the counter summaries:
     python bench.py --with-copy ...        also runs a 1 GiB device copy (known bytes)
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
@@ -243,8 +248,8 @@ def bench_decode(wkv, torch, dev, steps=20, warmup=3):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--with-copy", action="store_true",

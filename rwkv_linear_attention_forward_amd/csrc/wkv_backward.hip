@@ -517,46 +517,49 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
 }
 
 // dw[c], du[c]: the sums of the B * nseg window partials of each channel, in a fixed order.
-// One workgroup per 64 channels; wave q sums partials q, q + RW, q + 2 RW, ... (loads
-// issued in batches), then wave 0 adds the RW wave sums in order.
-constexpr int kReduceWaves = 16;
+// A workgroup takes kReduceCh channels (one 128-byte row segment of each partial array) and
+// kReduceSlices row slices: thread (slice r, channel) sums partials r, r + RS, r + 2 RS, ...
+// (loads issued in batches), then slice 0 adds the RS slice sums in order. ceil(C/16)
+// workgroups: enough to spread the 16 B per window and channel over the whole chip.
+constexpr int kReduceCh = 16;      // channels of a workgroup: one 128-byte row of fp64
+constexpr int kReduceSlices = 32;  // row slices of a workgroup
 
-__global__ __launch_bounds__(kReduceWaves * 64) void wkv_reduce_kernel(
+__global__ __launch_bounds__(kReduceCh * kReduceSlices) void wkv_reduce_kernel(
     int64_t npart, int64_t C, const double *__restrict__ part, float *__restrict__ dw,
     float *__restrict__ du) {
-    constexpr int RW = kReduceWaves, RB = 8;
-    __shared__ double sw_[RW][64], su_[RW][64];
-    const int lane = threadIdx.x & 63;
-    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    constexpr int RS = kReduceSlices, RB = 8;
+    __shared__ double sw_[RS][kReduceCh], su_[RS][kReduceCh];
+    const int ch = (int)threadIdx.x % kReduceCh;
+    const int sl = (int)threadIdx.x / kReduceCh;
+    const int64_t c = (int64_t)blockIdx.x * kReduceCh + ch;
     const int64_t cl = c < C ? c : C - 1;
     const int64_t nrec = npart * C;
     double sw = 0.0, su = 0.0;
-    for (int64_t i0 = q; i0 < npart; i0 += (int64_t)RW * RB) {
+    for (int64_t i0 = sl; i0 < npart; i0 += (int64_t)RS * RB) {
         double a[RB], b[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int64_t i = i0 + (int64_t)r * RW;
+            const int64_t i = i0 + (int64_t)r * RS;
             const int64_t ic = i < npart ? i : npart - 1;
             a[r] = part[ic * C + cl];
             b[r] = part[nrec + ic * C + cl];
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            if (i0 + (int64_t)r * RW < npart) {
+            if (i0 + (int64_t)r * RS < npart) {
                 sw += a[r];
                 su += b[r];
             }
         }
     }
-    sw_[q][lane] = sw;
-    su_[q][lane] = su;
+    sw_[sl][ch] = sw;
+    su_[sl][ch] = su;
     __syncthreads();
-    if (q == 0 && c < C) {
+    if (sl == 0 && c < C) {
         double tw = 0.0, tu = 0.0;
-        for (int qq = 0; qq < RW; ++qq) {
-            tw += sw_[qq][lane];
-            tu += su_[qq][lane];
+        for (int r = 0; r < RS; ++r) {
+            tw += sw_[r][ch];
+            tu += su_[r][ch];
         }
         dw[c] = (float)tw;
         du[c] = (float)tu;
@@ -585,7 +588,8 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, cons
                        k, v, dy, fc, dk, dv, dw, du, L.flags, L.ragg, L.rincl, L.part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)ngrp), dim3(kReduceWaves * 64), 0,
+    hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),
+                       dim3(kReduceCh * kReduceSlices), 0,
                        stream, B * L.nseg, C, L.part, dw, du);
     return hipGetLastError();
 }
