@@ -173,6 +173,7 @@ struct BwdShared {
     double a[NW][64];
     double b[NW][64];
     double r[NW][64];
+    double pu[NW][64], pw[NW][64];  // each wave's du, dw terms
     float2 sy[NW][CH][64];
     int status[2];
 };
@@ -236,8 +237,10 @@ __device__ __forceinline__ RevCarry chunk_pass(
         double dmin = __builtin_inf();
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0
-            const double e = exp2_64(((double)kc[j] - refd) * kLog2eD);
+            // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0; the clamp on den
+            // keeps 1/den finite where a padded token's den (the decayed carry alone) falls
+            // below the fp32 range, so that its sigma is 0 and not NaN
+            const double e = exp2_64(fma((double)kc[j], kLog2eD, -ref2));
             const double vv = (double)vc[j];
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
@@ -247,9 +250,10 @@ __device__ __forceinline__ RevCarry chunk_pass(
             const double yv = num * r;
             const double sg = (double)gc[j] * r;
             const double sgy = sg * yv;
-            // dw term s (A' - y B') / d, du term s e^{u+k} (v - y), both in the frame
+            // dw term s (A' - y B') / d and du term s e^{k} (v - y), both in the frame; the
+            // common factors d and e^u are applied after the loop
             dw_acc = fma(sg, fma(-yv, Pz, Ps), dw_acc);
-            du_acc = fma(sg * (K.eu * e), vv - yv, du_acc);
+            du_acc = fma(sg, fma(-e, yv, ev), du_acc);
             R = fma(pw, sg, R);
             Q = fma(pw, sgy, Q);
             kc[j] = (float)e;
@@ -261,6 +265,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
             Zx = fma(Zx, K.dwf, e);
         }
         dw_acc *= K.dwf;
+        du_acc *= K.eu;
         fx = wave_any(!(dmin >= (double)kTinyDen));
     }
     if (!fx) return RevCarry{R, Q, -ref2};
@@ -303,7 +308,7 @@ __device__ __forceinline__ RevCarry helper_summary(
         for (int j = 0; j < CH; ++j) {
             const bool in = j < Lv;
             const float kj = in ? kp[(int64_t)j * C] : -__builtin_inff();
-            const double e = exp2_64(((double)kj - refd) * kLog2eD);
+            const double e = exp2_64(fma((double)kj, kLog2eD, -ref2));
             const double vv = in ? (double)vp[(int64_t)j * C] : 0.0;
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
@@ -393,6 +398,9 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     RevCarry rsum = chunk_pass<CH>(ci, T, C, F, bidx, row0, cl, voff, stride,
                                          k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref, Lv,
                                          du_acc, dw_acc);
+    // the dw, du terms are staged with the reverse summaries (the fold's barrier covers both)
+    sh.pu[q][lane] = du_acc;
+    sh.pw[q][lane] = dw_acc;
     RevCarry agg, lfut;
     window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2, agg, lfut);
     const int64_t rec = (bidx * nseg + s) * C + cl;
@@ -402,7 +410,17 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     // covers the aggregate's stores and that read
     uint64_t next = 0;
     if (q == 0) {
-        if (cval) put_rrec(ragg, nrec, rec, agg);
+        if (cval) {
+            put_rrec(ragg, nrec, rec, agg);
+            // this window's dw, du partial: its chunks' terms summed in a fixed order
+            double su = 0.0, sw = 0.0;
+            for (int qq = 0; qq < NW; ++qq) {
+                su += sh.pu[qq][lane];
+                sw += sh.pw[qq][lane];
+            }
+            part[rec] = -sw;
+            part[nrec + rec] = su;
+        }
         if (s < nseg - 1) next = peek_flag(myflag - nbg);
         put_flag(myflag, epoch, kAggregate);
     }
@@ -498,21 +516,6 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
         double d0 = 0.0, d1 = 0.0;
         exact_chunk<CH, true, false>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
                                      K.uc, wc, d0, d1);
-    }
-
-    // ---- dw, du: this window's partial, its chunks summed in a fixed order ----
-    __syncthreads();
-    sh.a[q][lane] = du_acc;
-    sh.b[q][lane] = dw_acc;
-    __syncthreads();
-    if (q == 0 && cval) {
-        double su = 0.0, sw = 0.0;
-        for (int qq = 0; qq < NW; ++qq) {
-            su += sh.a[qq][lane];
-            sw += sh.b[qq][lane];
-        }
-        part[rec] = -sw;
-        part[nrec + rec] = su;
     }
 }
 

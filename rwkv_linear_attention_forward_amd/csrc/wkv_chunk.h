@@ -61,7 +61,8 @@ __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)
                                               float ref, bool force_exact, double dwf,
                                               Carry &sum) {
     const double refd = (double)ref;
-    sum = Carry{0.0, 0.0, 0.0, 0.0, refd * kLog2eD};
+    const double ref2 = refd * kLog2eD;
+    sum = Carry{0.0, 0.0, 0.0, 0.0, ref2};
     if (Lv == 0) {
         sum.P = kNegBigD;
         return false;
@@ -70,7 +71,7 @@ __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)
     double S = 0.0, Z = 0.0, Qs = 0.0, Qz = 0.0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const double e = exp2_64(((double)kc[j] - refd) * kLog2eD);
+        const double e = exp2_64(fma((double)kc[j], kLog2eD, -ref2));
         if (!KEEPK) kc[j] = (float)e;
         Qs = fma(Qs, dwf, S);
         Qz = fma(Qz, dwf, Z);

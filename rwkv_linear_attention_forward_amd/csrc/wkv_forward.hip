@@ -114,7 +114,7 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
             for (int i = 0; i < CH; ++i) {
                 const bool in = i < Lj;
                 const float ki = in ? kp[(int64_t)i * C] : -__builtin_inff();
-                const double e = exp2_64(((double)ki - refd) * kLog2eD);
+                const double e = exp2_64(fma((double)ki, kLog2eD, -sj.P));
                 const double vi = in ? (double)vp[(int64_t)i * C] : 0.0;
                 Qs = fma(Qs, dwfd, S);
                 Qz = fma(Qz, dwfd, Z);
