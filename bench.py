@@ -6,7 +6,7 @@ that workspace and writes dk, dv, dw, du. Inputs are synthetic and seeded (the
 distributions of the 3B-class layer workload in wkv_inputs.py) and resident in HBM
 before timing starts; the step reuses preallocated outputs and workspaces.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-state]
 
 prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
 `roofline` describes the kernel that takes most of the step, with its algorithmic bytes
@@ -16,7 +16,8 @@ library launches on. `traffic` comes from a committed rocprofv3 counter summary 
 reported only while the kernel sources still hash to the value recorded there.
 `cpu_baseline` times the fp64 CPU oracle (test infrastructure, OpenMP over all host
 threads) on the same workload. `decode` reports the batched decode step separately
-(B=256, C=5120, 40 layer states, 36 B per element per call).
+(B=256, C=5120, 40 layer states, 36 B per element per call); `forward_state` the forward
+from a given state that also returns the final state (prompt prefill), on the same layer.
 
 The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
 load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
@@ -245,6 +246,34 @@ def bench_decode(wkv, torch, dev, steps=20, warmup=3):
             "calls_per_step": L}
 
 
+def bench_forward_state(wkv, torch, dev, x, steps=100, warmup=100):
+    """The forward from a state on the benchmark layer (prompt prefill), back to back as the
+    step is timed: each call starts from the state the previous one left (random at first)
+    and leaves y and the final state; 12 B per element plus 24 B of state per (b, c)."""
+    import wkv_inputs
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v")}
+    B, T, C = t["k"].shape
+    st = [torch.from_numpy(a).to(dev) for a in wkv_inputs.random_state(B, C, seed=1006)]
+    ws = wkv.forward_workspace(B, T, C, dev)
+    y = torch.empty_like(t["k"])
+    for _ in range(warmup):
+        wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws, out=y)
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws, out=y)
+        e1.record()
+    torch.cuda.synchronize(dev)
+    us = statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    ok = bool(torch.isfinite(y).all()) and all(bool(torch.isfinite(a).all()) for a in st)
+    gbps = (12 * B * T * C + 24 * B * C) / (us * 1e-6) / 1e9
+    return {"workload": "forward from a state, B=%d T=%d C=%d" % (B, T, C),
+            "us": us, "elem_per_s": B * T * C / (us * 1e-6), "algorithmic_gbps": gbps,
+            "frac_of_peak": gbps / PEAK_GBPS, "steps": steps, "outputs_finite": ok}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +281,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-state", action="store_true",
+                    help="skip the forward-from-a-state measurement")
     ap.add_argument("--with-copy", action="store_true",
                     help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -313,6 +344,8 @@ def main(argv=None):
         out["copy_1gib"] = bench_copy(torch, dev)
     if not args.no_decode:
         out["decode"] = bench_decode(wkv, torch, dev)
+    if not args.no_state:
+        out["forward_state"] = bench_forward_state(wkv, torch, dev, x)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)
     else:

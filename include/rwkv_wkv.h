@@ -55,10 +55,12 @@ const char *wkv_status_string(int status);
 /* Message of the last failing call made by this thread ("" if none). Never NULL. */
 const char *wkv_last_error(void);
 
-/* Bytes of device scratch that wkv_forward needs for (B, T, C): publication flags plus,
- * for every (b, c) sequence and every 256-token window, the window's aggregate and the
- * recurrent state after it (the two sums of the recursive form with their scale), 32 bytes
- * per window. Returns 0 for invalid dims. */
+/* Bytes of device scratch that wkv_forward and wkv_forward_state need for (B, T, C):
+ * publication flags plus, for every (b, c) sequence and every 64-token window, the
+ * window's aggregate and the recurrent state after it, the state entering the window's
+ * second 32-token chunk (each: the two sums of the recursive form, their age-weighted
+ * counterparts and their scale, 40 bytes), and per (b, c) the state before token 0 and the
+ * final state. Returns 0 for invalid dims. */
 size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 
 /* Forward: y [B][T][C] from k, v [B][T][C] and w, u [C], starting from the empty state
@@ -67,10 +69,26 @@ size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C);
  * `workspace_bytes`) is required whenever B*T*C > 0; its previous content is ignored. After
  * the call it holds the states at window boundaries, which wkv_backward can reuse to skip
  * its own pass over k and v; it must not be used by two calls at the same time.
- * Requires C <= 2^24 and B*ceil(C/64)*ceil(T/256) < 2^31. */
+ * Requires C <= 2^24 and B*ceil(C/64)*ceil(T/64) < 2^31. */
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                 const float *k, const float *v, float *y, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* Forward from a given state, leaving the state after the last token: the T tokens run as
+ * in wkv_forward, but the scan starts from the decode state (a, b, p) [B][C] (same meaning
+ * as in wkv_decode_step: A = a e^p, B = b e^p) instead of the empty one, and a, b, p are
+ * overwritten with the state after token T-1, ready for wkv_decode_step. This is the
+ * prompt-then-generate use of the recursive form ("RWKV についての調査記録", section
+ * "コードを見ながらRWKVの構造を把握": the prompt's tokens go through the layer one after
+ * another, each updating the state, before the next token is predicted), with the prompt
+ * run in parallel. y and the workspace are as for wkv_forward (same size); a wkv_backward
+ * given this workspace treats the initial state as a constant (no gradient flows to it).
+ * The final state is accurate to fp32 (p is rounded first, a and b rescaled to match).
+ * a, b, p must not overlap each other, k, v, y, w, u or the workspace. A zero-sized
+ * dimension is a no-op that leaves the state unchanged. */
+int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, float *y, float *a, float *b, float *p,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device scratch that wkv_backward needs. With have_fwd_workspace != 0 the caller
  * will pass the workspace that wkv_forward filled for the same inputs; otherwise the

@@ -8,6 +8,7 @@ been built; there is no CPU fallback.
 Entry points mirror the C ABI in include/rwkv_wkv.h:
 
     forward(w, u, k, v, workspace=None) -> y
+    forward_state(w, u, k, v, a, b, p, workspace=None) -> y   (a, b, p: state in, state out)
     forward_workspace(B, T, C, device) -> uint8 tensor sized for the forward
     backward(w, u, k, v, dy, fwd_workspace=None) -> (dk, dv, dw, du)
     decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
@@ -33,7 +34,8 @@ WKV_ERR_HIP = 3
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
-           "wkv_forward", "wkv_backward_workspace_size", "wkv_backward", "wkv_decode_step")
+           "wkv_forward", "wkv_forward_state", "wkv_backward_workspace_size", "wkv_backward",
+           "wkv_decode_step")
 
 _lib = None
 _I64 = ctypes.c_int64
@@ -59,6 +61,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
     lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_forward_state.restype = ctypes.c_int
+    lib.wkv_forward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]
     lib.wkv_backward_workspace_size.restype = ctypes.c_size_t
     lib.wkv_backward_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
     lib.wkv_backward.restype = ctypes.c_int
@@ -153,6 +158,27 @@ def forward(w, u, k, v, workspace=None, out=None):
     _check_ws(workspace, dev, "workspace")
     _check(load_library().wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                       _ptr(workspace), workspace.numel(), _stream(dev)))
+    return y
+
+
+def forward_state(w, u, k, v, a, b, p, workspace=None, out=None):
+    """y [B,T,C] = WKV(w, u, k, v) started from the state (a, b, p) [B,C] (the decode
+    convention), which is overwritten with the state after the last token."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    for t, n in ((a, "a"), (b, "b"), (p, "p")):
+        _need(t, n, 2, dev)
+        if tuple(t.shape) != (B, C):
+            raise ValueError("%s must have shape %s, got %s" % (n, (B, C), tuple(t.shape)))
+    y = torch.empty_like(k) if out is None else out
+    _need(y, "out", 3, dev)
+    if y.shape != k.shape:
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = forward_workspace(B, T, C, dev)
+    _check_ws(workspace, dev, "workspace")
+    _check(load_library().wkv_forward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                            _ptr(y), _ptr(a), _ptr(b), _ptr(p),
+                                            _ptr(workspace), workspace.numel(), _stream(dev)))
     return y
 
 

@@ -115,13 +115,16 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
 int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
-// Forward workspace: flags, aggregates, inclusive carries, chunk carries (see wkv_launch.h).
+// Forward workspace: flags, aggregates, inclusive carries, chunk carries, the carry
+// entering token 0 and the final state (see wkv_launch.h).
 size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
-    const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
+    const size_t nbc = (size_t)B * (size_t)C;
+    const size_t recs = nbc * nseg * (wkvdev::kRecFields * sizeof(double));
     const size_t cin = recs * (size_t)wkvdev::kCinCarries;
     return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256) +
-           round_up(cin, 256);
+           round_up(cin, 256) + round_up(nbc * (wkvdev::kRecFields * sizeof(double)), 256) +
+           round_up(nbc * 3 * sizeof(float), 256);
 }
 
 wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
@@ -137,6 +140,10 @@ wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     L.incl = reinterpret_cast<double *>(p);
     p += round_up(recs, 256);
     L.cin = reinterpret_cast<double *>(p);
+    p += round_up(recs * (size_t)wkvdev::kCinCarries, 256);
+    L.init = reinterpret_cast<double *>(p);
+    p += round_up((size_t)B * (size_t)C * (wkvdev::kRecFields * sizeof(double)), 256);
+    L.fin = reinterpret_cast<float *>(p);
     return L;
 }
 
@@ -263,10 +270,15 @@ size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C) {
     return fwd_ws_bytes(B, T, C);
 }
 
-int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                const float *k, const float *v, float *y, void *workspace,
-                size_t workspace_bytes, void *stream) {
-    static const char *fn = "wkv_forward";
+}  // extern "C"
+
+namespace {
+
+// wkv_forward and wkv_forward_state: sa, sb, sp are the state arrays of the latter (all
+// three non-null) or null for the former.
+int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w,
+                 const float *u, const float *k, const float *v, float *y, float *sa,
+                 float *sb, float *sp, void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
@@ -290,12 +302,54 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
         overlap(workspace, need, v, nb) || overlap(workspace, need, w, C * 4u) ||
         overlap(workspace, need, u, C * 4u))
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
+    if (sa != nullptr) {
+        const size_t ns = (size_t)(B * C) * 4u;
+        float *st[3] = {sa, sb, sp};
+        const char *sn[3] = {"a", "b", "p"};
+        for (int i = 0; i < 3; ++i) {
+            if (!aligned(st[i], 4, sn[i], fn)) return WKV_ERR_INVALID_ARG;
+            if (overlap(st[i], ns, k, nb) || overlap(st[i], ns, v, nb) ||
+                overlap(st[i], ns, y, nb) || overlap(st[i], ns, w, C * 4u) ||
+                overlap(st[i], ns, u, C * 4u) || overlap(st[i], ns, workspace, need))
+                return fail(WKV_ERR_INVALID_ARG, "%s: state %s overlaps another tensor", fn,
+                            sn[i]);
+            for (int j = 0; j < i; ++j)
+                if (overlap(st[i], ns, st[j], ns))
+                    return fail(WKV_ERR_INVALID_ARG, "%s: state %s overlaps state %s", fn,
+                                sn[i], sn[j]);
+        }
+    }
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
-    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, y, fwd_layout(B, T, C, workspace),
-                                          next_epoch(), static_cast<hipStream_t>(stream));
+    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, y, sa, sb, sp,
+                                          fwd_layout(B, T, C, workspace), next_epoch(),
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                const float *k, const float *v, float *y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return forward_call("wkv_forward", B, T, C, w, u, k, v, y, nullptr, nullptr, nullptr,
+                        workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, float *y, float *a, float *b, float *p,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_forward_state";
+    if (B > 0 && T > 0 && C > 0) {
+        g_err[0] = '\0';
+        if (!nonnull(a, "a", fn) || !nonnull(b, "b", fn) || !nonnull(p, "p", fn))
+            return WKV_ERR_INVALID_ARG;
+    }
+    return forward_call(fn, B, T, C, w, u, k, v, y, a, b, p, workspace, workspace_bytes,
+                        stream);
 }
 
 size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace) {
@@ -360,7 +414,8 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
         F = fwd_layout(B, T, C, const_cast<void *>(fwd_workspace));
     } else {
         F = fwd_layout(B, T, C, own + bwd_own_bytes(B, T, C));
-        hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, F, next_epoch(), st);
+        hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, nullptr, nullptr,
+                                              nullptr, F, next_epoch(), st);
         if (e != hipSuccess) return fail_hip(e, fn);
     }
     hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, F, dk, dv, dw, du,

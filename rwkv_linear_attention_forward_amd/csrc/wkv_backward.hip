@@ -585,7 +585,7 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, cons
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
-    const FwdCarries fc{F.incl, F.cin, B * F.nseg * C, F.nseg};
+    const FwdCarries fc{F.incl, F.cin, F.init, B * F.nseg * C, F.nseg};
     hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk>), dim3((unsigned)units),
                        dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, epoch, w, u,
                        k, v, dy, fc, dk, dv, dw, du, L.flags, L.ragg, L.rincl, L.part);

@@ -279,13 +279,15 @@ __device__ __forceinline__ Carry get_cin(const double *f, int64_t n, int64_t i) 
 struct FwdCarries {
     const double *incl;
     const double *cin;
+    const double *init;  // [5][B][C]: the carry before token 0
     int64_t nrec;
     int64_t nseg;
 };
 
 // The forward carry entering kCinChunk-token chunk ci of sequence bidx, channel cl: for a
-// chunk that opens forward window s, the inclusive carry of window s-1 normalized (the
-// empty carry for s = 0) -- bitwise the carry the forward computed for that chunk, since
+// chunk that opens forward window s, the inclusive carry of window s-1 normalized (for
+// s = 0 the carry before token 0, normalized) -- bitwise the carry the forward computed for
+// that chunk, since
 // folding in an empty summary over no tokens leaves a carry unchanged -- else the carry
 // the forward kept (plain loads: the records come from an earlier launch).
 __device__ __forceinline__ Carry chunk_carry(const FwdCarries &F, int64_t bidx, int64_t ci,
@@ -294,8 +296,8 @@ __device__ __forceinline__ Carry chunk_carry(const FwdCarries &F, int64_t bidx, 
     const int64_t s = ci / CPW;
     const int r = (int)(ci - s * CPW);
     if (r == 0) {
-        if (s == 0) return carry_empty();
-        Carry c = get_cin(F.incl, F.nrec, (bidx * F.nseg + s - 1) * C + cl);
+        Carry c = s == 0 ? get_cin(F.init, F.nrec / F.nseg, bidx * C + cl)
+                         : get_cin(F.incl, F.nrec, (bidx * F.nseg + s - 1) * C + cl);
         normalize(c);
         return c;
     }

@@ -61,6 +61,64 @@ __device__ __forceinline__ void exact_outputs(const float *__restrict__ k,
     }
 }
 
+// The final state in the decode convention (fp32 a, b, p with A = a e^p, B = b e^p) from
+// sums S, Z at scale 2^P: p is rounded to fp32 first and a, b rescaled by the rounding, so
+// that the fp32 triple holds A and B to fp32 accuracy.
+__device__ __forceinline__ void store_state(double S, double Z, double P, float *__restrict__ fin,
+                                            int64_t n, int64_t i) {
+    const float p32 = (float)(P * kLn2D);
+    const double sc = exp2_64(P - (double)p32 * kLog2eD);
+    fin[i] = (float)(S * sc);
+    fin[n + i] = (float)(Z * sc);
+    fin[2 * n + i] = p32;
+}
+
+// State after token T-1 = t0 + Lv - 1, from the fp64 carry entering that token's chunk and
+// the chunk's weights e_j (fp32, in the chunk frame 2^{ref log2 e}) and values still in
+// registers: the recursion over the chunk's Lv tokens, accumulated in fp64 at the larger of
+// the two scales. One wave per sequence and channel group runs it.
+template <int CH>
+__device__ __forceinline__ void final_state(const float (&ec)[CH], const float (&vc)[CH], int Lv,
+                                         float ref, const Carry &mine, double dwf,
+                                         float *__restrict__ fin, int64_t n, int64_t i) {
+    const double ref2 = (double)ref * kLog2eD;
+    const double P = fmax(ref2, mine.P);
+    const double sc = exp2_64(mine.P - P), sk = exp2_64(ref2 - P);
+    double S = mine.a * sc, Z = mine.b * sc;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        if (j < Lv) {
+            const double e = (double)ec[j] * sk;
+            S = fma(S, dwf, e * (double)vc[j]);
+            Z = fma(Z, dwf, e);
+        }
+    }
+    store_state(S, Z, P, fin, n, i);
+}
+
+// The same for a chunk that took the per-token path (its weights are not in registers):
+// the rescaled recursion in fp64 with k and v read again from memory.
+template <int CH>
+__device__ __forceinline__ void final_state_exact(const float *__restrict__ k,
+                                               const float *__restrict__ v, int64_t row0,
+                                               int64_t t0, int Lv, int64_t C, int cl,
+                                               const Carry &mine, double w,
+                                               float *__restrict__ fin, int64_t n, int64_t i) {
+    double a = mine.a, b = mine.b, p = mine.P * kLn2D;
+#pragma unroll 1
+    for (int j = 0; j < Lv; ++j) {
+        const int64_t x = (row0 + t0 + j) * C + cl;
+        const double kk = (double)k[x], vv = (double)v[x];
+        const double pw = p - w;
+        const double m = fmax(pw, kk);
+        const double f1 = exp(pw - m), f2 = exp(kk - m);
+        a = fma(f1, a, f2 * vv);
+        b = fma(f1, b, f2);
+        p = m;
+    }
+    store_state(a, b, p * kLog2eD, fin, n, i);
+}
+
 // Window staging of chunk summaries (one per wave) for the in-window fold.
 template <int NW>
 struct FwdShared {
@@ -143,7 +201,9 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
     const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
     const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
-    double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin) {
+    double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
+    const float *__restrict__ sa, const float *__restrict__ sb, const float *__restrict__ sp,
+    double *__restrict__ init, float *__restrict__ fin) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
 
@@ -210,7 +270,13 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // start), making sure every window in between has its aggregate in memory; then fold
     // those aggregates forward in order. The result is bitwise the sequential chain
     // incl[s] = fold(incl[s-1], agg[s]) whatever the timing, so every run is deterministic.
-    Carry prefix = carry_empty();
+    // the carry before token 0: the empty carry, or the given state (A = a e^p)
+    auto start_carry = [&]() {
+        if (sa == nullptr) return carry_empty();
+        const int64_t ic = bidx * C + cl;
+        return Carry{(double)sa[ic], (double)sb[ic], 0.0, 0.0, (double)sp[ic] * kLog2eD};
+    };
+    Carry prefix = s == 0 ? start_carry() : carry_empty();
     if (s > 0) {
         __syncthreads();
         const int d = sh.depth;
@@ -246,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         }
         // j is the window with a published inclusive carry, or -1; the records are read
         // two at a time so that their round trips overlap
-        if (j >= 0) prefix = get_rec(incl, nrec, (bidx * nseg + j) * C + cl);
+        prefix = j >= 0 ? get_rec(incl, nrec, (bidx * nseg + j) * C + cl) : start_carry();
         int64_t m = j + 1;
         for (; m + 1 < s; m += 2) {
             const Carry a0 = get_rec(agg, nrec, (bidx * nseg + m) * C + cl);
@@ -271,6 +337,16 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         if (Lv > 0 && cval && q % CPC == 0 && r > 0)
             put_cin(cin, nrec * kCinCarries, ((bidx * nseg + s) * kCinCarries + r - 1) * C + cl,
                     mine);
+    }
+    // the carry entering token 0 is kept too (the backward's first chunk starts from it)
+    if (s == 0 && q == 0 && cval) put_cin(init, nrec / nseg, bidx * C + cl, mine);
+    // the wave that holds token T-1 gives the state after it, when asked for
+    if (fin != nullptr && t0 < T && T <= t0 + CH && cval) {
+        if (exact)
+            final_state_exact<CH>(k, v, row0, t0, Lv, C, cl, mine, wd, fin, nrec / nseg,
+                                  bidx * C + cl);
+        else
+            final_state<CH>(kc, vc, Lv, ref, mine, dwfd, fin, nrec / nseg, bidx * C + cl);
     }
     if (y == nullptr || Lv == 0) {
         if (q == 0) put_flag(myflag, epoch, kInclusive);
@@ -311,15 +387,34 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     }
 }
 
+// The state after the last token, from the forward's workspace into the caller's arrays.
+__global__ __launch_bounds__(256) void wkv_state_out_kernel(const float *__restrict__ fin,
+                                                            float *__restrict__ a,
+                                                            float *__restrict__ b,
+                                                            float *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        a[i] = fin[i];
+        b[i] = fin[n + i];
+        p[i] = fin[2 * n + i];
+    }
+}
+
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, const FwdLayout &L,
-                          uint64_t epoch, hipStream_t stream) {
+                          const float *k, const float *v, float *y, float *sa, float *sb,
+                          float *sp, const FwdLayout &L, uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
                        dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
-                       k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin);
+                       k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin, sa, sb, sp,
+                       L.init, sa != nullptr ? L.fin : nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sa == nullptr) return e;
+    const int64_t n = B * C;
+    hipLaunchKernelGGL(wkv_state_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, L.fin, sa, sb, sp, n);
     return hipGetLastError();
 }
 

@@ -39,12 +39,16 @@ constexpr int kRecFields = 5;
 //                           window but its first, normalized, one fp64 array per field
 //                           (a, b, a', b', P) so that a wave's 64 channels read and write
 //                           512 contiguous bytes per field.
+//   init[5][B][C]           the carry entering token 0 as the forward used it (normalized)
+//   fin[3][B][C]            fp32 state (a, b, p) after the last token, when one is asked for
 struct FwdLayout {
     int64_t nseg;
     uint64_t *flags;
     double *agg;
     double *incl;
     double *cin;
+    double *init;
+    float *fin;
 };
 
 // A reverse record has the fields (g, h, r): the future sums
@@ -74,9 +78,13 @@ struct BwdLayout {
 // at once: its occupancy per CU times the CU count (cached per device and kernel).
 hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out);
 
+// `sa`, `sb`, `sp` ([B][C], all three or none) hold the state before token 0 in the decode
+// convention (A = a e^p, B = b e^p); when given, they are overwritten with the state after
+// token T-1 (through L.fin, by a second kernel, so that no workgroup can read a state that
+// another has already replaced). Without them the scan starts from the empty state.
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, const FwdLayout &L,
-                          uint64_t epoch, hipStream_t stream);
+                          const float *k, const float *v, float *y, float *sa, float *sb,
+                          float *sp, const FwdLayout &L, uint64_t epoch, hipStream_t stream);
 
 // `F` is the forward workspace filled for the same inputs (its chunk carries are read).
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -46,12 +46,13 @@ def _r256(x):
 
 
 def _fwd_bytes(B, T, C, window=64, chunk=32):
-    """Forward workspace: flags, window aggregates and inclusive carries (40 B records), and
-    the carry entering each chunk of a window but its first (5 fp64 fields)."""
+    """Forward workspace: flags, window aggregates and inclusive carries (40 B records), the
+    carry entering each chunk of a window but its first (5 fp64 fields), the carry entering
+    token 0 (40 B per sequence and channel) and the final fp32 state (12 B)."""
     nseg, ngrp = -(-T // window), -(-C // 64)
     kept = window // chunk - 1
     return (_r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 40)
-            + _r256(B * nseg * kept * C * 40))
+            + _r256(B * nseg * kept * C * 40) + _r256(B * C * 40) + _r256(B * C * 12))
 
 
 def _bwd_bytes(B, T, C, window=64):
@@ -69,7 +70,7 @@ def test_sizes(pkg):
         own = _bwd_bytes(B, T, C)
         assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
         assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
-    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 768
+    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 768 + 256 + 256
     assert lib.wkv_forward_workspace_size(-1, 4, 4) == 0
     assert lib.wkv_forward_workspace_size(1, 4, (1 << 24) + 1) == 0
 
@@ -106,6 +107,30 @@ def test_forward_rejects_bad_arguments(pkg):
     assert b"16-byte aligned" in lib.wkv_last_error()
     # a workspace overlapping k
     assert _fwd(lib, 2, 300, 4, ws=ctypes.c_void_p(FAKE[2].value + 64)) == pkg.WKV_ERR_INVALID_ARG
+
+
+def test_forward_state_rejects_bad_arguments(pkg):
+    lib = pkg.load_library()
+    f = FAKE
+    ab, bb, pb = (ctypes.c_void_p(0x900000 + 0x10000 * i) for i in range(3))
+
+    def call(a=ab, b=bb, p=pb, B=2, T=3, C=4):
+        return lib.wkv_forward_state(B, T, C, f[0], f[1], f[2], f[3], f[4], a, b, p, f[6],
+                                     1 << 40, None)
+
+    assert call(a=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"a is NULL" in lib.wkv_last_error()
+    assert call(p=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"p is NULL" in lib.wkv_last_error()
+    assert call(b=ctypes.c_void_p(f[2].value + 8)) == pkg.WKV_ERR_INVALID_ARG  # inside k
+    assert b"state b overlaps" in lib.wkv_last_error()
+    assert call(b=ctypes.c_void_p(ab.value + 4)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"state b overlaps state a" in lib.wkv_last_error()
+    assert call(a=ctypes.c_void_p(0x900002)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"aligned" in lib.wkv_last_error()
+    # zero-sized: a no-op that touches nothing, state pointers not needed
+    assert call(a=None, b=None, p=None, T=0) == pkg.WKV_OK
+    assert lib.wkv_last_error() == b""
 
 
 def test_zero_sized_forward_is_a_noop(pkg):

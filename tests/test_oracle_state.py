@@ -1,0 +1,99 @@
+"""Pins for the oracle's forward from a given state (CPU only).
+
+Prompt tokens pass through the layer one after another, each updating the state, and the
+next token is then predicted from that state ("RWKV についての調査記録", section
+"コードを見ながらRWKVの構造を把握"; the state is what inference carries from token to
+token, same page, section "RWKVとは？"). The oracle's forward_rescaled with a given state is
+that computation. It is pinned here against the direct O(T^2) definition through a
+construction the definition itself fixes: the state (a, b, p) before token 0 holds
+A = a e^p and B = b e^p, which decay by e^{-t w} by token t, exactly as the contribution
+of one extra token placed just before the sequence with key p + ln b and value a / b
+(its weight e^{-(t-1-(-1)) w + k} = e^{-t w} b e^p). So the state-in forward equals the
+direct forward of the sequence with that token prepended, dropping its output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from state_ref import backward_with_state, prepend_state_token as _prepend
+
+
+def _rand(B, T, C, seed, kscale=1.0):
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(-6.0, 1.5, size=C))
+    u = rng.uniform(-1.0, 1.0, size=C)
+    k = kscale * rng.standard_normal((B, T, C))
+    v = rng.standard_normal((B, T, C))
+    return rng, w, u, k, v
+
+
+def _state(rng, B, C):
+    b = rng.uniform(0.5, 8.0, size=(B, C))
+    a = b * rng.standard_normal((B, C))
+    p = rng.uniform(-4.0, 4.0, size=(B, C))
+    return a, b, p
+
+
+@pytest.mark.parametrize("T", [1, 2, 17])
+def test_state_forward_equals_direct_with_prepended_token(T):
+    rng, w, u, k, v = _rand(3, T, 5, 40 + T, kscale=2.0)
+    st = _state(rng, 3, 5)
+    y, _ = oracle.forward_rescaled(w, u, k, v, st)
+    kk, vv = _prepend(st, k, v)
+    ref = oracle.forward_direct(w, u, kk, vv)[:, 1:]
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_first_output_from_a_state_closed_form():
+    # y_0 = (a e^p + e^{u+k_0} v_0) / (b e^p + e^{u+k_0}), whatever w is
+    rng, w, u, k, v = _rand(2, 1, 4, 45)
+    a, b, p = _state(rng, 2, 4)
+    y, _ = oracle.forward_rescaled(w, u, k, v, (a, b, p))
+    e = np.exp(u + k[:, 0] - p)
+    np.testing.assert_allclose(y[:, 0], (a + e * v[:, 0]) / (b + e), rtol=1e-13)
+
+
+def test_final_state_predicts_the_next_token():
+    # the state after the last token, advanced by one more token, gives that token's output
+    # of the direct form over the whole sequence (prepended state token included)
+    rng, w, u, k, v = _rand(2, 23, 6, 46, kscale=2.0)
+    st = _state(rng, 2, 6)
+    _, fin = oracle.forward_rescaled(w, u, k[:, :22], v[:, :22], st)
+    y_next, _ = oracle.decode_step(w, u, k[:, 22], v[:, 22], fin)
+    kk, vv = _prepend(st, k, v)
+    ref = oracle.forward_direct(w, u, kk, vv)[:, -1]
+    np.testing.assert_allclose(y_next, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_empty_state_is_the_plain_forward():
+    _, w, u, k, v = _rand(2, 30, 4, 47, kscale=3.0)
+    empty = (np.zeros((2, 4)), np.zeros((2, 4)), np.full((2, 4), -1e38))
+    y, _ = oracle.forward_rescaled(w, u, k, v, empty)
+    np.testing.assert_allclose(y, oracle.forward_direct(w, u, k, v), rtol=1e-11, atol=1e-13)
+
+
+def test_backward_with_state_finite_differences():
+    rng, w, u, k, v = _rand(2, 5, 3, 48, kscale=1.5)
+    st = _state(rng, 2, 3)
+    dy = rng.standard_normal(k.shape)
+    got = backward_with_state(w, u, k, v, dy, st)
+
+    def loss(w_, u_, k_, v_):
+        return float(np.sum(dy * oracle.forward_rescaled(w_, u_, k_, v_, st)[0]))
+
+    args = [w, u, k, v]
+    names = ["w", "u", "k", "v"]
+    grads = {"k": got[0], "v": got[1], "w": got[2], "u": got[3]}
+    for i, name in enumerate(names):
+        x = args[i]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-6 * max(1.0, abs(x[idx]))
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap = list(args)
+            am = list(args)
+            ap[i], am[i] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)

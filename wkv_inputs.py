@@ -71,6 +71,16 @@ def generate(name: str, seed: int | None = None, B: int | None = None, T: int | 
     return out
 
 
+def random_state(B: int, C: int, seed: int, p_range=(-4.0, 4.0)):
+    """A decode-convention state (a, b, p) [B, C] fp32 to start a forward from: b ~ U(0.5, 8),
+    a = b * N(0, 1) (so a / b, the state's mean value, is ~ N(0, 1)), p ~ U(p_range)."""
+    rng = np.random.default_rng(seed)
+    b = rng.uniform(0.5, 8.0, size=(B, C)).astype(np.float32)
+    a = (b * rng.standard_normal(size=(B, C))).astype(np.float32)
+    p = rng.uniform(p_range[0], p_range[1], size=(B, C)).astype(np.float32)
+    return a, b, p
+
+
 def decode_layer_params(layer: int, seed: int | None = None, C: int | None = None):
     """Per-layer (w, u) [C] fp32 for the batched-decode workload."""
     C = DECODE["C"] if C is None else C
