@@ -7,6 +7,7 @@ distributions of the 3B-class layer workload in wkv_inputs.py) and resident in H
 before timing starts; the step reuses preallocated outputs and workspaces.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-state]
+                    [--no-gated]
 
 prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
 `roofline` describes the kernel that takes most of the step, with its algorithmic bytes
@@ -17,7 +18,8 @@ reported only while the kernel sources still hash to the value recorded there.
 `cpu_baseline` times the fp64 CPU oracle (test infrastructure, OpenMP over all host
 threads) on the same workload. `decode` reports the batched decode step separately
 (B=256, C=5120, 40 layer states, 36 B per element per call); `forward_state` the forward
-from a given state that also returns the final state (prompt prefill), on the same layer.
+from a given state that also returns the final state (prompt prefill), on the same layer;
+`gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer.
 
 The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
 load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
@@ -274,6 +276,52 @@ def bench_forward_state(wkv, torch, dev, x, steps=100, warmup=100):
             "frac_of_peak": gbps / PEAK_GBPS, "steps": steps, "outputs_finite": ok}
 
 
+def bench_gated(wkv, torch, dev, x, steps=100, warmup=100):
+    """The receptance-gated step on the benchmark layer, back to back: forward_gated
+    (k, v, r read, out written: 16 B per element) and backward_gated (k, v, r, dout read;
+    dk, dv, dr written: 28 B per element)."""
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v", "dy")}
+    B, T, C = t["k"].shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1007)
+    r = torch.randn(B, T, C, dtype=torch.float32, device=dev, generator=gen)
+    fws = wkv.forward_workspace(B, T, C, dev)
+    bws = torch.empty(max(16, wkv.backward_workspace_size(B, T, C, True)), dtype=torch.uint8,
+                      device=dev)
+    o = torch.empty_like(t["k"])
+    outs = (torch.empty_like(t["k"]), torch.empty_like(t["k"]), torch.empty_like(t["k"]),
+            torch.empty_like(t["w"]), torch.empty_like(t["u"]))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wkv.forward_gated(t["w"], t["u"], t["k"], t["v"], r, workspace=fws, out=o)
+        if ev is not None:
+            ev[1].record()
+        wkv.backward_gated(t["w"], t["u"], t["k"], t["v"], r, t["dy"], fwd_workspace=fws,
+                           workspace=bws, out=outs)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize(dev)
+    f_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    b_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    n = B * T * C
+    ok = all(bool(torch.isfinite(a).all()) for a in (o,) + outs)
+    return {"workload": "receptance-gated forward + backward, B=%d T=%d C=%d" % (B, T, C),
+            "forward_us": f_us, "backward_us": b_us,
+            "elem_per_s": n / ((f_us + b_us) * 1e-6),
+            "forward_frac_of_peak": 16 * n / (f_us * 1e-6) / 1e9 / PEAK_GBPS,
+            "backward_frac_of_peak": 28 * n / (b_us * 1e-6) / 1e9 / PEAK_GBPS,
+            "steps": steps, "outputs_finite": ok}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +331,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-state", action="store_true",
                     help="skip the forward-from-a-state measurement")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the receptance-gated measurement")
     ap.add_argument("--with-copy", action="store_true",
                     help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -346,6 +396,8 @@ def main(argv=None):
         out["decode"] = bench_decode(wkv, torch, dev)
     if not args.no_state:
         out["forward_state"] = bench_forward_state(wkv, torch, dev, x)
+    if not args.no_gated:
+        out["gated"] = bench_gated(wkv, torch, dev, x)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)
     else:

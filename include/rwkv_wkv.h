@@ -90,7 +90,18 @@ int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const flo
                       const float *k, const float *v, float *y, float *a, float *b, float *p,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of device scratch that wkv_backward needs. With have_fwd_workspace != 0 the caller
+/* The gated forward: out = sigma(r) * y elementwise, sigma(x) = 1 / (1 + e^{-x}), with y as in
+ * wkv_forward and r [B][T][C] the receptance: the time-mixing block passes the WKV result
+ * through a sigmoid gate of r ("RWKV解读：在Transformer的时代的新RNN", section 二.3: R is
+ * sigmoid-activated, a forgetting mechanism, formula (9); "RWKV についての調査記録", section
+ * "コードを見ながらRWKVの構造を把握": wkv is computed, then gated by sigma). y itself is
+ * not written. The workspace is as for wkv_forward and serves wkv_backward_gated (or
+ * wkv_backward) the same way. out must not overlap any input. */
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, const float *r, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device scratch that wkv_backward and wkv_backward_gated need. With have_fwd_workspace != 0 the caller
  * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
  * window states are recomputed into this workspace, which then also covers
  * wkv_forward_workspace_size(B, T, C). */
@@ -108,6 +119,15 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
                  const float *k, const float *v, const float *dy, const void *fwd_workspace,
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* Backward of the gated forward, L = sum dout * sigma(r) * y: as wkv_backward with the
+ * cotangent dy = dout * sigma(r) formed on the fly, plus dr [B][T][C] =
+ * dout * sigma(r) * (1 - sigma(r)) * y (y recomputed, never read). `fwd_workspace` is NULL
+ * or the workspace wkv_forward_gated (or wkv_forward) filled for the same inputs. */
+int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *r, const float *dout,
+                       const void *fwd_workspace, float *dk, float *dv, float *dr, float *dw,
+                       float *du, void *workspace, size_t workspace_bytes, void *stream);
 
 /* One decode step for B sequences (the recursive form; "RWKV についての調査記録",
  * section "RWKVとは？"). k, v, y are [B][C]; the state is three [B][C] arrays a, b, p

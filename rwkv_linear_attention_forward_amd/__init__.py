@@ -9,6 +9,8 @@ Entry points mirror the C ABI in include/rwkv_wkv.h:
 
     forward(w, u, k, v, workspace=None) -> y
     forward_state(w, u, k, v, a, b, p, workspace=None) -> y   (a, b, p: state in, state out)
+    forward_gated(w, u, k, v, r, workspace=None) -> sigma(r) * y
+    backward_gated(w, u, k, v, r, dout, fwd_workspace=None) -> (dk, dv, dr, dw, du)
     forward_workspace(B, T, C, device) -> uint8 tensor sized for the forward
     backward(w, u, k, v, dy, fwd_workspace=None) -> (dk, dv, dw, du)
     decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
@@ -34,8 +36,8 @@ WKV_ERR_HIP = 3
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
-           "wkv_forward", "wkv_forward_state", "wkv_backward_workspace_size", "wkv_backward",
-           "wkv_decode_step")
+           "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_backward_workspace_size",
+           "wkv_backward", "wkv_backward_gated", "wkv_decode_step")
 
 _lib = None
 _I64 = ctypes.c_int64
@@ -61,6 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
     lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_forward_gated.restype = ctypes.c_int
+    lib.wkv_forward_gated.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]
+    lib.wkv_backward_gated.restype = ctypes.c_int
+    lib.wkv_backward_gated.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_forward_state.restype = ctypes.c_int
     lib.wkv_forward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
@@ -214,6 +222,57 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
                             _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
                             _ptr(workspace), workspace.numel(), _stream(dev)))
     return dk, dv, dw, du
+
+
+def forward_gated(w, u, k, v, r, workspace=None, out=None):
+    """sigma(r) * WKV(w, u, k, v) [B,T,C], the receptance-gated output (y is not written)."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    _need(r, "r", 3, dev)
+    if r.shape != k.shape:
+        raise ValueError("r has the wrong shape")
+    o = torch.empty_like(k) if out is None else out
+    _need(o, "out", 3, dev)
+    if o.shape != k.shape:
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = forward_workspace(B, T, C, dev)
+    _check_ws(workspace, dev, "workspace")
+    _check(load_library().wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                            _ptr(r), _ptr(o), _ptr(workspace),
+                                            workspace.numel(), _stream(dev)))
+    return o
+
+
+def backward_gated(w, u, k, v, r, dout, fwd_workspace=None, workspace=None, out=None):
+    """(dk, dv, dr, dw, du) of sum(dout * sigma(r) * y). `fwd_workspace` as for backward();
+    `out` may hold preallocated (dk, dv, dr, dw, du)."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    for t, n in ((r, "r"), (dout, "dout")):
+        _need(t, n, 3, dev)
+        if t.shape != k.shape:
+            raise ValueError("%s has the wrong shape" % n)
+    if fwd_workspace is not None:
+        _check_ws(fwd_workspace, dev, "fwd_workspace")
+    wsz = backward_workspace_size(B, T, C, fwd_workspace is not None)
+    if workspace is None or workspace.numel() < wsz:
+        workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
+    _check_ws(workspace, dev, "workspace")
+    if out is None:
+        dk, dv, dr = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+        dw, du = torch.empty_like(w), torch.empty_like(u)
+    else:
+        dk, dv, dr, dw, du = out
+        for t, n, ref in ((dk, "dk", k), (dv, "dv", k), (dr, "dr", k), (dw, "dw", w),
+                          (du, "du", u)):
+            _need(t, n, ref.dim(), dev)
+            if t.shape != ref.shape:
+                raise ValueError("%s has the wrong shape" % n)
+    _check(load_library().wkv_backward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                             _ptr(r), _ptr(dout), _ptr(fwd_workspace),
+                                             _ptr(dk), _ptr(dv), _ptr(dr), _ptr(dw), _ptr(du),
+                                             _ptr(workspace), workspace.numel(),
+                                             _stream(dev)))
+    return dk, dv, dr, dw, du
 
 
 def decode_step(w, u, k, v, a, b, p, out=None):

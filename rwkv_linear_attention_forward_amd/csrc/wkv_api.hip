@@ -274,11 +274,12 @@ size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C) {
 
 namespace {
 
-// wkv_forward and wkv_forward_state: sa, sb, sp are the state arrays of the latter (all
-// three non-null) or null for the former.
+// wkv_forward, wkv_forward_state and wkv_forward_gated: sa, sb, sp are the state arrays of
+// the second (all three non-null) or null, r the gate of the third or null.
 int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w,
-                 const float *u, const float *k, const float *v, float *y, float *sa,
-                 float *sb, float *sp, void *workspace, size_t workspace_bytes, void *stream) {
+                 const float *u, const float *k, const float *v, const float *r, float *y,
+                 float *sa, float *sb, float *sp, void *workspace, size_t workspace_bytes,
+                 void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
@@ -296,8 +297,13 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
     if (overlap(y, nb, k, nb) || overlap(y, nb, v, nb) || overlap(y, nb, w, C * 4u) ||
-        overlap(y, nb, u, C * 4u))
-        return fail(WKV_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
+        overlap(y, nb, u, C * 4u) || (r != nullptr && overlap(y, nb, r, nb)))
+        return fail(WKV_ERR_INVALID_ARG, "%s: %s overlaps an input", fn, r ? "out" : "y");
+    if (r != nullptr) {
+        if (!aligned(r, 4, "r", fn)) return WKV_ERR_INVALID_ARG;
+        if (overlap(workspace, need, r, nb))
+            return fail(WKV_ERR_INVALID_ARG, "%s: workspace overlaps r", fn);
+    }
     if (overlap(workspace, need, y, nb) || overlap(workspace, need, k, nb) ||
         overlap(workspace, need, v, nb) || overlap(workspace, need, w, C * 4u) ||
         overlap(workspace, need, u, C * 4u))
@@ -321,7 +327,7 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w
     }
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
-    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, y, sa, sb, sp,
+    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, r, y, sa, sb, sp,
                                           fwd_layout(B, T, C, workspace), next_epoch(),
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
@@ -335,8 +341,8 @@ extern "C" {
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                 const float *k, const float *v, float *y, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    return forward_call("wkv_forward", B, T, C, w, u, k, v, y, nullptr, nullptr, nullptr,
-                        workspace, workspace_bytes, stream);
+    return forward_call("wkv_forward", B, T, C, w, u, k, v, nullptr, y, nullptr, nullptr,
+                        nullptr, workspace, workspace_bytes, stream);
 }
 
 int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -348,8 +354,20 @@ int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const flo
         if (!nonnull(a, "a", fn) || !nonnull(b, "b", fn) || !nonnull(p, "p", fn))
             return WKV_ERR_INVALID_ARG;
     }
-    return forward_call(fn, B, T, C, w, u, k, v, y, a, b, p, workspace, workspace_bytes,
-                        stream);
+    return forward_call(fn, B, T, C, w, u, k, v, nullptr, y, a, b, p, workspace,
+                        workspace_bytes, stream);
+}
+
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, const float *r, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_forward_gated";
+    if (B > 0 && T > 0 && C > 0) {
+        g_err[0] = '\0';
+        if (!nonnull(r, "r", fn)) return WKV_ERR_INVALID_ARG;
+    }
+    return forward_call(fn, B, T, C, w, u, k, v, r, out, nullptr, nullptr, nullptr, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace) {
@@ -360,11 +378,16 @@ size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd
     return ws;
 }
 
-int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
-                 float *dk, float *dv, float *dw, float *du, void *workspace,
-                 size_t workspace_bytes, void *stream) {
-    static const char *fn = "wkv_backward";
+}  // extern "C"
+
+namespace {
+
+// wkv_backward and wkv_backward_gated: r and dr are the gate and its gradient of the latter
+// (both non-null) or null for the former.
+int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w,
+                  const float *u, const float *k, const float *v, const float *dy,
+                  const float *r, const void *fwd_workspace, float *dk, float *dv, float *dr,
+                  float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (C == 0) return WKV_OK;
@@ -379,12 +402,14 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
         return WKV_OK;
     }
     if (!bwd_grid_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
-    const void *ptrs[9] = {w, u, k, v, dy, dk, dv, workspace, nullptr};
-    const char *names[9] = {"w", "u", "k", "v", "dy", "dk", "dv", "workspace", ""};
-    for (int i = 0; i < 8; ++i)
+    const bool gated = r != nullptr || dr != nullptr;
+    const char *gname = gated ? "dout" : "dy";
+    const void *ptrs[10] = {w, u, k, v, dy, dk, dv, workspace, r, dr};
+    const char *names[10] = {"w", "u", "k", "v", gname, "dk", "dv", "workspace", "r", "dr"};
+    for (int i = 0; i < (gated ? 10 : 8); ++i)
         if (!nonnull(ptrs[i], names[i], fn)) return WKV_ERR_INVALID_ARG;
-    for (int i = 0; i < 7; ++i)
-        if (!aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
+    for (int i = 0; i < (gated ? 10 : 8); ++i)
+        if (i != 7 && !aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
     if (!aligned(workspace, 16, "workspace", fn)) return WKV_ERR_INVALID_ARG;
     if (fwd_workspace != nullptr && !aligned(fwd_workspace, 16, "fwd_workspace", fn))
         return WKV_ERR_INVALID_ARG;
@@ -393,15 +418,16 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
     const size_t nb = (size_t)(B * T * C) * 4u, nc = (size_t)C * 4u;
-    const void *outs[5] = {dk, dv, dw, du, workspace};
-    const size_t osz[5] = {nb, nb, nc, nc, need};
-    const void *ins[6] = {w, u, k, v, dy, fwd_workspace};
-    const size_t isz[6] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0};
-    for (int i = 0; i < 5; ++i) {
-        for (int j = 0; j < 6; ++j)
+    const void *outs[6] = {dk, dv, dw, du, workspace, dr};
+    const size_t osz[6] = {nb, nb, nc, nc, need, dr ? nb : 0};
+    const void *ins[7] = {w, u, k, v, dy, fwd_workspace, r};
+    const size_t isz[7] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0,
+                           r ? nb : 0};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 7; ++j)
             if (overlap(outs[i], osz[i], ins[j], isz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
-        for (int j = i + 1; j < 5; ++j)
+        for (int j = i + 1; j < 6; ++j)
             if (overlap(outs[i], osz[i], outs[j], osz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
     }
@@ -415,13 +441,38 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
     } else {
         F = fwd_layout(B, T, C, own + bwd_own_bytes(B, T, C));
         hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, nullptr, nullptr,
-                                              nullptr, F, next_epoch(), st);
+                                              nullptr, nullptr, F, next_epoch(), st);
         if (e != hipSuccess) return fail_hip(e, fn);
     }
-    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, F, dk, dv, dw, du,
+    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, r, F, dk, dv, dr, dw, du,
                                            bwd_layout(B, T, C, own), next_epoch(), st);
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
+                 float *dk, float *dv, float *dw, float *du, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    return backward_call("wkv_backward", B, T, C, w, u, k, v, dy, nullptr, fwd_workspace, dk,
+                         dv, nullptr, dw, du, workspace, workspace_bytes, stream);
+}
+
+int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *r, const float *dout,
+                       const void *fwd_workspace, float *dk, float *dv, float *dr, float *dw,
+                       float *du, void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_backward_gated";
+    if (B > 0 && T > 0 && C > 0) {
+        g_err[0] = '\0';
+        if (!nonnull(r, "r", fn) || !nonnull(dr, "dr", fn)) return WKV_ERR_INVALID_ARG;
+    }
+    return backward_call(fn, B, T, C, w, u, k, v, dout, r, fwd_workspace, dk, dv, dr, dw, du,
+                         workspace, workspace_bytes, stream);
 }
 
 int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,

@@ -100,7 +100,9 @@ __device__ __forceinline__ RevCarry get_rrec(const double *p, int64_t n, int64_t
 // private arrays), so that this rare path holds few registers wherever it is inlined. `fin` is the forward carry
 // entering the chunk, `rin` the future sums at the chunk's nominal end (CH tokens on).
 // The forward sweep adds the chunk's dw, du terms if FG; the reverse sweep stores dk, dv
-// if OUT. Returns the future sums at the chunk start.
+// if OUT. With `r` the cotangent is gated (dy = dout sigma(r), dout read from `dy`), and
+// with `dr` the forward sweep also stores dr = dout sigma(r) (1 - sigma(r)) y. Returns the
+// future sums at the chunk start.
 // ---------------------------------------------------------------------------------
 struct RevState64 {  // (G, H) = (g, h) e^{r - ref}
     double g, h, r;
@@ -111,7 +113,8 @@ __device__ __forceinline__ RevCarry exact_chunk(
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
     float *__restrict__ dk, float *__restrict__ dv, int64_t row0, int64_t t0, int Lv,
     int64_t C, int cl, bool st_ok, float ref, const Carry &fin, RevCarry rin, float uc,
-    float wc, double &du_acc, double &dw_acc) {
+    float wc, double &du_acc, double &dw_acc, const float *__restrict__ r = nullptr,
+    float *__restrict__ dr = nullptr) {
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;  // the frame 2^{ref2} the carries refer to
     // the carries are relative to 2^{ref2}; the per-token path works relative to e^{ref}
@@ -128,7 +131,13 @@ __device__ __forceinline__ RevCarry exact_chunk(
         const double e1 = exp(st.p - m), e2 = exp(uk - m);
         const double rden = 1.0 / fma(e1, st.b, e2);
         const double yv = fma(e1, st.a, e2 * vv) * rden;
-        const double sg = (double)dy[i] * rden;  // dy / D in units of e^{-(m + ref)}
+        double g = (double)dy[i];
+        if (r != nullptr) {
+            const double sr = sigmoid64(r[i]);
+            g *= sr;  // the gated cotangent, in fp64 (dw, du cancel too much for fp32)
+            if (FG && dr != nullptr) dr[i] = (float)(g * (1.0 - sr) * yv);
+        }
+        const double sg = g * rden;  // dy / D in units of e^{-(m + ref)}
         if (FG) {
             // s (A' - y B') and s e^{u+k} (v - y), with A' = a' e^{p+ref}
             dw_acc = fma(sg * e1, fma(-yv, st.bp, st.ap), dw_acc);
@@ -198,10 +207,11 @@ struct BwdConst {
 // wave; the chunk then takes the per-token path). helper_summary repeats the summary
 // arithmetic op for op, so a helper publishes the bits the owner would (every fused
 // multiply-add is written out; the build does not contract).
-template <int CH>
+template <int CH, bool GATE>
 __device__ __forceinline__ RevCarry chunk_pass(
     int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
-    int cl, int voff, int stride,
+    int cl, bool cval, int voff, int stride, const float *__restrict__ rgate,
+    float *__restrict__ dr,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
     const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
     float2 (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
@@ -210,6 +220,8 @@ __device__ __forceinline__ RevCarry chunk_pass(
     Lv = chunk_len(t0, T, CH);
     load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
     load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
+    float rr[GATE ? CH : 1];  // r, then dr (gc holds dout)
+    if constexpr (GATE) load_chunk1<CH>(rr, rgate, row0, t0, T, C, voff);
     ref = chunk_ref<CH>(kc, Lv);
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
@@ -248,7 +260,14 @@ __device__ __forceinline__ RevCarry chunk_pass(
             dmin = (j < Lv) ? fmin(dmin, den) : dmin;
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
-            const double sg = (double)gc[j] * r;
+            double gd = (double)gc[j];
+            if constexpr (GATE) {
+                // the gated cotangent dout sigma(r) in fp64, and dr = dout sigma (1 - sigma) y
+                const double sr = sigmoid64(rr[j]);
+                gd *= sr;
+                rr[j] = (float)(gd * (1.0 - sr) * yv);
+            }
+            const double sg = gd * r;
             const double sgy = sg * yv;
             // dw term s (A' - y B') / d and du term s e^{k} (v - y), both in the frame; the
             // common factors d and e^u are applied after the loop
@@ -268,11 +287,22 @@ __device__ __forceinline__ RevCarry chunk_pass(
         du_acc *= K.eu;
         fx = wave_any(!(dmin >= (double)kTinyDen));
     }
-    if (!fx) return RevCarry{R, Q, -ref2};
+    if (!fx) {
+        if constexpr (GATE) {
+            if (dr != nullptr && cval) {
+                const rsrc_t rdr = make_rsrc(dr + (row0 + t0) * C);
+#pragma unroll
+                for (int j = 0; j < CH; ++j)
+                    if (j < Lv) bstore(rdr, rr[j], voff, j * stride);
+            }
+        }
+        return RevCarry{R, Q, -ref2};
+    }
     du_acc = 0.0;
     dw_acc = 0.0;
     return exact_chunk<CH, false, true>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
-                                       ref, fin, rev_zero(), K.uc, (float)K.w, du_acc, dw_acc);
+                                       ref, fin, rev_zero(), K.uc, (float)K.w, du_acc, dw_acc,
+                                       GATE ? rgate : nullptr, GATE && cval ? dr : nullptr);
 }
 
 // Reverse summary of another unit's chunk, for the look-back's recomputation of a window
@@ -284,7 +314,8 @@ template <int CH>
 __device__ __forceinline__ RevCarry helper_summary(
     int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
     int cl, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ dy, const BwdConst &K) {
+    const float *__restrict__ v, const float *__restrict__ dy, const float *__restrict__ rg,
+    const BwdConst &K) {
     const int64_t t0 = ci * CH;
     const int Lv = chunk_len(t0, T, CH);
     if (Lv == 0) return rev_zero();
@@ -316,7 +347,9 @@ __device__ __forceinline__ RevCarry helper_summary(
             dmin = in ? fmin(dmin, den) : dmin;
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
-            const double sg = (in ? (double)gp[(int64_t)j * C] : 0.0) * r;
+            double g = in ? (double)gp[(int64_t)j * C] : 0.0;
+            if (rg != nullptr) g *= sigmoid64(in ? rg[(row0 + t0 + j) * C + cl] : 0.0f);
+            const double sg = g * r;
             const double sgy = sg * yv;
             R = fma(pw, sg, R);
             Q = fma(pw, sgy, Q);
@@ -329,7 +362,7 @@ __device__ __forceinline__ RevCarry helper_summary(
     }
     double du, dw;
     return exact_chunk<CH, false, false>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
-                                         ref, fin, rev_zero(), K.uc, (float)K.w, du, dw);
+                                         ref, fin, rev_zero(), K.uc, (float)K.w, du, dw, rg);
 }
 
 // Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
@@ -353,13 +386,16 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const Rev
     }
 }
 
-template <int NW, int CH>
+// GATE: the output was sigma(r) * y; `dy` holds the cotangent of that gated output, and dr
+// is written too.
+template <int NW, int CH, bool GATE>
 __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg,
     uint64_t epoch, const float *__restrict__ w, const float *__restrict__ u,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
-    const FwdCarries F, float *__restrict__ dk,
-    float *__restrict__ dv, float *__restrict__ dw, float *__restrict__ du,
+    const float *__restrict__ r, const FwdCarries F, float *__restrict__ dk,
+    float *__restrict__ dv, float *__restrict__ dr, float *__restrict__ dw,
+    float *__restrict__ du,
     uint64_t *__restrict__ flags, double *__restrict__ ragg, double *__restrict__ rincl,
     double *__restrict__ part) {
     constexpr int WIN = NW * CH;
@@ -395,9 +431,9 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     float ref;
     int Lv;
     double du_acc, dw_acc;
-    RevCarry rsum = chunk_pass<CH>(ci, T, C, F, bidx, row0, cl, voff, stride,
-                                         k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref, Lv,
-                                         du_acc, dw_acc);
+    RevCarry rsum = chunk_pass<CH, GATE>(ci, T, C, F, bidx, row0, cl, cval, voff, stride, r,
+                                         dr, k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref,
+                                         Lv, du_acc, dw_acc);
     // the dw, du terms are staged with the reverse summaries (the fold's barrier covers both)
     sh.pu[q][lane] = du_acc;
     sh.pw[q][lane] = dw_acc;
@@ -450,8 +486,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: recompute window j's reverse aggregate here and
                 // publish it (bitwise what unit j itself publishes)
-                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, F,
-                                                         bidx, row0, cl, k, v, dy, K);
+                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, F, bidx, row0, cl,
+                                                         k, v, dy, GATE ? r : nullptr, K);
                 RevCarry agg_j, lf_j;
                 window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
                 if (q == 0) {
@@ -515,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
         const Carry fin = chunk_carry(F, bidx, ci, C, cl);
         double d0 = 0.0, d1 = 0.0;
         exact_chunk<CH, true, false>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
-                                     K.uc, wc, d0, d1);
+                                     K.uc, wc, d0, d1, GATE ? r : nullptr);
     }
 }
 
@@ -579,16 +615,23 @@ __global__ __launch_bounds__(256) void wkv_zero2_kernel(float *__restrict__ a,
 }
 
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const FwdLayout &F,
-                           float *dk, float *dv, float *dw, float *du, const BwdLayout &L,
-                           uint64_t epoch, hipStream_t stream) {
+                           const float *k, const float *v, const float *dy, const float *r,
+                           const FwdLayout &F, float *dk, float *dv, float *dr, float *dw,
+                           float *du, const BwdLayout &L, uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     const FwdCarries fc{F.incl, F.cin, F.init, B * F.nseg * C, F.nseg};
-    hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk>), dim3((unsigned)units),
-                       dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp, nbg, L.nseg, epoch, w, u,
-                       k, v, dy, fc, dk, dv, dw, du, L.flags, L.ragg, L.rincl, L.part);
+    if (r != nullptr)
+        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, true>),
+                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, k, v, dy, r, fc, dk, dv, dr, dw, du,
+                           L.flags, L.ragg, L.rincl, L.part);
+    else
+        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, false>),
+                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, k, v, dy, r, fc, dk, dv, dr, dw, du,
+                           L.flags, L.ragg, L.rincl, L.part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),

@@ -43,6 +43,8 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float expn(float x) { return ex2(x * kLog2e); }
 __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
+// The logistic gate 1 / (1 + e^{-x}) in fp32 (0 and 1 at the extremes, no NaN).
+__device__ __forceinline__ float sigmoidf_(float x) { return rcpf(1.0f + ex2(-x * kLog2e)); }
 
 // ---- raw buffer access: per-lane byte offset in a VGPR, per-row offset in an SGPR ----
 using rsrc_t = __amdgpu_buffer_rsrc_t;
@@ -132,6 +134,12 @@ __device__ __forceinline__ void normalize(Carry &c) {
 __device__ __forceinline__ double rcpd(double x) {
     const double r0 = (double)rcpf((float)x);
     return fma(r0, fma(-x, r0, 1.0), r0);
+}
+
+// The logistic gate in fp64, 1 / (1 + 2^{-x log2 e}) (exp2_64 and rcpd; the argument is
+// capped so that a very negative x gives 0 rather than inf/inf).
+__device__ __forceinline__ double sigmoid64(float x) {
+    return rcpd(1.0 + exp2_64(fmin(-(double)x * kLog2eD, 200.0)));
 }
 
 // ---------------------------------------------------------------------------------

@@ -41,23 +41,35 @@
 
 namespace wkvdev {
 
-// Outputs of one lane's chunk by the per-token rescaled recursion (Rs, fp32), from the
-// carry entering the chunk; for chunks whose fixed frame would under- or overflow. Reads
-// k, v straight from memory in a loop that is not unrolled: few registers.
+// Outputs of one lane's chunk by the per-token rescaled recursion, in fp64 with library
+// exponentials, from the carry entering the chunk; for chunks whose fixed frame would under-
+// or overflow (keys hundreds apart, extreme u). fp64 throughout: with a key of 1000 setting
+// the frame, k - ref alone would carry 6e-5 of fp32 rounding into every weight. Reads k, v
+// (and r) straight from memory in a loop that is not unrolled: few registers.
 template <int CH>
 __device__ __forceinline__ void exact_outputs(const float *__restrict__ k,
-                                           const float *__restrict__ v, float *__restrict__ y,
+                                           const float *__restrict__ v,
+                                           const float *__restrict__ r, float *__restrict__ y,
                                            int64_t row0, int64_t t0, int Lv, int64_t C, int cl,
-                                           float ref, const Carry &mine, float uc,
-                                           const Decay &dc) {
-    const double ref2 = (double)ref * kLog2eD;
-    Rs st{(float)mine.a, (float)mine.b, (float)((mine.P - ref2) * kLn2D)};
+                                           float ref, const Carry &mine, float uc, double w) {
+    const double refd = (double)ref, u = (double)uc;
+    // A = a e^{p + ref}, B = b e^{p + ref}
+    double a = mine.a, b = mine.b, p = (mine.P - refd * kLog2eD) * kLn2D;
 #pragma unroll 1
     for (int j = 0; j < Lv; ++j) {
         const int64_t i = (row0 + t0 + j) * C + cl;
-        const float kr = k[i] - ref, vv = v[i];
-        y[i] = rs_out(st, kr, vv, uc);
-        rs_push(st, kr, vv, dc);
+        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double uk = u + kr;
+        const double m = fmax(p, uk);
+        const double e1 = exp(p - m), e2 = exp(uk - m);
+        const float o = (float)(fma(e1, a, e2 * vv) / fma(e1, b, e2));
+        y[i] = r != nullptr ? o * sigmoidf_(r[i]) : o;
+        const double pw = p - w;
+        const double m2 = fmax(pw, kr);
+        const double f1 = exp(pw - m2), f2 = exp(kr - m2);
+        a = fma(f1, a, f2 * vv);
+        b = fma(f1, b, f2);
+        p = m2;
     }
 }
 
@@ -196,11 +208,13 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
     return X;
 }
 
-template <int NW, int CH>
+// GATE: the output is sigma(r) * y (r [B][T][C]) instead of y.
+template <int NW, int CH, bool GATE>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
     const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
-    const float *__restrict__ v, float *__restrict__ y, uint64_t *__restrict__ flags,
+    const float *__restrict__ v, const float *__restrict__ r, float *__restrict__ y,
+    uint64_t *__restrict__ flags,
     double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
     const float *__restrict__ sa, const float *__restrict__ sb, const float *__restrict__ sp,
     double *__restrict__ init, float *__restrict__ fin) {
@@ -355,6 +369,10 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
 
     // ---- phase 3: outputs ----
     const double ref2 = (double)ref * kLog2eD;
+    float rc[GATE ? CH : 1];  // r of the chunk, loaded while the sweep runs
+    if constexpr (GATE) {
+        if (!exact) load_chunk1<CH>(rc, r, row0, t0, T, C, voff);
+    }
     if (!exact) {
         const double gap = mine.P - ref2;
         bool bad = gap > (double)kCarryGap;
@@ -375,15 +393,21 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     }
     if (q == 0) put_flag(myflag, epoch, kInclusive);
     if (exact) {
-        if (cval) exact_outputs<CH>(k, v, y, row0, t0, Lv, C, cl, ref, mine, uc, dc);
+        if (cval)
+            exact_outputs<CH>(k, v, GATE ? r : nullptr, y, row0, t0, Lv, C, cl, ref, mine, uc, wd);
         return;
     }
     if (cval) {
         const rsrc_t ry = make_rsrc(y + (row0 + t0) * C);
         const int stride = (int)(C * 4);
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
-            if (j < Lv) bstore(ry, kc[j], voff, j * stride);
+        for (int j = 0; j < CH; ++j) {
+            if (j < Lv) {
+                float o = kc[j];
+                if constexpr (GATE) o *= sigmoidf_(rc[j]);
+                bstore(ry, o, voff, j * stride);
+            }
+        }
     }
 }
 
@@ -401,15 +425,23 @@ __global__ __launch_bounds__(256) void wkv_state_out_kernel(const float *__restr
 }
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, float *sa, float *sb,
-                          float *sp, const FwdLayout &L, uint64_t epoch, hipStream_t stream) {
+                          const float *k, const float *v, const float *r, float *y, float *sa,
+                          float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
+                          hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
-    hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk>), dim3((unsigned)units),
-                       dim3(kFwdWaves * 64), 0, stream, T, C, ngrp, nbg, L.nseg, epoch, w, u,
-                       k, v, y, L.flags, L.agg, L.incl, B * L.nseg * C, L.cin, sa, sb, sp,
-                       L.init, sa != nullptr ? L.fin : nullptr);
+    float *fin = sa != nullptr ? L.fin : nullptr;
+    if (r != nullptr)
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true>),
+                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, k, v, r, y, L.flags, L.agg, L.incl,
+                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+    else
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false>),
+                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, k, v, r, y, L.flags, L.agg, L.incl,
+                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sa == nullptr) return e;
     const int64_t n = B * C;

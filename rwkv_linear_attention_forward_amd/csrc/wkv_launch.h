@@ -82,15 +82,18 @@ hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out);
 // convention (A = a e^p, B = b e^p); when given, they are overwritten with the state after
 // token T-1 (through L.fin, by a second kernel, so that no workgroup can read a state that
 // another has already replaced). Without them the scan starts from the empty state.
+// `r` ([B][T][C]) or null: with it the output is sigma(r) * y, the receptance gate.
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, float *y, float *sa, float *sb,
-                          float *sp, const FwdLayout &L, uint64_t epoch, hipStream_t stream);
+                          const float *k, const float *v, const float *r, float *y, float *sa,
+                          float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
+                          hipStream_t stream);
 
 // `F` is the forward workspace filled for the same inputs (its chunk carries are read).
+// With `r` (and `dr`) the forward output was sigma(r) * y and `dy` is its cotangent.
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const FwdLayout &F,
-                           float *dk, float *dv, float *dw, float *du, const BwdLayout &L,
-                           uint64_t epoch, hipStream_t stream);
+                           const float *k, const float *v, const float *dy, const float *r,
+                           const FwdLayout &F, float *dk, float *dv, float *dr, float *dw,
+                           float *du, const BwdLayout &L, uint64_t epoch, hipStream_t stream);
 
 // dw = du = 0 over C channels (backward of an empty batch or sequence).
 hipError_t launch_zero2(float *dw, float *du, int64_t C, hipStream_t stream);
