@@ -7,7 +7,7 @@ distributions of the 3B-class layer workload in wkv_inputs.py) and resident in H
 before timing starts; the step reuses preallocated outputs and workspaces.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-state]
-                    [--no-gated]
+                    [--no-gated] [--no-bf16]
 
 prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
 `roofline` describes the kernel that takes most of the step, with its algorithmic bytes
@@ -19,7 +19,9 @@ reported only while the kernel sources still hash to the value recorded there.
 threads) on the same workload. `decode` reports the batched decode step separately
 (B=256, C=5120, 40 layer states, 36 B per element per call); `forward_state` the forward
 from a given state that also returns the final state (prompt prefill), on the same layer;
-`gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer.
+`gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer; `bf16`
+the step with the [B, T, C] tensors stored as bfloat16 (reported apart: the benchmark's own
+workload is fp32).
 
 The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
 load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
@@ -322,6 +324,50 @@ def bench_gated(wkv, torch, dev, x, steps=100, warmup=100):
             "steps": steps, "outputs_finite": ok}
 
 
+def bench_bf16(wkv, torch, dev, x, steps=100, warmup=100):
+    """The step with k, v, dy, y, dk, dv stored as bfloat16 (state and arithmetic as in fp32),
+    back to back: forward 6 B and backward 10 B per element."""
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v", "dy")}
+    for n in ("k", "v", "dy"):
+        t[n] = t[n].to(torch.bfloat16)
+    B, T, C = t["k"].shape
+    fws = wkv.forward_workspace(B, T, C, dev)
+    bws = torch.empty(max(16, wkv.backward_workspace_size(B, T, C, True)), dtype=torch.uint8,
+                      device=dev)
+    y = torch.empty_like(t["k"])
+    outs = (torch.empty_like(t["k"]), torch.empty_like(t["k"]), torch.empty_like(t["w"]),
+            torch.empty_like(t["u"]))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wkv.forward(t["w"], t["u"], t["k"], t["v"], workspace=fws, out=y)
+        if ev is not None:
+            ev[1].record()
+        wkv.backward(t["w"], t["u"], t["k"], t["v"], t["dy"], fwd_workspace=fws, workspace=bws,
+                     out=outs)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize(dev)
+    f_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    b_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    n = B * T * C
+    ok = all(bool(torch.isfinite(a).all()) for a in (y,) + outs)
+    return {"workload": "bfloat16 k, v, dy, y, dk, dv, B=%d T=%d C=%d" % (B, T, C),
+            "forward_us": f_us, "backward_us": b_us,
+            "elem_per_s": n / ((f_us + b_us) * 1e-6),
+            "forward_frac_of_peak": 6 * n / (f_us * 1e-6) / 1e9 / PEAK_GBPS,
+            "backward_frac_of_peak": 10 * n / (b_us * 1e-6) / 1e9 / PEAK_GBPS,
+            "steps": steps, "outputs_finite": ok}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +379,7 @@ def main(argv=None):
                     help="skip the forward-from-a-state measurement")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the receptance-gated measurement")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bfloat16 measurement")
     ap.add_argument("--with-copy", action="store_true",
                     help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -398,6 +445,8 @@ def main(argv=None):
         out["forward_state"] = bench_forward_state(wkv, torch, dev, x)
     if not args.no_gated:
         out["gated"] = bench_gated(wkv, torch, dev, x)
+    if not args.no_bf16:
+        out["bf16"] = bench_bf16(wkv, torch, dev, x)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)
     else:

@@ -46,6 +46,11 @@ extern "C" {
 #define WKV_ERR_UNSUPPORTED 2 /* the current device is not gfx950 */
 #define WKV_ERR_HIP 3         /* a HIP runtime call or kernel launch failed */
 
+/* Storage formats of the [B][T][C] tensors for the *_typed entry points. */
+#define WKV_F32 0  /* IEEE binary32 */
+#define WKV_BF16 1 /* bfloat16: the upper half of a binary32 */
+#define WKV_F16 2  /* IEEE binary16 */
+
 /* Library version, as 10000*major + 100*minor + patch. */
 int wkv_version(void);
 
@@ -101,6 +106,15 @@ int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const flo
                       const float *k, const float *v, const float *r, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* wkv_forward (r == NULL) or wkv_forward_gated (r != NULL) with k, v, r and y/out in the
+ * storage format `dtype` (WKV_F32, WKV_BF16 or WKV_F16); w and u stay fp32. Values are
+ * widened to fp32 on load; every sum, carry and state is kept in fp32/fp64 as in the fp32
+ * entry points, and only the outputs are rounded to the format (to nearest even). 16-bit
+ * tensors must be 2-byte aligned. The workspace is the same as wkv_forward's. */
+int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                      const float *u, const void *k, const void *v, const void *r, void *y,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device scratch that wkv_backward and wkv_backward_gated need. With have_fwd_workspace != 0 the caller
  * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
  * window states are recomputed into this workspace, which then also covers
@@ -128,6 +142,16 @@ int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const fl
                        const float *k, const float *v, const float *r, const float *dout,
                        const void *fwd_workspace, float *dk, float *dv, float *dr, float *dw,
                        float *du, void *workspace, size_t workspace_bytes, void *stream);
+
+/* wkv_backward (r == dr == NULL; dy is the cotangent of y) or wkv_backward_gated (r, dr
+ * given; dy is the cotangent of the gated output) with k, v, dy, r, dk, dv, dr in the
+ * storage format `dtype`; w, u, dw, du stay fp32. Arithmetic as in the fp32 entry points;
+ * dk, dv, dr are rounded to the format on store. */
+int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                       const float *u, const void *k, const void *v, const void *dy,
+                       const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,
+                       float *dw, float *du, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* One decode step for B sequences (the recursive form; "RWKV についての調査記録",
  * section "RWKVとは？"). k, v, y are [B][C]; the state is three [B][C] arrays a, b, p

@@ -36,8 +36,13 @@ WKV_ERR_HIP = 3
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
-           "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_backward_workspace_size",
-           "wkv_backward", "wkv_backward_gated", "wkv_decode_step")
+           "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
+           "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
+           "wkv_backward_typed", "wkv_decode_step")
+
+# Storage formats of the [B, T, C] tensors (dtype codes of the *_typed entry points).
+WKV_F32, WKV_BF16, WKV_F16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: WKV_F32, torch.bfloat16: WKV_BF16, torch.float16: WKV_F16}
 
 _lib = None
 _I64 = ctypes.c_int64
@@ -63,6 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
     lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_forward_typed.restype = ctypes.c_int
+    lib.wkv_forward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]
+    lib.wkv_backward_typed.restype = ctypes.c_int
+    lib.wkv_backward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_forward_gated.restype = ctypes.c_int
     lib.wkv_forward_gated.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
@@ -108,11 +119,11 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, ndim, device=None):
+def _need(t, name, ndim, device=None, dtype=torch.float32):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype != torch.float32:
-        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_cuda:
         raise ValueError("%s must be on a GPU device" % name)
     if device is not None and t.device != device:
@@ -123,10 +134,16 @@ def _need(t, name, ndim, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _check_btc(w, u, k, v):
-    _need(k, "k", 3)
+def _check_btc(w, u, k, v, typed=False):
+    """Shapes and devices of the operands. With typed=True the [B, T, C] tensors may be
+    float32, bfloat16 or float16 (all the same); w and u are always float32."""
+    if not isinstance(k, torch.Tensor):
+        raise TypeError("k must be a torch.Tensor")
+    if typed and k.dtype not in _DTYPE_CODE:
+        raise TypeError("k must be float32, bfloat16 or float16, got %s" % k.dtype)
+    _need(k, "k", 3, dtype=k.dtype if typed else torch.float32)
     dev = k.device
-    _need(v, "v", 3, dev)
+    _need(v, "v", 3, dev, dtype=k.dtype)
     _need(w, "w", 1, dev)
     _need(u, "u", 1, dev)
     B, T, C = k.shape
@@ -153,20 +170,40 @@ def _check_ws(ws, dev, name):
         raise ValueError("%s must be a contiguous uint8 tensor on %s" % (name, dev))
 
 
-def forward(w, u, k, v, workspace=None, out=None):
-    """y [B,T,C] = WKV(w, u, k, v). `workspace` (uint8, forward_workspace_size bytes) is
-    allocated if not given; after the call it holds the states backward() can reuse."""
-    B, T, C, dev = _check_btc(w, u, k, v)
+def _forward_common(w, u, k, v, r, workspace, out):
+    B, T, C, dev = _check_btc(w, u, k, v, typed=True)
+    if r is not None:
+        _need(r, "r", 3, dev, dtype=k.dtype)
+        if r.shape != k.shape:
+            raise ValueError("r has the wrong shape")
     y = torch.empty_like(k) if out is None else out
-    _need(y, "out", 3, dev)
+    _need(y, "out", 3, dev, dtype=k.dtype)
     if y.shape != k.shape:
         raise ValueError("out has the wrong shape")
     if workspace is None:
         workspace = forward_workspace(B, T, C, dev)
     _check_ws(workspace, dev, "workspace")
-    _check(load_library().wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                      _ptr(workspace), workspace.numel(), _stream(dev)))
+    lib = load_library()
+    if k.dtype == torch.float32:
+        if r is None:
+            rc = lib.wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
+        else:
+            rc = lib.wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                       _ptr(y), _ptr(workspace), workspace.numel(), _stream(dev))
+    else:
+        rc = lib.wkv_forward_typed(_DTYPE_CODE[k.dtype], B, T, C, _ptr(w), _ptr(u), _ptr(k),
+                                   _ptr(v), _ptr(r), _ptr(y), _ptr(workspace), workspace.numel(),
+                                   _stream(dev))
+    _check(rc)
     return y
+
+
+def forward(w, u, k, v, workspace=None, out=None):
+    """y [B,T,C] = WKV(w, u, k, v). k, v (and y) are float32, bfloat16 or float16 (all the
+    same; w, u float32). `workspace` (uint8, forward_workspace_size bytes) is allocated if not
+    given; after the call it holds the states backward() can reuse."""
+    return _forward_common(w, u, k, v, None, workspace, out)
 
 
 def forward_state(w, u, k, v, a, b, p, workspace=None, out=None):
@@ -194,61 +231,11 @@ def backward_workspace_size(B: int, T: int, C: int, have_fwd_workspace: bool) ->
     return int(load_library().wkv_backward_workspace_size(B, T, C, 1 if have_fwd_workspace else 0))
 
 
-def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
-    """(dk, dv, dw, du) of sum(dy * y). `fwd_workspace` is the workspace forward() filled for
-    the same inputs (optional: without it the window states are recomputed). `out` may hold
-    preallocated (dk, dv, dw, du)."""
-    B, T, C, dev = _check_btc(w, u, k, v)
-    _need(dy, "dy", 3, dev)
-    if dy.shape != k.shape:
-        raise ValueError("dy has the wrong shape")
-    if fwd_workspace is not None:
-        _check_ws(fwd_workspace, dev, "fwd_workspace")
-    lib = load_library()
-    wsz = backward_workspace_size(B, T, C, fwd_workspace is not None)
-    if workspace is None or workspace.numel() < wsz:
-        workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
-    _check_ws(workspace, dev, "workspace")
-    if out is None:
-        dk, dv, dw, du = torch.empty_like(k), torch.empty_like(k), torch.empty_like(w), \
-            torch.empty_like(u)
-    else:
-        dk, dv, dw, du = out
-        for t, n, ref in ((dk, "dk", k), (dv, "dv", k), (dw, "dw", w), (du, "du", u)):
-            _need(t, n, ref.dim(), dev)
-            if t.shape != ref.shape:
-                raise ValueError("%s has the wrong shape" % n)
-    _check(lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
-                            _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
-                            _ptr(workspace), workspace.numel(), _stream(dev)))
-    return dk, dv, dw, du
-
-
-def forward_gated(w, u, k, v, r, workspace=None, out=None):
-    """sigma(r) * WKV(w, u, k, v) [B,T,C], the receptance-gated output (y is not written)."""
-    B, T, C, dev = _check_btc(w, u, k, v)
-    _need(r, "r", 3, dev)
-    if r.shape != k.shape:
-        raise ValueError("r has the wrong shape")
-    o = torch.empty_like(k) if out is None else out
-    _need(o, "out", 3, dev)
-    if o.shape != k.shape:
-        raise ValueError("out has the wrong shape")
-    if workspace is None:
-        workspace = forward_workspace(B, T, C, dev)
-    _check_ws(workspace, dev, "workspace")
-    _check(load_library().wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
-                                            _ptr(r), _ptr(o), _ptr(workspace),
-                                            workspace.numel(), _stream(dev)))
-    return o
-
-
-def backward_gated(w, u, k, v, r, dout, fwd_workspace=None, workspace=None, out=None):
-    """(dk, dv, dr, dw, du) of sum(dout * sigma(r) * y). `fwd_workspace` as for backward();
-    `out` may hold preallocated (dk, dv, dr, dw, du)."""
-    B, T, C, dev = _check_btc(w, u, k, v)
-    for t, n in ((r, "r"), (dout, "dout")):
-        _need(t, n, 3, dev)
+def _backward_common(w, u, k, v, dy, r, fwd_workspace, workspace, out):
+    B, T, C, dev = _check_btc(w, u, k, v, typed=True)
+    gated = r is not None
+    for t, n in ((dy, "dout" if gated else "dy"),) + (((r, "r"),) if gated else ()):
+        _need(t, n, 3, dev, dtype=k.dtype)
         if t.shape != k.shape:
             raise ValueError("%s has the wrong shape" % n)
     if fwd_workspace is not None:
@@ -257,22 +244,58 @@ def backward_gated(w, u, k, v, r, dout, fwd_workspace=None, workspace=None, out=
     if workspace is None or workspace.numel() < wsz:
         workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
     _check_ws(workspace, dev, "workspace")
+    names = ("dk", "dv") + (("dr",) if gated else ()) + ("dw", "du")
+    refs = (k, k) + ((k,) if gated else ()) + (w, u)
     if out is None:
-        dk, dv, dr = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
-        dw, du = torch.empty_like(w), torch.empty_like(u)
+        grads = tuple(torch.empty_like(ref) for ref in refs)
     else:
-        dk, dv, dr, dw, du = out
-        for t, n, ref in ((dk, "dk", k), (dv, "dv", k), (dr, "dr", k), (dw, "dw", w),
-                          (du, "du", u)):
-            _need(t, n, ref.dim(), dev)
+        grads = tuple(out)
+        if len(grads) != len(names):
+            raise ValueError("out must hold %d tensors" % len(names))
+        for t, n, ref in zip(grads, names, refs):
+            _need(t, n, ref.dim(), dev, dtype=ref.dtype)
             if t.shape != ref.shape:
                 raise ValueError("%s has the wrong shape" % n)
-    _check(load_library().wkv_backward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
-                                             _ptr(r), _ptr(dout), _ptr(fwd_workspace),
-                                             _ptr(dk), _ptr(dv), _ptr(dr), _ptr(dw), _ptr(du),
-                                             _ptr(workspace), workspace.numel(),
-                                             _stream(dev)))
-    return dk, dv, dr, dw, du
+    dk, dv = grads[0], grads[1]
+    dr = grads[2] if gated else None
+    dw, du = grads[-2], grads[-1]
+    lib = load_library()
+    if k.dtype == torch.float32 and not gated:
+        rc = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                              _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
+                              _ptr(workspace), workspace.numel(), _stream(dev))
+    elif k.dtype == torch.float32:
+        rc = lib.wkv_backward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                    _ptr(dy), _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dr),
+                                    _ptr(dw), _ptr(du), _ptr(workspace), workspace.numel(),
+                                    _stream(dev))
+    else:
+        rc = lib.wkv_backward_typed(_DTYPE_CODE[k.dtype], B, T, C, _ptr(w), _ptr(u), _ptr(k),
+                                    _ptr(v), _ptr(dy), _ptr(r), _ptr(fwd_workspace), _ptr(dk),
+                                    _ptr(dv), _ptr(dr), _ptr(dw), _ptr(du), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
+    _check(rc)
+    return grads
+
+
+def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
+    """(dk, dv, dw, du) of sum(dy * y). `fwd_workspace` is the workspace forward() filled for
+    the same inputs (optional: without it the window states are recomputed). `out` may hold
+    preallocated (dk, dv, dw, du). k, v, dy (and dk, dv) share one of float32, bfloat16,
+    float16; w, u, dw, du are float32."""
+    return _backward_common(w, u, k, v, dy, None, fwd_workspace, workspace, out)
+
+
+def forward_gated(w, u, k, v, r, workspace=None, out=None):
+    """sigma(r) * WKV(w, u, k, v) [B,T,C], the receptance-gated output (y is not written).
+    Formats as for forward()."""
+    return _forward_common(w, u, k, v, r, workspace, out)
+
+
+def backward_gated(w, u, k, v, r, dout, fwd_workspace=None, workspace=None, out=None):
+    """(dk, dv, dr, dw, du) of sum(dout * sigma(r) * y). `fwd_workspace` as for backward();
+    `out` may hold preallocated (dk, dv, dr, dw, du). Formats as for backward()."""
+    return _backward_common(w, u, k, v, dout, r, fwd_workspace, workspace, out)
 
 
 def decode_step(w, u, k, v, a, b, p, out=None):

@@ -188,6 +188,16 @@ uint64_t next_epoch() {
     return (g_epoch.fetch_add(1) + 1) & ((uint64_t(1) << 61) - 1);
 }
 
+// The storage format of a dtype code (WKV_F32, WKV_BF16, WKV_F16).
+bool io_of(int dtype, const char *fn, wkvdev::Io *out) {
+    switch (dtype) {
+    case WKV_F32: *out = wkvdev::Io::F32; return true;
+    case WKV_BF16: *out = wkvdev::Io::BF16; return true;
+    case WKV_F16: *out = wkvdev::Io::F16; return true;
+    default: fail(WKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype); return false;
+    }
+}
+
 bool grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
     const int64_t units = B * ((C + 63) / 64) * nseg_of(T);
     if (units > INT32_MAX) {
@@ -276,10 +286,10 @@ namespace {
 
 // wkv_forward, wkv_forward_state and wkv_forward_gated: sa, sb, sp are the state arrays of
 // the second (all three non-null) or null, r the gate of the third or null.
-int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w,
-                 const float *u, const float *k, const float *v, const float *r, float *y,
-                 float *sa, float *sb, float *sp, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt,
+                 const float *w, const float *u, const void *k, const void *v, const void *r,
+                 void *y, float *sa, float *sb, float *sp, void *workspace,
+                 size_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
@@ -287,11 +297,12 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w
     if (!nonnull(w, "w", fn) || !nonnull(u, "u", fn) || !nonnull(k, "k", fn) ||
         !nonnull(v, "v", fn) || !nonnull(y, "y", fn) || !nonnull(workspace, "workspace", fn))
         return WKV_ERR_INVALID_ARG;
-    if (!aligned(w, 4, "w", fn) || !aligned(u, 4, "u", fn) || !aligned(k, 4, "k", fn) ||
-        !aligned(v, 4, "v", fn) || !aligned(y, 4, "y", fn) ||
+    const size_t es = fmt == wkvdev::Io::F32 ? 4u : 2u;
+    if (!aligned(w, 4, "w", fn) || !aligned(u, 4, "u", fn) || !aligned(k, es, "k", fn) ||
+        !aligned(v, es, "v", fn) || !aligned(y, es, r ? "out" : "y", fn) ||
         !aligned(workspace, 16, "workspace", fn))
         return WKV_ERR_INVALID_ARG;
-    const size_t nb = (size_t)(B * T * C) * 4u;
+    const size_t nb = (size_t)(B * T * C) * es;
     const size_t need = fwd_ws_bytes(B, T, C);
     if (workspace_bytes < need)
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
@@ -300,7 +311,7 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w
         overlap(y, nb, u, C * 4u) || (r != nullptr && overlap(y, nb, r, nb)))
         return fail(WKV_ERR_INVALID_ARG, "%s: %s overlaps an input", fn, r ? "out" : "y");
     if (r != nullptr) {
-        if (!aligned(r, 4, "r", fn)) return WKV_ERR_INVALID_ARG;
+        if (!aligned(r, es, "r", fn)) return WKV_ERR_INVALID_ARG;
         if (overlap(workspace, need, r, nb))
             return fail(WKV_ERR_INVALID_ARG, "%s: workspace overlaps r", fn);
     }
@@ -327,7 +338,7 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w
     }
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
-    hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, r, y, sa, sb, sp,
+    hipError_t e = wkvdev::launch_forward(B, T, C, fmt, w, u, k, v, r, y, sa, sb, sp,
                                           fwd_layout(B, T, C, workspace), next_epoch(),
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
@@ -341,8 +352,8 @@ extern "C" {
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                 const float *k, const float *v, float *y, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    return forward_call("wkv_forward", B, T, C, w, u, k, v, nullptr, y, nullptr, nullptr,
-                        nullptr, workspace, workspace_bytes, stream);
+    return forward_call("wkv_forward", B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y,
+                        nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -354,8 +365,8 @@ int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const flo
         if (!nonnull(a, "a", fn) || !nonnull(b, "b", fn) || !nonnull(p, "p", fn))
             return WKV_ERR_INVALID_ARG;
     }
-    return forward_call(fn, B, T, C, w, u, k, v, nullptr, y, a, b, p, workspace,
-                        workspace_bytes, stream);
+    return forward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, a, b, p,
+                        workspace, workspace_bytes, stream);
 }
 
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -366,8 +377,18 @@ int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const flo
         g_err[0] = '\0';
         if (!nonnull(r, "r", fn)) return WKV_ERR_INVALID_ARG;
     }
-    return forward_call(fn, B, T, C, w, u, k, v, r, out, nullptr, nullptr, nullptr, workspace,
-                        workspace_bytes, stream);
+    return forward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, r, out, nullptr, nullptr,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                      const float *u, const void *k, const void *v, const void *r, void *y,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_forward_typed";
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    return forward_call(fn, B, T, C, fmt, w, u, k, v, r, y, nullptr, nullptr, nullptr,
+                        workspace, workspace_bytes, stream);
 }
 
 size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace) {
@@ -384,9 +405,9 @@ namespace {
 
 // wkv_backward and wkv_backward_gated: r and dr are the gate and its gradient of the latter
 // (both non-null) or null for the former.
-int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *w,
-                  const float *u, const float *k, const float *v, const float *dy,
-                  const float *r, const void *fwd_workspace, float *dk, float *dv, float *dr,
+int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt,
+                  const float *w, const float *u, const void *k, const void *v, const void *dy,
+                  const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,
                   float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
@@ -408,8 +429,10 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *
     const char *names[10] = {"w", "u", "k", "v", gname, "dk", "dv", "workspace", "r", "dr"};
     for (int i = 0; i < (gated ? 10 : 8); ++i)
         if (!nonnull(ptrs[i], names[i], fn)) return WKV_ERR_INVALID_ARG;
+    const size_t es = fmt == wkvdev::Io::F32 ? 4u : 2u;
     for (int i = 0; i < (gated ? 10 : 8); ++i)
-        if (i != 7 && !aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
+        if (i != 7 && !aligned(ptrs[i], i < 2 ? 4u : es, names[i], fn))
+            return WKV_ERR_INVALID_ARG;
     if (!aligned(workspace, 16, "workspace", fn)) return WKV_ERR_INVALID_ARG;
     if (fwd_workspace != nullptr && !aligned(fwd_workspace, 16, "fwd_workspace", fn))
         return WKV_ERR_INVALID_ARG;
@@ -417,7 +440,7 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *
     if (workspace_bytes < need)
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
-    const size_t nb = (size_t)(B * T * C) * 4u, nc = (size_t)C * 4u;
+    const size_t nb = (size_t)(B * T * C) * es, nc = (size_t)C * 4u;
     const void *outs[6] = {dk, dv, dw, du, workspace, dr};
     const size_t osz[6] = {nb, nb, nc, nc, need, dr ? nb : 0};
     const void *ins[7] = {w, u, k, v, dy, fwd_workspace, r};
@@ -440,12 +463,12 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, const float *
         F = fwd_layout(B, T, C, const_cast<void *>(fwd_workspace));
     } else {
         F = fwd_layout(B, T, C, own + bwd_own_bytes(B, T, C));
-        hipError_t e = wkvdev::launch_forward(B, T, C, w, u, k, v, nullptr, nullptr, nullptr,
-                                              nullptr, nullptr, F, next_epoch(), st);
+        hipError_t e = wkvdev::launch_forward(B, T, C, fmt, w, u, k, v, nullptr, nullptr,
+                                              nullptr, nullptr, nullptr, F, next_epoch(), st);
         if (e != hipSuccess) return fail_hip(e, fn);
     }
-    hipError_t e = wkvdev::launch_backward(B, T, C, w, u, k, v, dy, r, F, dk, dv, dr, dw, du,
-                                           bwd_layout(B, T, C, own), next_epoch(), st);
+    hipError_t e = wkvdev::launch_backward(B, T, C, fmt, w, u, k, v, dy, r, F, dk, dv, dr, dw,
+                                           du, bwd_layout(B, T, C, own), next_epoch(), st);
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
 }
@@ -458,8 +481,9 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
                  const float *k, const float *v, const float *dy, const void *fwd_workspace,
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream) {
-    return backward_call("wkv_backward", B, T, C, w, u, k, v, dy, nullptr, fwd_workspace, dk,
-                         dv, nullptr, dw, du, workspace, workspace_bytes, stream);
+    return backward_call("wkv_backward", B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr,
+                         fwd_workspace, dk, dv, nullptr, dw, du, workspace, workspace_bytes,
+                         stream);
 }
 
 int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -471,7 +495,21 @@ int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const fl
         g_err[0] = '\0';
         if (!nonnull(r, "r", fn) || !nonnull(dr, "dr", fn)) return WKV_ERR_INVALID_ARG;
     }
-    return backward_call(fn, B, T, C, w, u, k, v, dout, r, fwd_workspace, dk, dv, dr, dw, du,
+    return backward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, dout, r, fwd_workspace, dk,
+                         dv, dr, dw, du, workspace, workspace_bytes, stream);
+}
+
+int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                       const float *u, const void *k, const void *v, const void *dy,
+                       const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,
+                       float *dw, float *du, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    static const char *fn = "wkv_backward_typed";
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    if ((r == nullptr) != (dr == nullptr) && B > 0 && T > 0 && C > 0)
+        return fail(WKV_ERR_INVALID_ARG, "%s: r and dr must be given together", fn);
+    return backward_call(fn, B, T, C, fmt, w, u, k, v, dy, r, fwd_workspace, dk, dv, dr, dw, du,
                          workspace, workspace_bytes, stream);
 }
 

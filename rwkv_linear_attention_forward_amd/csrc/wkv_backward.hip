@@ -108,13 +108,14 @@ struct RevState64 {  // (G, H) = (g, h) e^{r - ref}
     double g, h, r;
 };
 
-template <int CH, bool OUT, bool FG>
+template <int CH, bool OUT, bool FG, Io IO>
 __device__ __forceinline__ RevCarry exact_chunk(
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
-    float *__restrict__ dk, float *__restrict__ dv, int64_t row0, int64_t t0, int Lv,
+    const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
+    const io_t<IO> *__restrict__ dy, io_t<IO> *__restrict__ dk, io_t<IO> *__restrict__ dv,
+    int64_t row0, int64_t t0, int Lv,
     int64_t C, int cl, bool st_ok, float ref, const Carry &fin, RevCarry rin, float uc,
-    float wc, double &du_acc, double &dw_acc, const float *__restrict__ r = nullptr,
-    float *__restrict__ dr = nullptr) {
+    float wc, double &du_acc, double &dw_acc, const io_t<IO> *__restrict__ r = nullptr,
+    io_t<IO> *__restrict__ dr = nullptr) {
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;  // the frame 2^{ref2} the carries refer to
     // the carries are relative to 2^{ref2}; the per-token path works relative to e^{ref}
@@ -125,17 +126,17 @@ __device__ __forceinline__ RevCarry exact_chunk(
 #pragma unroll 1
     for (int j = 0; j < Lv; ++j) {
         const int64_t i = (row0 + t0 + j) * C + cl;
-        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double kr = (double)io_ld<IO>(k, i) - refd, vv = (double)io_ld<IO>(v, i);
         const double uk = u + kr;
         const double m = fmax(st.p, uk);
         const double e1 = exp(st.p - m), e2 = exp(uk - m);
         const double rden = 1.0 / fma(e1, st.b, e2);
         const double yv = fma(e1, st.a, e2 * vv) * rden;
-        double g = (double)dy[i];
+        double g = (double)io_ld<IO>(dy, i);
         if (r != nullptr) {
-            const double sr = sigmoid64(r[i]);
+            const double sr = sigmoid64(io_ld<IO>(r, i));
             g *= sr;  // the gated cotangent, in fp64 (dw, du cancel too much for fp32)
-            if (FG && dr != nullptr) dr[i] = (float)(g * (1.0 - sr) * yv);
+            if (FG && dr != nullptr) io_st<IO>(dr, i, (float)(g * (1.0 - sr) * yv));
         }
         const double sg = g * rden;  // dy / D in units of e^{-(m + ref)}
         if (FG) {
@@ -154,14 +155,14 @@ __device__ __forceinline__ RevCarry exact_chunk(
 #pragma unroll 1
     for (int j = Lv - 1; j >= 0; --j) {
         const int64_t i = (row0 + t0 + j) * C + cl;
-        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double kr = (double)io_ld<IO>(k, i) - refd, vv = (double)io_ld<IO>(v, i);
         const double yy = ys[j], sg = ss[j], M = ms[j];
         if (OUT) {
             const double ekr = exp(kr + rs.r);
             const double cpi = sg * exp(u + kr - M);
             if (st_ok) {
-                dv[i] = (float)fma(ekr, rs.g, cpi);
-                dk[i] = (float)fma(cpi, vv - yy, ekr * fma(vv, rs.g, -rs.h));
+                io_st<IO>(dv, i, (float)fma(ekr, rs.g, cpi));
+                io_st<IO>(dk, i, (float)fma(cpi, vv - yy, ekr * fma(vv, rs.g, -rs.h)));
             }
         }
         const double a = rs.r - w, b = -M;
@@ -207,21 +208,21 @@ struct BwdConst {
 // wave; the chunk then takes the per-token path). helper_summary repeats the summary
 // arithmetic op for op, so a helper publishes the bits the owner would (every fused
 // multiply-add is written out; the build does not contract).
-template <int CH, bool GATE>
+template <int CH, bool GATE, Io IO>
 __device__ __forceinline__ RevCarry chunk_pass(
     int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
-    int cl, bool cval, int voff, int stride, const float *__restrict__ rgate,
-    float *__restrict__ dr,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
+    int cl, bool cval, int voff, int stride, const io_t<IO> *__restrict__ rgate,
+    io_t<IO> *__restrict__ dr, const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
+    const io_t<IO> *__restrict__ dy,
     const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
     float2 (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
     double &dw_acc) {
     const int64_t t0 = ci * CH;
     Lv = chunk_len(t0, T, CH);
-    load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
-    load_chunk1<CH>(gc, dy, row0, t0, T, C, voff);
+    load_chunk<CH, IO>(kc, vc, k, v, row0, t0, T, C, voff);
+    load_chunk1<CH, IO>(gc, dy, row0, t0, T, C, voff);
     float rr[GATE ? CH : 1];  // r, then dr (gc holds dout)
-    if constexpr (GATE) load_chunk1<CH>(rr, rgate, row0, t0, T, C, voff);
+    if constexpr (GATE) load_chunk1<CH, IO>(rr, rgate, row0, t0, T, C, voff);
     ref = chunk_ref<CH>(kc, Lv);
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
@@ -293,14 +294,14 @@ __device__ __forceinline__ RevCarry chunk_pass(
                 const rsrc_t rdr = make_rsrc(dr + (row0 + t0) * C);
 #pragma unroll
                 for (int j = 0; j < CH; ++j)
-                    if (j < Lv) bstore(rdr, rr[j], voff, j * stride);
+                    if (j < Lv) bstore_io<IO>(rdr, rr[j], voff, j * stride);
             }
         }
         return RevCarry{R, Q, -ref2};
     }
     du_acc = 0.0;
     dw_acc = 0.0;
-    return exact_chunk<CH, false, true>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
+    return exact_chunk<CH, false, true, IO>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
                                        ref, fin, rev_zero(), K.uc, (float)K.w, du_acc, dw_acc,
                                        GATE ? rgate : nullptr, GATE && cval ? dr : nullptr);
 }
@@ -310,21 +311,21 @@ __device__ __forceinline__ RevCarry chunk_pass(
 // for op and in the same order (so the bits are those the owner publishes), but streaming
 // k, v, dy from memory in a loop that is not unrolled, so that the unit's own chunk stays
 // in registers across the look-back.
-template <int CH>
+template <int CH, Io IO>
 __device__ __forceinline__ RevCarry helper_summary(
     int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
-    int cl, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ dy, const float *__restrict__ rg,
+    int cl, const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
+    const io_t<IO> *__restrict__ dy, const io_t<IO> *__restrict__ rg,
     const BwdConst &K) {
     const int64_t t0 = ci * CH;
     const int Lv = chunk_len(t0, T, CH);
     if (Lv == 0) return rev_zero();
-    const float *kp = k + (row0 + t0) * C + cl;
-    const float *vp = v + (row0 + t0) * C + cl;
-    const float *gp = dy + (row0 + t0) * C + cl;
+    const io_t<IO> *kp = k + (row0 + t0) * C + cl;
+    const io_t<IO> *vp = v + (row0 + t0) * C + cl;
+    const io_t<IO> *gp = dy + (row0 + t0) * C + cl;
     float ref = kNegBig;
 #pragma unroll 1
-    for (int j = 0; j < Lv; ++j) ref = fmaxf(ref, kp[(int64_t)j * C]);
+    for (int j = 0; j < Lv; ++j) ref = fmaxf(ref, io_ld<IO>(kp, (int64_t)j * C));
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
     const Carry fin = chunk_carry(F, bidx, ci, C, cl);
@@ -338,17 +339,17 @@ __device__ __forceinline__ RevCarry helper_summary(
 #pragma unroll 1
         for (int j = 0; j < CH; ++j) {
             const bool in = j < Lv;
-            const float kj = in ? kp[(int64_t)j * C] : -__builtin_inff();
+            const float kj = in ? io_ld<IO>(kp, (int64_t)j * C) : -__builtin_inff();
             const double e = exp2_64(fma((double)kj, kLog2eD, -ref2));
-            const double vv = in ? (double)vp[(int64_t)j * C] : 0.0;
+            const double vv = in ? (double)io_ld<IO>(vp, (int64_t)j * C) : 0.0;
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
             dmin = in ? fmin(dmin, den) : dmin;
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
-            double g = in ? (double)gp[(int64_t)j * C] : 0.0;
-            if (rg != nullptr) g *= sigmoid64(in ? rg[(row0 + t0 + j) * C + cl] : 0.0f);
+            double g = in ? (double)io_ld<IO>(gp, (int64_t)j * C) : 0.0;
+            if (rg != nullptr) g *= sigmoid64(in ? io_ld<IO>(rg, (row0 + t0 + j) * C + cl) : 0.0f);
             const double sg = g * r;
             const double sgy = sg * yv;
             R = fma(pw, sg, R);
@@ -361,8 +362,9 @@ __device__ __forceinline__ RevCarry helper_summary(
         if (!fx) return RevCarry{R, Q, -ref2};
     }
     double du, dw;
-    return exact_chunk<CH, false, false>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
-                                         ref, fin, rev_zero(), K.uc, (float)K.w, du, dw, rg);
+    return exact_chunk<CH, false, false, IO>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl,
+                                             false, ref, fin, rev_zero(), K.uc, (float)K.w, du,
+                                             dw, rg);
 }
 
 // Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
@@ -387,14 +389,15 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const Rev
 }
 
 // GATE: the output was sigma(r) * y; `dy` holds the cotangent of that gated output, and dr
-// is written too.
-template <int NW, int CH, bool GATE>
+// is written too. IO: the storage format of k, v, dy, r, dk, dv and dr.
+template <int NW, int CH, bool GATE, Io IO>
 __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg,
     uint64_t epoch, const float *__restrict__ w, const float *__restrict__ u,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dy,
-    const float *__restrict__ r, const FwdCarries F, float *__restrict__ dk,
-    float *__restrict__ dv, float *__restrict__ dr, float *__restrict__ dw,
+    const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
+    const io_t<IO> *__restrict__ dy, const io_t<IO> *__restrict__ r, const FwdCarries F,
+    io_t<IO> *__restrict__ dk, io_t<IO> *__restrict__ dv, io_t<IO> *__restrict__ dr,
+    float *__restrict__ dw,
     float *__restrict__ du,
     uint64_t *__restrict__ flags, double *__restrict__ ragg, double *__restrict__ rincl,
     double *__restrict__ part) {
@@ -411,8 +414,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     const int64_t c = (int64_t)grp * 64 + lane;
     const bool cval = c < C;
     const int cl = (int)(cval ? c : C - 1);
-    const int voff = cl * 4;
-    const int stride = (int)(C * 4);
+    const int voff = cl * kIoBytes<IO>;
+    const int stride = (int)(C * kIoBytes<IO>);
 
     const float wc = w[cl];
     BwdConst K;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     float ref;
     int Lv;
     double du_acc, dw_acc;
-    RevCarry rsum = chunk_pass<CH, GATE>(ci, T, C, F, bidx, row0, cl, cval, voff, stride, r,
+    RevCarry rsum = chunk_pass<CH, GATE, IO>(ci, T, C, F, bidx, row0, cl, cval, voff, stride, r,
                                          dr, k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref,
                                          Lv, du_acc, dw_acc);
     // the dw, du terms are staged with the reverse summaries (the fold's barrier covers both)
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             if (st != (int)kAggregate) {
                 // not published in time: recompute window j's reverse aggregate here and
                 // publish it (bitwise what unit j itself publishes)
-                const RevCarry rs_j = helper_summary<CH>(j * NW + q, T, C, F, bidx, row0, cl,
+                const RevCarry rs_j = helper_summary<CH, IO>(j * NW + q, T, C, F, bidx, row0, cl,
                                                          k, v, dy, GATE ? r : nullptr, K);
                 RevCarry agg_j, lf_j;
                 window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
@@ -543,14 +546,14 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             if (j < Lv && cval) {
-                bstore(rdv, kc[j], voff, j * stride);
-                bstore(rdk, vc[j], voff, j * stride);
+                bstore_io<IO>(rdv, kc[j], voff, j * stride);
+                bstore_io<IO>(rdk, vc[j], voff, j * stride);
             }
         }
     } else {
         const Carry fin = chunk_carry(F, bidx, ci, C, cl);
         double d0 = 0.0, d1 = 0.0;
-        exact_chunk<CH, true, false>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
+        exact_chunk<CH, true, false, IO>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
                                      K.uc, wc, d0, d1, GATE ? r : nullptr);
     }
 }
@@ -614,24 +617,47 @@ __global__ __launch_bounds__(256) void wkv_zero2_kernel(float *__restrict__ a,
     }
 }
 
-hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const float *r,
-                           const FwdLayout &F, float *dk, float *dv, float *dr, float *dw,
-                           float *du, const BwdLayout &L, uint64_t epoch, hipStream_t stream) {
+template <Io IO>
+static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int64_t T,
+                               int64_t C, int ngrp, int64_t nbg, const BwdLayout &L,
+                               uint64_t epoch, const float *w, const float *u, const void *k,
+                               const void *v, const void *dy, const void *r,
+                               const FwdCarries &fc, void *dk, void *dv, void *dr, float *dw,
+                               float *du) {
+    using E = io_t<IO>;
+    const E *kk = static_cast<const E *>(k), *vv = static_cast<const E *>(v),
+            *gg = static_cast<const E *>(dy), *rr = static_cast<const E *>(r);
+    E *ddk = static_cast<E *>(dk), *ddv = static_cast<E *>(dv), *ddr = static_cast<E *>(dr);
+    if (r != nullptr)
+        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, true, IO>),
+                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, kk, vv, gg, rr, fc, ddk, ddv, ddr, dw, du,
+                           L.flags, L.ragg, L.rincl, L.part);
+    else
+        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, false, IO>),
+                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, kk, vv, gg, rr, fc, ddk, ddv, ddr, dw, du,
+                           L.flags, L.ragg, L.rincl, L.part);
+}
+
+hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
+                           const float *u, const void *k, const void *v, const void *dy,
+                           const void *r, const FwdLayout &F, void *dk, void *dv, void *dr,
+                           float *dw, float *du, const BwdLayout &L, uint64_t epoch,
+                           hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     const FwdCarries fc{F.incl, F.cin, F.init, B * F.nseg * C, F.nseg};
-    if (r != nullptr)
-        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, true>),
-                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, k, v, dy, r, fc, dk, dv, dr, dw, du,
-                           L.flags, L.ragg, L.rincl, L.part);
+    if (fmt == Io::BF16)
+        launch_backward_io<Io::BF16>(units, stream, B, T, C, ngrp, nbg, L, epoch, w, u, k, v, dy,
+                                     r, fc, dk, dv, dr, dw, du);
+    else if (fmt == Io::F16)
+        launch_backward_io<Io::F16>(units, stream, B, T, C, ngrp, nbg, L, epoch, w, u, k, v, dy,
+                                    r, fc, dk, dv, dr, dw, du);
     else
-        hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, false>),
-                           dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, k, v, dy, r, fc, dk, dv, dr, dw, du,
-                           L.flags, L.ragg, L.rincl, L.part);
+        launch_backward_io<Io::F32>(units, stream, B, T, C, ngrp, nbg, L, epoch, w, u, k, v, dy,
+                                    r, fc, dk, dv, dr, dw, du);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),

@@ -12,10 +12,10 @@ namespace wkvdev {
 // padding: k = -inf (weight e^{k - ref} = 0 in every frame), v = 0. The loads carry no
 // branches (a padded token re-reads the last valid row), so the unrolled chunk stays in
 // straight-line code.
-template <int CH>
+template <int CH, Io F = Io::F32>
 __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
-                                           const float *__restrict__ k,
-                                           const float *__restrict__ v, int64_t row0,
+                                           const io_t<F> *__restrict__ k,
+                                           const io_t<F> *__restrict__ v, int64_t row0,
                                            int64_t t0, int64_t T, int64_t C, int voff) {
     if (t0 >= T) {
 #pragma unroll
@@ -27,13 +27,13 @@ __device__ __forceinline__ void load_chunk(float (&kc)[CH], float (&vc)[CH],
     }
     const rsrc_t rk = make_rsrc(k + (row0 + t0) * C);
     const rsrc_t rv = make_rsrc(v + (row0 + t0) * C);
-    const int stride = (int)(C * 4);
+    const int stride = (int)(C * kIoBytes<F>);
     const int last = (int)(T - t0 < CH ? T - t0 : CH) - 1;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const int soff = (j < last ? j : last) * stride;
-        kc[j] = bload(rk, voff, soff);
-        vc[j] = bload(rv, voff, soff);
+        kc[j] = bload_io<F>(rk, voff, soff);
+        vc[j] = bload_io<F>(rv, voff, soff);
     }
     if (last < CH - 1) {
 #pragma unroll
@@ -86,8 +86,8 @@ __device__ __forceinline__ bool chunk_summary(float (&kc)[CH], const float (&vc)
 }
 
 // Load one tensor's CH-token chunk (tokens past T are 0), branch-free as load_chunk.
-template <int CH>
-__device__ __forceinline__ void load_chunk1(float (&gc)[CH], const float *__restrict__ g,
+template <int CH, Io F = Io::F32>
+__device__ __forceinline__ void load_chunk1(float (&gc)[CH], const io_t<F> *__restrict__ g,
                                             int64_t row0, int64_t t0, int64_t T, int64_t C,
                                             int voff) {
     if (t0 >= T) {
@@ -96,10 +96,10 @@ __device__ __forceinline__ void load_chunk1(float (&gc)[CH], const float *__rest
         return;
     }
     const rsrc_t rg = make_rsrc(g + (row0 + t0) * C);
-    const int stride = (int)(C * 4);
+    const int stride = (int)(C * kIoBytes<F>);
     const int last = (int)(T - t0 < CH ? T - t0 : CH) - 1;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) gc[j] = bload(rg, voff, (j < last ? j : last) * stride);
+    for (int j = 0; j < CH; ++j) gc[j] = bload_io<F>(rg, voff, (j < last ? j : last) * stride);
     if (last < CH - 1) {
 #pragma unroll
         for (int j = 1; j < CH; ++j)
@@ -144,9 +144,9 @@ __device__ __forceinline__ void rs64_skip(Rs64 &s, double w) {
 // Chunk summary in the per-token form (fp64), same meaning as chunk_summary's, for the
 // rare chunks the fixed frame cannot take. Reads k, v straight from memory in a loop that
 // is not unrolled: few registers wherever it is inlined.
-template <int CH>
-__device__ __forceinline__ Carry exact_summary(const float *__restrict__ k,
-                                            const float *__restrict__ v, int64_t row0,
+template <int CH, Io F = Io::F32>
+__device__ __forceinline__ Carry exact_summary(const io_t<F> *__restrict__ k,
+                                            const io_t<F> *__restrict__ v, int64_t row0,
                                             int64_t t0, int Lv, int64_t C, int cl, float ref,
                                             double w) {
     const double refd = (double)ref;
@@ -155,7 +155,7 @@ __device__ __forceinline__ Carry exact_summary(const float *__restrict__ k,
     for (int j = 0; j < CH; ++j) {
         if (j < Lv) {
             const int64_t i = (row0 + t0 + j) * C + cl;
-            rs64_push(s, (double)k[i] - refd, (double)v[i], w);
+            rs64_push(s, (double)io_ld<F>(k, i) - refd, (double)io_ld<F>(v, i), w);
         } else {
             rs64_skip(s, w);
         }

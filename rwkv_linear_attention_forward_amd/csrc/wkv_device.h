@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wkv_launch.h"
+
 namespace wkvdev {
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -59,6 +61,59 @@ __device__ __forceinline__ float bload(rsrc_t r, int voff, int soff) {
 }
 __device__ __forceinline__ void bstore(rsrc_t r, float x, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 2);
+}
+
+// ---------------------------------------------------------------------------------
+// Storage formats of the [B][T][C] tensors at the boundary. Whatever the format, values are
+// widened to fp32 on load and all arithmetic (and every carry and state) stays fp32/fp64;
+// outputs are rounded to the format on store (round to nearest even).
+// ---------------------------------------------------------------------------------
+template <Io F> struct IoType;
+template <> struct IoType<Io::F32> { using T = float; };
+template <> struct IoType<Io::BF16> { using T = uint16_t; };
+template <> struct IoType<Io::F16> { using T = uint16_t; };
+template <Io F> using io_t = typename IoType<F>::T;
+template <Io F> constexpr int kIoBytes = F == Io::F32 ? 4 : 2;
+
+template <Io F> __device__ __forceinline__ float io_widen(io_t<F> x) {
+    if constexpr (F == Io::F32) {
+        return x;
+    } else if constexpr (F == Io::BF16) {
+        return __builtin_bit_cast(float, (unsigned)x << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, x);
+    }
+}
+template <Io F> __device__ __forceinline__ io_t<F> io_narrow(float x) {
+    if constexpr (F == Io::F32) {
+        return x;
+    } else if constexpr (F == Io::BF16) {
+        const unsigned u = __builtin_bit_cast(unsigned, x);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
+        return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+}
+// Element i of a tensor in format F, widened (plain load, for the rare per-token paths).
+template <Io F> __device__ __forceinline__ float io_ld(const io_t<F> *p, int64_t i) {
+    return io_widen<F>(p[i]);
+}
+template <Io F> __device__ __forceinline__ void io_st(io_t<F> *p, int64_t i, float x) {
+    p[i] = io_narrow<F>(x);
+}
+// Buffer load/store of one element per lane; voff, soff in bytes.
+template <Io F> __device__ __forceinline__ float bload_io(rsrc_t r, int voff, int soff) {
+    if constexpr (F == Io::F32)
+        return bload(r, voff, soff);
+    else
+        return io_widen<F>((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 2));
+}
+template <Io F> __device__ __forceinline__ void bstore_io(rsrc_t r, float x, int voff, int soff) {
+    if constexpr (F == Io::F32)
+        bstore(r, x, voff, soff);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(io_narrow<F>(x), r, voff, soff, 2);
 }
 
 // ---------------------------------------------------------------------------------

@@ -46,10 +46,10 @@ namespace wkvdev {
 // or overflow (keys hundreds apart, extreme u). fp64 throughout: with a key of 1000 setting
 // the frame, k - ref alone would carry 6e-5 of fp32 rounding into every weight. Reads k, v
 // (and r) straight from memory in a loop that is not unrolled: few registers.
-template <int CH>
-__device__ __forceinline__ void exact_outputs(const float *__restrict__ k,
-                                           const float *__restrict__ v,
-                                           const float *__restrict__ r, float *__restrict__ y,
+template <int CH, Io F>
+__device__ __forceinline__ void exact_outputs(const io_t<F> *__restrict__ k,
+                                           const io_t<F> *__restrict__ v,
+                                           const io_t<F> *__restrict__ r, io_t<F> *__restrict__ y,
                                            int64_t row0, int64_t t0, int Lv, int64_t C, int cl,
                                            float ref, const Carry &mine, float uc, double w) {
     const double refd = (double)ref, u = (double)uc;
@@ -58,12 +58,12 @@ __device__ __forceinline__ void exact_outputs(const float *__restrict__ k,
 #pragma unroll 1
     for (int j = 0; j < Lv; ++j) {
         const int64_t i = (row0 + t0 + j) * C + cl;
-        const double kr = (double)k[i] - refd, vv = (double)v[i];
+        const double kr = (double)io_ld<F>(k, i) - refd, vv = (double)io_ld<F>(v, i);
         const double uk = u + kr;
         const double m = fmax(p, uk);
         const double e1 = exp(p - m), e2 = exp(uk - m);
         const float o = (float)(fma(e1, a, e2 * vv) / fma(e1, b, e2));
-        y[i] = r != nullptr ? o * sigmoidf_(r[i]) : o;
+        io_st<F>(y, i, r != nullptr ? o * sigmoidf_(io_ld<F>(r, i)) : o);
         const double pw = p - w;
         const double m2 = fmax(pw, kr);
         const double f1 = exp(pw - m2), f2 = exp(kr - m2);
@@ -110,9 +110,9 @@ __device__ __forceinline__ void final_state(const float (&ec)[CH], const float (
 
 // The same for a chunk that took the per-token path (its weights are not in registers):
 // the rescaled recursion in fp64 with k and v read again from memory.
-template <int CH>
-__device__ __forceinline__ void final_state_exact(const float *__restrict__ k,
-                                               const float *__restrict__ v, int64_t row0,
+template <int CH, Io F>
+__device__ __forceinline__ void final_state_exact(const io_t<F> *__restrict__ k,
+                                               const io_t<F> *__restrict__ v, int64_t row0,
                                                int64_t t0, int Lv, int64_t C, int cl,
                                                const Carry &mine, double w,
                                                float *__restrict__ fin, int64_t n, int64_t i) {
@@ -120,7 +120,7 @@ __device__ __forceinline__ void final_state_exact(const float *__restrict__ k,
 #pragma unroll 1
     for (int j = 0; j < Lv; ++j) {
         const int64_t x = (row0 + t0 + j) * C + cl;
-        const double kk = (double)k[x], vv = (double)v[x];
+        const double kk = (double)io_ld<F>(k, x), vv = (double)io_ld<F>(v, x);
         const double pw = p - w;
         const double m = fmax(pw, kk);
         const double f1 = exp(pw - m), f2 = exp(kk - m);
@@ -159,33 +159,33 @@ __device__ __forceinline__ Carry staged(const FwdShared<NW> &sh, int q, int lane
 // a loop that is not unrolled, repeating chunk_summary's arithmetic op for op and in the
 // same order (bitwise what unit j computes itself), so the unit's own chunk stays in
 // registers.
-template <int NW, int CH>
+template <int NW, int CH, Io F>
 __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, int q, int lane,
                                                   int64_t T, int64_t C, int64_t row0, int cl,
-                                                  const float *__restrict__ k,
-                                                  const float *__restrict__ v, bool slow_wave,
+                                                  const io_t<F> *__restrict__ k,
+                                                  const io_t<F> *__restrict__ v, bool slow_wave,
                                                   double dwfd, double wd, double cw2) {
     const int64_t tj = j * (NW * CH) + (int64_t)q * CH;
     const int Lj = chunk_len(tj, T, CH);
     Carry sj = carry_empty();
     if (Lj > 0) {
-        const float *kp = k + (row0 + tj) * C + cl;
-        const float *vp = v + (row0 + tj) * C + cl;
+        const io_t<F> *kp = k + (row0 + tj) * C + cl;
+        const io_t<F> *vp = v + (row0 + tj) * C + cl;
         float rj = kNegBig;
 #pragma unroll 1
-        for (int i = 0; i < Lj; ++i) rj = fmaxf(rj, kp[(int64_t)i * C]);
+        for (int i = 0; i < Lj; ++i) rj = fmaxf(rj, io_ld<F>(kp, (int64_t)i * C));
         const double refd = (double)rj;
         sj.P = refd * kLog2eD;
         if (slow_wave) {
-            sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
+            sj = exact_summary<CH, F>(k, v, row0, tj, Lj, C, cl, rj, wd);
         } else {
             double S = 0.0, Z = 0.0, Qs = 0.0, Qz = 0.0;
 #pragma unroll 1
             for (int i = 0; i < CH; ++i) {
                 const bool in = i < Lj;
-                const float ki = in ? kp[(int64_t)i * C] : -__builtin_inff();
+                const float ki = in ? io_ld<F>(kp, (int64_t)i * C) : -__builtin_inff();
                 const double e = exp2_64(fma((double)ki, kLog2eD, -sj.P));
-                const double vi = in ? (double)vp[(int64_t)i * C] : 0.0;
+                const double vi = in ? (double)io_ld<F>(vp, (int64_t)i * C) : 0.0;
                 Qs = fma(Qs, dwfd, S);
                 Qz = fma(Qz, dwfd, Z);
                 S = fma(S, dwfd, e * vi);
@@ -195,7 +195,8 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
             sj.b = Z;
             sj.ap = dwfd * Qs;
             sj.bp = dwfd * Qz;
-            if (wave_any(!(Z >= kTinySum))) sj = exact_summary<CH>(k, v, row0, tj, Lj, C, cl, rj, wd);
+            if (wave_any(!(Z >= kTinySum)))
+                sj = exact_summary<CH, F>(k, v, row0, tj, Lj, C, cl, rj, wd);
         }
     }
     __syncthreads();
@@ -208,12 +209,13 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
     return X;
 }
 
-// GATE: the output is sigma(r) * y (r [B][T][C]) instead of y.
-template <int NW, int CH, bool GATE>
+// GATE: the output is sigma(r) * y (r [B][T][C]) instead of y. F: the storage format of k,
+// v, r and y.
+template <int NW, int CH, bool GATE, Io F>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
-    const float *__restrict__ w, const float *__restrict__ u, const float *__restrict__ k,
-    const float *__restrict__ v, const float *__restrict__ r, float *__restrict__ y,
+    const float *__restrict__ w, const float *__restrict__ u, const io_t<F> *__restrict__ k,
+    const io_t<F> *__restrict__ v, const io_t<F> *__restrict__ r, io_t<F> *__restrict__ y,
     uint64_t *__restrict__ flags,
     double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
     const float *__restrict__ sa, const float *__restrict__ sb, const float *__restrict__ sp,
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const int64_t c = (int64_t)grp * 64 + lane;
     const bool cval = c < C;
     const int cl = (int)(cval ? c : C - 1);
-    const int voff = cl * 4;
+    const int voff = cl * kIoBytes<F>;
 
     const float wc = w[cl];
     const float uc = u[cl];
@@ -248,11 +250,11 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
 
     // ---- phase 1: frame and summary of this wave's chunk ----
     float kc[CH], vc[CH];
-    load_chunk<CH>(kc, vc, k, v, row0, t0, T, C, voff);
+    load_chunk<CH, F>(kc, vc, k, v, row0, t0, T, C, voff);
     const float ref = chunk_ref<CH>(kc, Lv);
     Carry sum;
     bool exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, sum);
-    if (exact) sum = exact_summary<CH>(k, v, row0, t0, Lv, C, cl, ref, wd);
+    if (exact) sum = exact_summary<CH, F>(k, v, row0, t0, Lv, C, cl, ref, wd);
 
     // ---- window: local carries and aggregate ----
     stage(sh, q, lane, sum);
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
                 if (st != (int)kAggregate) {
                     // not published in time: compute window j's aggregate here and publish
                     // it (bitwise what unit j itself publishes)
-                    const Carry X = window_aggregate<NW, CH>(sh, j, q, lane, T, C, row0, cl, k,
+                    const Carry X = window_aggregate<NW, CH, F>(sh, j, q, lane, T, C, row0, cl, k,
                                                              v, slow_wave, dwfd, wd, cw2);
                     if (q == 0) {
                         if (cval) put_rec(agg, nrec, (bidx * nseg + j) * C + cl, X);
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // the wave that holds token T-1 gives the state after it, when asked for
     if (fin != nullptr && t0 < T && T <= t0 + CH && cval) {
         if (exact)
-            final_state_exact<CH>(k, v, row0, t0, Lv, C, cl, mine, wd, fin, nrec / nseg,
+            final_state_exact<CH, F>(k, v, row0, t0, Lv, C, cl, mine, wd, fin, nrec / nseg,
                                   bidx * C + cl);
         else
             final_state<CH>(kc, vc, Lv, ref, mine, dwfd, fin, nrec / nseg, bidx * C + cl);
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const double ref2 = (double)ref * kLog2eD;
     float rc[GATE ? CH : 1];  // r of the chunk, loaded while the sweep runs
     if constexpr (GATE) {
-        if (!exact) load_chunk1<CH>(rc, r, row0, t0, T, C, voff);
+        if (!exact) load_chunk1<CH, F>(rc, r, row0, t0, T, C, voff);
     }
     if (!exact) {
         const double gap = mine.P - ref2;
@@ -394,18 +396,19 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     if (q == 0) put_flag(myflag, epoch, kInclusive);
     if (exact) {
         if (cval)
-            exact_outputs<CH>(k, v, GATE ? r : nullptr, y, row0, t0, Lv, C, cl, ref, mine, uc, wd);
+            exact_outputs<CH, F>(k, v, GATE ? r : nullptr, y, row0, t0, Lv, C, cl, ref, mine, uc,
+                                 wd);
         return;
     }
     if (cval) {
         const rsrc_t ry = make_rsrc(y + (row0 + t0) * C);
-        const int stride = (int)(C * 4);
+        const int stride = (int)(C * kIoBytes<F>);
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             if (j < Lv) {
                 float o = kc[j];
                 if constexpr (GATE) o *= sigmoidf_(rc[j]);
-                bstore(ry, o, voff, j * stride);
+                bstore_io<F>(ry, o, voff, j * stride);
             }
         }
     }
@@ -424,24 +427,43 @@ __global__ __launch_bounds__(256) void wkv_state_out_kernel(const float *__restr
     }
 }
 
-hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, const float *r, float *y, float *sa,
-                          float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
+template <Io F>
+static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int64_t C, int ngrp,
+                              int64_t nbg, uint64_t epoch, const float *w, const float *u,
+                              const void *k, const void *v, const void *r, void *y, float *sa,
+                              float *sb, float *sp, float *fin, const FwdLayout &L, int64_t B) {
+    const io_t<F> *kk = static_cast<const io_t<F> *>(k), *vv = static_cast<const io_t<F> *>(v),
+                  *rr = static_cast<const io_t<F> *>(r);
+    io_t<F> *yy = static_cast<io_t<F> *>(y);
+    if (r != nullptr)
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F>),
+                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, kk, vv, rr, yy, L.flags, L.agg, L.incl,
+                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+    else
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F>),
+                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
+                           nbg, L.nseg, epoch, w, u, kk, vv, rr, yy, L.flags, L.agg, L.incl,
+                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+}
+
+hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
+                          const float *u, const void *k, const void *v, const void *r, void *y,
+                          float *sa, float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
                           hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     float *fin = sa != nullptr ? L.fin : nullptr;
-    if (r != nullptr)
-        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true>),
-                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, k, v, r, y, L.flags, L.agg, L.incl,
-                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+    if (fmt == Io::BF16)
+        launch_forward_io<Io::BF16>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
+                                    sb, sp, fin, L, B);
+    else if (fmt == Io::F16)
+        launch_forward_io<Io::F16>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
+                                   sb, sp, fin, L, B);
     else
-        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false>),
-                           dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, k, v, r, y, L.flags, L.agg, L.incl,
-                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+        launch_forward_io<Io::F32>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
+                                   sb, sp, fin, L, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sa == nullptr) return e;
     const int64_t n = B * C;

@@ -6,6 +6,10 @@
 
 namespace wkvdev {
 
+// Storage formats of the [B][T][C] tensors at the boundary (the state and all arithmetic
+// stay fp32/fp64 whatever the format).
+enum class Io { F32, BF16, F16 };
+
 // Forward geometry: a unit is 64 channels x one window of kFwdWaves * kFwdChunk tokens.
 constexpr int kFwdWaves = 2;
 constexpr int kFwdChunk = 32;
@@ -82,18 +86,21 @@ hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out);
 // convention (A = a e^p, B = b e^p); when given, they are overwritten with the state after
 // token T-1 (through L.fin, by a second kernel, so that no workgroup can read a state that
 // another has already replaced). Without them the scan starts from the empty state.
-// `r` ([B][T][C]) or null: with it the output is sigma(r) * y, the receptance gate.
-hipError_t launch_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                          const float *k, const float *v, const float *r, float *y, float *sa,
-                          float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
+// `r` ([B][T][C]) or null: with it the output is sigma(r) * y, the receptance gate. k, v, r
+// and y are in storage format `fmt` (the state sa, sb, sp stays fp32).
+hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
+                          const float *u, const void *k, const void *v, const void *r, void *y,
+                          float *sa, float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
                           hipStream_t stream);
 
 // `F` is the forward workspace filled for the same inputs (its chunk carries are read).
-// With `r` (and `dr`) the forward output was sigma(r) * y and `dy` is its cotangent.
-hipError_t launch_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                           const float *k, const float *v, const float *dy, const float *r,
-                           const FwdLayout &F, float *dk, float *dv, float *dr, float *dw,
-                           float *du, const BwdLayout &L, uint64_t epoch, hipStream_t stream);
+// With `r` (and `dr`) the forward output was sigma(r) * y and `dy` is its cotangent. k, v,
+// dy, r, dk, dv, dr are in storage format `fmt`; dw, du are fp32.
+hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
+                           const float *u, const void *k, const void *v, const void *dy,
+                           const void *r, const FwdLayout &F, void *dk, void *dv, void *dr,
+                           float *dw, float *du, const BwdLayout &L, uint64_t epoch,
+                           hipStream_t stream);
 
 // dw = du = 0 over C channels (backward of an empty batch or sequence).
 hipError_t launch_zero2(float *dw, float *du, int64_t C, hipStream_t stream);

@@ -31,3 +31,38 @@ def assert_wkv_close(got, ref, what="", rtol=RTOL, floor=FLOOR):
         raise AssertionError("%s: tolerance exceeded %.3gx at %s: got %r, oracle %r"
                              % (what, v, idx, float(got[idx]), float(ref[idx])))
     return v
+
+
+# Spacing of the representable numbers next to x in a 16-bit output format (mantissa bits
+# after the leading one; smallest normal exponent): one unit in the last place.
+_FMT = {"bfloat16": (7, -126), "float16": (10, -14)}
+
+
+def fmt_ulp(x, fmt):
+    mant, emin = _FMT[fmt]
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** emin)))
+    return 2.0 ** (e - mant)
+
+
+def assert_io_close(got, ref, fmt, what="", rtol=RTOL, floor=FLOOR):
+    """A 16-bit output against the fp64 oracle on the same (exactly widened) inputs: within
+    the fp32 tolerance plus one unit in the last place of the format (a faithfully rounded
+    result of a computation accurate to the fp32 tolerance). Returns the largest fraction of
+    that allowance used."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise AssertionError("shape %s != %s" % (got.shape, ref.shape))
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        raise AssertionError("%s: non-finite output" % what)
+    allow = rtol * np.maximum(np.abs(ref), floor) + fmt_ulp(ref, fmt)
+    r = np.abs(got - ref) / allow
+    v = float(np.max(r))
+    if not v <= 1.0:
+        idx = np.unravel_index(int(np.argmax(r)), r.shape)
+        raise AssertionError("%s: allowance exceeded %.3gx at %s: got %r, oracle %r"
+                             % (what, v, idx, float(got[idx]), float(ref[idx])))
+    return v
