@@ -133,6 +133,32 @@ def test_forward_state_rejects_bad_arguments(pkg):
     assert lib.wkv_last_error() == b""
 
 
+def test_typed_entry_points_reject_bad_arguments(pkg):
+    lib = pkg.load_library()
+    f = FAKE
+
+    def fwd(dtype, k=f[2], r=None):
+        return lib.wkv_forward_typed(dtype, 2, 3, 4, f[0], f[1], k, f[3], r, f[4], f[6],
+                                     1 << 40, None)
+
+    assert fwd(7) == pkg.WKV_ERR_INVALID_ARG
+    assert b"unknown dtype 7" in lib.wkv_last_error()
+    # 16-bit tensors need 2-byte alignment only, fp32 ones 4
+    assert fwd(pkg.WKV_BF16, k=ctypes.c_void_p(f[2].value + 1)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"2-byte aligned" in lib.wkv_last_error()
+    assert fwd(pkg.WKV_F32, k=ctypes.c_void_p(f[2].value + 2)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"4-byte aligned" in lib.wkv_last_error()
+
+    def bwd(dtype, r=None, dr=None):
+        return lib.wkv_backward_typed(dtype, 2, 3, 4, f[0], f[1], f[2], f[3], f[4], r, None,
+                                      f[5], f[6], dr, f[9], f[10], f[11], 1 << 40, None)
+
+    assert bwd(pkg.WKV_F16, r=f[7]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"r and dr must be given together" in lib.wkv_last_error()
+    assert bwd(-1) == pkg.WKV_ERR_INVALID_ARG
+    assert b"unknown dtype" in lib.wkv_last_error()
+
+
 def test_zero_sized_forward_is_a_noop(pkg):
     lib = pkg.load_library()
     none = [None] * 5
