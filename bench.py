@@ -7,7 +7,7 @@ distributions of the 3B-class layer workload in wkv_inputs.py) and resident in H
 before timing starts; the step reuses preallocated outputs and workspaces.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-state]
-                    [--no-gated] [--no-bf16]
+                    [--no-gated] [--no-bf16] [--no-shift]
 
 prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
 `roofline` describes the kernel that takes most of the step, with its algorithmic bytes
@@ -21,7 +21,7 @@ threads) on the same workload. `decode` reports the batched decode step separate
 from a given state that also returns the final state (prompt prefill), on the same layer;
 `gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer; `bf16`
 the step with the [B, T, C] tensors stored as bfloat16 (reported apart: the benchmark's own
-workload is fp32).
+workload is fp32); `token_shift` the mix that produces the projections' inputs.
 
 The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
 load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
@@ -368,6 +368,38 @@ def bench_bf16(wkv, torch, dev, x, steps=100, warmup=100):
             "steps": steps, "outputs_finite": ok}
 
 
+def bench_shift(wkv, torch, dev, steps=100, warmup=50):
+    """The token-shift mix on the benchmark layer's shape, back to back: forward 16 B
+    (x read, three mixes written) and backward 20 B per element (three cotangents and x
+    read, dx written)."""
+    B, T, C = 8, 4096, 2560
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1008)
+    x = torch.randn(B, T, C, device=dev, generator=gen)
+    mu = torch.rand(3, C, device=dev, generator=gen)
+    prev = torch.randn(B, C, device=dev, generator=gen)
+    dout = [torch.randn(B, T, C, device=dev, generator=gen) for _ in range(3)]
+    for _ in range(warmup):
+        wkv.token_shift(x, mu, prev)
+        wkv.token_shift_backward(x, mu, dout, prev)
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        wkv.token_shift(x, mu, prev)
+        e[1].record()
+        wkv.token_shift_backward(x, mu, dout, prev)
+        e[2].record()
+    torch.cuda.synchronize(dev)
+    f_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    b_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    n = B * T * C
+    return {"workload": "token-shift mix, B=%d T=%d C=%d" % (B, T, C), "forward_us": f_us,
+            "backward_us": b_us,
+            "forward_frac_of_peak": 16 * n / (f_us * 1e-6) / 1e9 / PEAK_GBPS,
+            "backward_frac_of_peak": 20 * n / (b_us * 1e-6) / 1e9 / PEAK_GBPS, "steps": steps}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +412,7 @@ def main(argv=None):
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the receptance-gated measurement")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bfloat16 measurement")
+    ap.add_argument("--no-shift", action="store_true", help="skip the token-shift measurement")
     ap.add_argument("--with-copy", action="store_true",
                     help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -447,6 +480,8 @@ def main(argv=None):
         out["gated"] = bench_gated(wkv, torch, dev, x)
     if not args.no_bf16:
         out["bf16"] = bench_bf16(wkv, torch, dev, x)
+    if not args.no_shift:
+        out["token_shift"] = bench_shift(wkv, torch, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)
     else:

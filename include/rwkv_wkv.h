@@ -162,6 +162,27 @@ int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *
 int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
                     const float *v, float *a, float *b, float *p, float *y, void *stream);
 
+/* Token-shift mix, the step that produces the inputs of the R, K, V projections
+ * ("RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (7): they are computed from a
+ * weighted sum of the current and the previous token's input, one trained per-channel weight
+ * each): for x [B][T][C] and mu [3][C] (rows r, k, v),
+ *     out_m[b][t][c] = mu[m][c] x[b][t][c] + (1 - mu[m][c]) x[b][t-1][c],   m = r, k, v,
+ * where x[b][-1] is x_prev[b] ([B][C]; NULL means zeros, a fresh sequence). x_last ([B][C])
+ * receives x[b][T-1] (the next call's x_prev) unless NULL. Outputs must not overlap inputs. */
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, const float *x, const float *x_prev,
+                    const float *mu, float *out_r, float *out_k, float *out_v, float *x_last,
+                    void *stream);
+
+/* Bytes of device scratch wkv_token_shift_backward needs (fp64 partials of dmu). */
+size_t wkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+
+/* Backward of L = sum_m sum dout_m * out_m: dx [B][T][C], dx_prev [B][C] (unless NULL) and
+ * dmu [3][C], the last summed over b and t in a fixed order and overwritten. */
+int wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, const float *x,
+                             const float *x_prev, const float *mu, const float *dout_r,
+                             const float *dout_k, const float *dout_v, float *dx, float *dx_prev,
+                             float *dmu, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

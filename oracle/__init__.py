@@ -19,7 +19,9 @@ Routines: ``forward_direct`` (the O(T^2) definition), ``forward_recurrent`` (pla
 recursion), ``forward_rescaled`` / ``decode_step`` (recursion on a rescaled state),
 ``backward_direct`` (O(T^2) from the softmax form) and ``backward_recurrent``
 (linear-time carries). Each is pinned in tests/ against closed forms, invariants,
-finite differences and autograd, not against another routine alone.
+finite differences and autograd, not against another routine alone. ``token_shift`` and
+``token_shift_backward`` (numpy, token_shift.py) are the mix of formula (7) that feeds the
+projections.
 """
 from __future__ import annotations
 
@@ -190,3 +192,6 @@ def backward_recurrent(w, u, k, v, dy):
     if rc:
         raise OverflowError("plain recursion needs max|k| + max|u| < 600")
     return dk, dv, dw, du
+
+
+from .token_shift import token_shift, token_shift_backward  # noqa: E402,F401

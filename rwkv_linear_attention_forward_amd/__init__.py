@@ -14,6 +14,8 @@ Entry points mirror the C ABI in include/rwkv_wkv.h:
     forward_workspace(B, T, C, device) -> uint8 tensor sized for the forward
     backward(w, u, k, v, dy, fwd_workspace=None) -> (dk, dv, dw, du)
     decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
+    token_shift(x, mu, x_prev=None) -> (out_r, out_k, out_v, x_last)
+    token_shift_backward(x, mu, dout, x_prev=None) -> (dx, dx_prev, dmu)
 
 Operator ("RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (8)):
     y_t = (sum_{i<t} e^{-(t-1-i)w + k_i} v_i + e^{u+k_t} v_t)
@@ -38,7 +40,8 @@ WKV_ERR_HIP = 3
 EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
-           "wkv_backward_typed", "wkv_decode_step")
+           "wkv_backward_typed", "wkv_decode_step", "wkv_token_shift",
+           "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
 
 # Storage formats of the [B, T, C] tensors (dtype codes of the *_typed entry points).
 WKV_F32, WKV_BF16, WKV_F16 = 0, 1, 2
@@ -74,6 +77,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_typed.restype = ctypes.c_int
     lib.wkv_backward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_token_shift.restype = ctypes.c_int
+    lib.wkv_token_shift.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wkv_token_shift_backward_workspace_size.restype = ctypes.c_size_t
+    lib.wkv_token_shift_backward_workspace_size.argtypes = [_I64, _I64, _I64]
+    lib.wkv_token_shift_backward.restype = ctypes.c_int
+    lib.wkv_token_shift_backward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, ctypes.c_size_t, _P]
     lib.wkv_forward_gated.restype = ctypes.c_int
     lib.wkv_forward_gated.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
@@ -315,6 +325,57 @@ def decode_step(w, u, k, v, a, b, p, out=None):
     _check(load_library().wkv_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(a),
                                           _ptr(b), _ptr(p), _ptr(y), _stream(dev)))
     return y
+
+
+def _check_shift(x, mu, x_prev):
+    _need(x, "x", 3)
+    dev = x.device
+    B, T, C = x.shape
+    _need(mu, "mu", 2, dev)
+    if tuple(mu.shape) != (3, C):
+        raise ValueError("mu must have shape (3, %d)" % C)
+    if x_prev is not None:
+        _need(x_prev, "x_prev", 2, dev)
+        if tuple(x_prev.shape) != (B, C):
+            raise ValueError("x_prev must have shape (%d, %d)" % (B, C))
+    return B, T, C, dev
+
+
+def token_shift(x, mu, x_prev=None):
+    """The token-shift mix: out_m = mu[m] * x[t] + (1 - mu[m]) * x[t-1] for m = r, k, v
+    (x[-1] = x_prev, zeros if None). Returns (out_r, out_k, out_v, x_last)."""
+    B, T, C, dev = _check_shift(x, mu, x_prev)
+    outs = tuple(torch.empty_like(x) for _ in range(3))
+    last = torch.empty(B, C, dtype=torch.float32, device=dev)
+    _check(load_library().wkv_token_shift(B, T, C, _ptr(x), _ptr(x_prev), _ptr(mu),
+                                          _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                          _ptr(last) if T > 0 else None, _stream(dev)))
+    if T == 0:
+        last = x_prev.clone() if x_prev is not None else torch.zeros(B, C, device=dev)
+    return outs + (last,)
+
+
+def token_shift_backward(x, mu, dout, x_prev=None):
+    """(dx, dx_prev, dmu) of sum over m of dout[m] * out_m; dx_prev is None without x_prev
+    (a fresh sequence has no previous input)."""
+    B, T, C, dev = _check_shift(x, mu, x_prev)
+    if len(dout) != 3:
+        raise ValueError("dout must hold the three cotangents (r, k, v)")
+    for t, n in zip(dout, ("dout_r", "dout_k", "dout_v")):
+        _need(t, n, 3, dev)
+        if t.shape != x.shape:
+            raise ValueError("%s has the wrong shape" % n)
+    lib = load_library()
+    ws = torch.empty(max(16, int(lib.wkv_token_shift_backward_workspace_size(B, T, C))),
+                     dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(x)
+    dprev = torch.empty(B, C, dtype=torch.float32, device=dev) if x_prev is not None else None
+    dmu = torch.empty(3, C, dtype=torch.float32, device=dev)
+    _check(lib.wkv_token_shift_backward(B, T, C, _ptr(x), _ptr(x_prev), _ptr(mu),
+                                        _ptr(dout[0]), _ptr(dout[1]), _ptr(dout[2]), _ptr(dx),
+                                        _ptr(dprev), _ptr(dmu), _ptr(ws), ws.numel(),
+                                        _stream(dev)))
+    return dx, dprev, dmu
 
 
 class WKV(torch.autograd.Function):

@@ -544,4 +544,115 @@ int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const 
     return WKV_OK;
 }
 
+namespace {
+
+// Written buffers (the first nout of ptrs) must not overlap any other non-null buffer.
+bool disjoint(const void *const *ptrs, const size_t *sizes, const char *const *names, int n,
+              int nout, const char *fn) {
+    for (int i = 0; i < nout; ++i)
+        for (int j = 0; j < n; ++j)
+            if (j != i && ptrs[i] != nullptr && ptrs[j] != nullptr &&
+                overlap(ptrs[i], sizes[i], ptrs[j], sizes[j])) {
+                fail(WKV_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, names[i], names[j]);
+                return false;
+            }
+    return true;
+}
+
+bool shift_dims_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
+    if (!dims_ok(B, T, C, fn)) return false;
+    const int64_t waves = B * ((T + 63) / 64) * ((C + 63) / 64);
+    if (waves / 4 + 1 > INT32_MAX) {
+        fail(WKV_ERR_INVALID_ARG, "%s: too many workgroups", fn);
+        return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, const float *x, const float *x_prev,
+                    const float *mu, float *out_r, float *out_k, float *out_v, float *x_last,
+                    void *stream) {
+    static const char *fn = "wkv_token_shift";
+    g_err[0] = '\0';
+    if (!shift_dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    if (!nonnull(x, "x", fn) || !nonnull(mu, "mu", fn) || !nonnull(out_r, "out_r", fn) ||
+        !nonnull(out_k, "out_k", fn) || !nonnull(out_v, "out_v", fn))
+        return WKV_ERR_INVALID_ARG;
+    const size_t nb = (size_t)(B * T * C) * 4u, ns = (size_t)(B * C) * 4u, nm = (size_t)C * 12u;
+    const void *ptrs[7] = {out_r, out_k, out_v, x_last, x, x_prev, mu};
+    const size_t sizes[7] = {nb, nb, nb, ns, nb, ns, nm};
+    const char *names[7] = {"out_r", "out_k", "out_v", "x_last", "x", "x_prev", "mu"};
+    for (int i = 0; i < 7; ++i)
+        if (ptrs[i] != nullptr && !aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
+    if (!disjoint(ptrs, sizes, names, 7, 4, fn)) return WKV_ERR_INVALID_ARG;
+    int rc = check_device(fn);
+    if (rc != WKV_OK) return rc;
+    hipError_t e = wkvdev::launch_shift(B, T, C, x, x_prev, mu, out_r, out_k, out_v, x_last,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, fn);
+    return WKV_OK;
+}
+
+size_t wkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || C > kMaxC) return 0;
+    if (B > 0 && T > 0 && C > 0 && (T > kMaxElems / B || B * T > kMaxElems / C)) return 0;
+    return round_up((size_t)3 * (size_t)B * (size_t)wkvdev::shift_chunks(T) * (size_t)C * 8u,
+                    256);
+}
+
+int wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, const float *x,
+                             const float *x_prev, const float *mu, const float *dout_r,
+                             const float *dout_k, const float *dout_v, float *dx, float *dx_prev,
+                             float *dmu, void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_token_shift_backward";
+    g_err[0] = '\0';
+    if (!shift_dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (C == 0) return WKV_OK;
+    if (!nonnull(dmu, "dmu", fn) || !aligned(dmu, 4, "dmu", fn)) return WKV_ERR_INVALID_ARG;
+    if (B == 0 || T == 0) {
+        int rc = check_device(fn);
+        if (rc != WKV_OK) return rc;
+        // dmu = 0 over its 3C entries
+        hipError_t e = wkvdev::launch_zero2(dmu, dmu + C, C, static_cast<hipStream_t>(stream));
+        if (e == hipSuccess)
+            e = wkvdev::launch_zero2(dmu + 2 * C, dmu + 2 * C, C, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, fn);
+        if (dx_prev != nullptr && B > 0) {
+            // no token: nothing flows to the previous token's input
+            e = wkvdev::launch_zero2(dx_prev, dx_prev, B * C, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return fail_hip(e, fn);
+        }
+        return WKV_OK;
+    }
+    if (!nonnull(x, "x", fn) || !nonnull(mu, "mu", fn) || !nonnull(dout_r, "dout_r", fn) ||
+        !nonnull(dout_k, "dout_k", fn) || !nonnull(dout_v, "dout_v", fn) ||
+        !nonnull(dx, "dx", fn) || !nonnull(workspace, "workspace", fn))
+        return WKV_ERR_INVALID_ARG;
+    const size_t need = wkv_token_shift_backward_workspace_size(B, T, C);
+    if (workspace_bytes < need)
+        return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    if (!aligned(workspace, 16, "workspace", fn)) return WKV_ERR_INVALID_ARG;
+    const size_t nb = (size_t)(B * T * C) * 4u, ns = (size_t)(B * C) * 4u, nm = (size_t)C * 12u;
+    const void *ptrs[10] = {dx, dx_prev, dmu, workspace, x, x_prev, mu, dout_r, dout_k, dout_v};
+    const size_t sizes[10] = {nb, ns, nm, need, nb, ns, nm, nb, nb, nb};
+    const char *names[10] = {"dx", "dx_prev", "dmu", "workspace", "x", "x_prev", "mu",
+                             "dout_r", "dout_k", "dout_v"};
+    for (int i = 0; i < 10; ++i)
+        if (i != 3 && ptrs[i] != nullptr && !aligned(ptrs[i], 4, names[i], fn))
+            return WKV_ERR_INVALID_ARG;
+    if (!disjoint(ptrs, sizes, names, 10, 4, fn)) return WKV_ERR_INVALID_ARG;
+    int rc = check_device(fn);
+    if (rc != WKV_OK) return rc;
+    hipError_t e = wkvdev::launch_shift_backward(B, T, C, x, x_prev, mu, dout_r, dout_k, dout_v,
+                                                 dx, dx_prev, dmu,
+                                                 static_cast<double *>(workspace),
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, fn);
+    return WKV_OK;
+}
+
 }  // extern "C"

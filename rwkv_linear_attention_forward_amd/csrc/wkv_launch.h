@@ -105,6 +105,17 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
 // dw = du = 0 over C channels (backward of an empty batch or sequence).
 hipError_t launch_zero2(float *dw, float *du, int64_t C, hipStream_t stream);
 
+// Token-shift mix (out_m = mu_m x[t] + (1 - mu_m) x[t-1], m = r, k, v) and its backward;
+// `part` holds 3 * B * shift_chunks(T) * C fp64 partials of dmu.
+int64_t shift_chunks(int64_t T);
+hipError_t launch_shift(int64_t B, int64_t T, int64_t C, const float *x, const float *x_prev,
+                        const float *mu, float *o_r, float *o_k, float *o_v, float *x_last,
+                        hipStream_t stream);
+hipError_t launch_shift_backward(int64_t B, int64_t T, int64_t C, const float *x,
+                                 const float *x_prev, const float *mu, const float *d_r,
+                                 const float *d_k, const float *d_v, float *dx, float *dx_prev,
+                                 float *dmu, double *part, hipStream_t stream);
+
 hipError_t launch_decode(int64_t B, int64_t C, const float *w, const float *u, const float *k,
                          const float *v, float *a, float *b, float *p, float *y,
                          hipStream_t stream);

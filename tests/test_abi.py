@@ -159,6 +159,24 @@ def test_typed_entry_points_reject_bad_arguments(pkg):
     assert b"unknown dtype" in lib.wkv_last_error()
 
 
+def test_token_shift_rejects_bad_arguments(pkg):
+    lib = pkg.load_library()
+    f = FAKE
+    assert lib.wkv_token_shift(2, 3, 4, None, None, f[1], f[2], f[3], f[4], None,
+                               None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"x is NULL" in lib.wkv_last_error()
+    # an output overlapping x
+    assert lib.wkv_token_shift(2, 3, 4, f[0], None, f[1], ctypes.c_void_p(f[0].value + 8), f[3],
+                               f[4], None, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"out_r overlaps x" in lib.wkv_last_error()
+    assert lib.wkv_token_shift(0, 3, 4, *([None] * 7), None) == pkg.WKV_OK
+    # fp64 partials of dmu: 3 fields x B x ceil(T / 32) stretches x C
+    assert lib.wkv_token_shift_backward_workspace_size(8, 4096, 2560) == 3 * 8 * 128 * 2560 * 8
+    assert lib.wkv_token_shift_backward(2, 3, 4, f[0], None, f[1], f[2], f[3], f[4], f[5], None,
+                                        f[6], f[7], 10, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace has 10 bytes" in lib.wkv_last_error()
+
+
 def test_zero_sized_forward_is_a_noop(pkg):
     lib = pkg.load_library()
     none = [None] * 5
