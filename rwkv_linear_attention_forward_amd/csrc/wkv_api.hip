@@ -219,45 +219,6 @@ bool bwd_grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
 
 }  // namespace
 
-namespace wkvdev {
-
-hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out) {
-    struct Entry {
-        int dev;
-        const void *kernel;
-        int threads;
-        int64_t n;
-    };
-    static std::mutex mu;
-    static Entry cache[64];
-    static int ncache = 0;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    {
-        std::lock_guard<std::mutex> lk(mu);
-        for (int i = 0; i < ncache; ++i)
-            if (cache[i].dev == dev && cache[i].kernel == kernel && cache[i].threads == threads) {
-                *out = cache[i].n;
-                return hipSuccess;
-            }
-    }
-    int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    const int64_t n = (int64_t)(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
-    {
-        std::lock_guard<std::mutex> lk(mu);
-        if (ncache < 64) cache[ncache++] = Entry{dev, kernel, threads, n};
-    }
-    *out = n;
-    return hipSuccess;
-}
-
-}  // namespace wkvdev
-
 extern "C" {
 
 int wkv_version(void) { return 100; }  // 0.1.0

@@ -78,10 +78,6 @@ struct BwdLayout {
     double *part;
 };
 
-// Workgroups of `kernel` (block of `threads`, static LDS only) that the current device holds
-// at once: its occupancy per CU times the CU count (cached per device and kernel).
-hipError_t resident_workgroups(const void *kernel, int threads, int64_t *out);
-
 // `sa`, `sb`, `sp` ([B][C], all three or none) hold the state before token 0 in the decode
 // convention (A = a e^p, B = b e^p); when given, they are overwritten with the state after
 // token T-1 (through L.fin, by a second kernel, so that no workgroup can read a state that
