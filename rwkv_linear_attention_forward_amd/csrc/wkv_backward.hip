@@ -177,14 +177,15 @@ __device__ __forceinline__ RevCarry exact_chunk(
 }
 
 // LDS of a backward unit: staging for the window's reverse summaries and the dw/du
-// partials, and each wave's per-token (sigma_j, y_j) from F3 until its reverse sweep.
+// partials, and each wave's per-token sigma_j y_j from F3 until its reverse sweep (sigma_j
+// itself stays in the registers that held dy_j: half the LDS of staging both).
 template <int NW, int CH>
 struct BwdShared {
     double a[NW][64];
     double b[NW][64];
     double r[NW][64];
     double pu[NW][64], pw[NW][64];  // each wave's du, dw terms
-    float2 sy[NW][CH][64];
+    float sy[NW][CH][64];
     int status[2];
 };
 
@@ -203,7 +204,7 @@ struct BwdConst {
 // reverse summary from a zero future (R1):
 //   R = sum_j e^{-j w} sigma_j,  Q = sum_j e^{-j w} sigma_j y_j   (future sums at the
 // chunk start, in the chunk frame).
-// Also the chunk's dw, du terms; e_j, v_j are left in kc, vc and (sigma_j, sigma_j y_j) in
+// Also the chunk's dw, du terms; e_j, v_j, sigma_j are left in kc, vc, gc and sigma_j y_j in
 // `sy` (fp32) for the reverse sweep, unless fx (the fixed frame failed for some lane of the
 // wave; the chunk then takes the per-token path). helper_summary repeats the summary
 // arithmetic op for op, so a helper publishes the bits the owner would (every fused
@@ -215,7 +216,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
     io_t<IO> *__restrict__ dr, const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
     const io_t<IO> *__restrict__ dy,
     const BwdConst &K, float (&kc)[CH], float (&vc)[CH], float (&gc)[CH],
-    float2 (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
+    float (*__restrict__ sy)[64], int lane, bool &fx, float &ref, int &Lv, double &du_acc,
     double &dw_acc) {
     const int64_t t0 = ci * CH;
     Lv = chunk_len(t0, T, CH);
@@ -277,7 +278,8 @@ __device__ __forceinline__ RevCarry chunk_pass(
             R = fma(pw, sg, R);
             Q = fma(pw, sgy, Q);
             kc[j] = (float)e;
-            sy[j][lane] = make_float2((float)sg, (float)sgy);
+            gc[j] = (float)sg;
+            sy[j][lane] = (float)sgy;
             pw *= K.dwf;
             Ps = fma(Ps, K.dwf, Sx);
             Pz = fma(Pz, K.dwf, Zx);
@@ -528,9 +530,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
 #pragma unroll
         for (int j = CH - 1; j >= 0; --j) {
             // dv = e (e^u s + R),  dk = e (e^u s (v - y) + v R - Q) = v dv - e (e^u s y + Q)
-            const float2 p = sh.sy[q][j][lane];
             const double e = (double)kc[j], vv = (double)vc[j];
-            const double sg = (double)p.x, sgy = (double)p.y;
+            const double sg = (double)gc[j], sgy = (double)sh.sy[q][j][lane];
             const double dvv = e * fma(K.eu, sg, R);
             const double dkk = fma(vv, dvv, -(e * fma(K.eu, sgy, Q)));
             kc[j] = (float)dvv;
