@@ -322,6 +322,9 @@ def decode_step(w, u, k, v, a, b, p, out=None):
     if w.shape[0] != C or u.shape[0] != C:
         raise ValueError("w and u must have C=%d elements" % C)
     y = torch.empty_like(k) if out is None else out
+    _need(y, "out", 2, dev)
+    if y.shape != k.shape:
+        raise ValueError("out has the wrong shape")
     _check(load_library().wkv_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(a),
                                           _ptr(b), _ptr(p), _ptr(y), _stream(dev)))
     return y

@@ -103,3 +103,92 @@ def test_sentinels_and_large_keys(wkv, dev):
         yg = y.cpu().numpy()
         assert np.all(np.isfinite(yg))
         assert_wkv_close(yg, yr, "step %d" % s, rtol=2e-3)
+
+
+def test_decode_rejects_bad_output_tensor(wkv, dev):
+    # a wrong `out` is refused before any launch (the kernel would write B*C floats to it)
+    import torch
+    B, C = 4, 96
+    k = torch.zeros(B, C, device=dev)
+    w = torch.ones(C, device=dev)
+    st = [torch.zeros(B, C, device=dev) for _ in range(3)]
+    for bad in (torch.zeros(B, C - 1, device=dev), torch.zeros(B * C, device=dev),
+                torch.zeros(B, C, device=dev, dtype=torch.float64)):
+        with pytest.raises((ValueError, TypeError)):
+            wkv.decode_step(w, w, k, k, *st, out=bad)
+    y = wkv.decode_step(w, w, k, k, *st, out=torch.empty(B, C, device=dev))
+    torch.cuda.synchronize()
+    assert y.shape == (B, C)
+
+
+def _decode_inputs(torch, dev, B, C, seed):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    w = torch.exp(torch.rand(C, device=dev, generator=g) * 10 - 8)
+    u = torch.rand(C, device=dev, generator=g) * 2 - 1
+    k = torch.randn(B, C, device=dev, generator=g) * 3
+    v = torch.randn(B, C, device=dev, generator=g)
+    b = torch.rand(B, C, device=dev, generator=g) * 4 + 1
+    a = b * torch.randn(B, C, device=dev, generator=g)
+    p = torch.randn(B, C, device=dev, generator=g) * 5
+    return w, u, k, v, a, b, p
+
+
+def test_decode_grid_stride_pass(wkv, dev):
+    # B*C past 2^28 elements: the launch caps its grid and lanes loop; the result is bitwise
+    # that of the same rows decoded in two calls of one pass each
+    import torch
+    B, C = 65600, 4099
+    assert B * C > (1 << 28)
+    w, u, k, v, a, b, p = _decode_inputs(torch, dev, B, C, 32)
+    st = [t.clone() for t in (a, b, p)]
+    y = wkv.decode_step(w, u, k, v, *st)
+    half = B // 2
+    yh = torch.empty_like(y)
+    for r0, r1 in ((0, half), (half, B)):
+        wkv.decode_step(w, u, k[r0:r1], v[r0:r1], a[r0:r1], b[r0:r1], p[r0:r1], out=yh[r0:r1])
+    torch.cuda.synchronize()
+    assert torch.equal(y, yh)
+    for x, z in zip(st, (a, b, p)):
+        assert torch.equal(x, z)
+
+
+def test_decode_graph_replays_match_eager(wkv, dev):
+    # a serving loop captures its per-layer decode calls once and replays them: every replay
+    # (with eager work and synchronizations in between) must equal the same calls made eagerly
+    import torch
+    B, C, L = 16, 320, 4
+    per = [_decode_inputs(torch, dev, B, C, 40 + l) for l in range(L)]
+    gst = [[t.clone() for t in x[4:]] for x in per]
+    est = [[t.clone() for t in x[4:]] for x in per]
+    kv = torch.empty(L, 2, B, C, device=dev)
+    y = torch.empty(L, B, C, device=dev)
+
+    def calls(st, out):
+        for l in range(L):
+            w, u = per[l][0], per[l][1]
+            wkv.decode_step(w, u, kv[l, 0], kv[l, 1], *st[l], out=out[l])
+
+    kv.normal_()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(gst, y)  # warm-up outside the capture, as a real loop would
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ye = torch.empty_like(y)
+    calls(est, ye)  # the eager twin takes the same first step
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(gst, y)
+    torch.cuda.synchronize()
+    for r in range(4):
+        kv.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        calls(est, ye)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ye), "replay %d" % r
+        for l in range(L):
+            for x, z in zip(gst[l], est[l]):
+                assert torch.equal(x, z), "replay %d layer %d" % (r, l)
