@@ -101,6 +101,22 @@ def test_parameter_extremes(wkv, dev, case):
     _check(got, ref, case)
 
 
+def test_large_bonus_with_a_vanishing_first_key(wkv, dev):
+    # A sequence opening with a key ~95 below its chunk's largest, on channels with a large
+    # bonus u (20..45): the first token's denominator is e^u e^{k_0} alone, its in-frame
+    # weight e^{k_0 - ref} lies below the fp32 normal range and e^u sigma_0 above it, while
+    # dv_0 ~ dy_0 is ordinary (an fp32 sweep over such a chunk overflows).
+    B, T, C = 2, 96, 64
+    x = wkv_inputs.generate("l3b", seed=29, B=B, T=T, C=C)
+    x["k"][:, 0, :] = np.float32(-95.0)
+    x["u"] = np.linspace(20, 45, C).astype(np.float32)
+    got = _gpu_backward(wkv, dev, x)
+    for g in got:
+        assert np.all(np.isfinite(g))
+    ref = oracle.backward_direct(x["w"], x["u"], x["k"], x["v"], x["dy"])
+    _check(got, ref, "vanishing first key")
+
+
 def test_autograd_wrapper(wkv, dev):
     import torch
     x = wkv_inputs.generate("small", B=2, T=300, C=72)
