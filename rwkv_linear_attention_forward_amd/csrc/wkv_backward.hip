@@ -253,13 +253,14 @@ __device__ __forceinline__ RevCarry chunk_pass(
         for (int j = 0; j < CH; ++j) {
             // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0; the clamp on den
             // keeps 1/den finite where a padded token's den (the decayed carry alone) falls
-            // below the fp32 range, so that its sigma is 0 and not NaN
+            // below the fp32 range, so that its sigma is 0 and not NaN. Their den enters dmin
+            // too: at worst a ragged last chunk takes the per-token path.
             const double e = exp2_64(fma((double)kc[j], kLog2eD, -ref2));
             const double vv = (double)vc[j];
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            dmin = (j < Lv) ? fmin(dmin, den) : dmin;
+            dmin = fmin(dmin, den);
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
             double gd = (double)gc[j];
@@ -544,11 +545,13 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     if (Lv == 0) {
         // past the sequence end: nothing to store
     } else if (!rx) {
+        if (cval) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            if (j < Lv && cval) {
-                bstore_io<IO>(rdv, kc[j], voff, j * stride);
-                bstore_io<IO>(rdk, vc[j], voff, j * stride);
+            for (int j = 0; j < CH; ++j) {
+                if (j < Lv) {
+                    bstore_io<IO>(rdv, kc[j], voff, j * stride);
+                    bstore_io<IO>(rdk, vc[j], voff, j * stride);
+                }
             }
         }
     } else {

@@ -386,8 +386,8 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             const float e = kc[j], ev = e * vc[j];
             const float num = fmaf(eu, ev, Sx);
             const float den = fmaf(eu, e, Zx);
-            dmin = (j < Lv) ? fminf(dmin, den) : dmin;
-            kc[j] = num * rcpf(den);
+            dmin = fminf(dmin, den);  // padded tokens too: at worst a ragged last chunk
+            kc[j] = num * rcpf(den);     // goes the per-token way (its decayed carry is tiny)
             Sx = fmaf(Sx, dc.dwf, ev);
             Zx = fmaf(Zx, dc.dwf, e);
         }
