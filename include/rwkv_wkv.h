@@ -54,6 +54,16 @@ extern "C" {
 /* Library version, as 10000*major + 100*minor + patch. */
 int wkv_version(void);
 
+/* The look-back's patience, for every later call from any thread: how many times a
+ * workgroup re-reads the flag of a window that has published nothing yet (an earlier
+ * window in the forward, a later one in the backward) before it recomputes that window's
+ * aggregate from the inputs itself. The scan is canonical, so results are bitwise the same
+ * whatever the value; it trades waiting for recomputation. `tries` >= 0 (default 2000; 0
+ * recomputes whenever a flag is not already there, which tests use to drive that path).
+ * Returns WKV_OK, or WKV_ERR_INVALID_ARG for a negative count. */
+int wkv_set_poll_limit(int tries);
+int wkv_poll_limit(void);
+
 /* Static description of a status code ("ok", "invalid argument", ...). Never NULL. */
 const char *wkv_status_string(int status);
 

@@ -37,7 +37,8 @@ WKV_ERR_UNSUPPORTED = 2
 WKV_ERR_HIP = 3
 
 # Every symbol the header declares, for the export check.
-EXPORTS = ("wkv_version", "wkv_status_string", "wkv_last_error", "wkv_forward_workspace_size",
+EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_string",
+           "wkv_last_error", "wkv_forward_workspace_size",
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
            "wkv_backward_typed", "wkv_decode_step", "wkv_token_shift",
@@ -63,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.wkv_version.restype = ctypes.c_int
     lib.wkv_version.argtypes = []
+    lib.wkv_set_poll_limit.restype = ctypes.c_int
+    lib.wkv_set_poll_limit.argtypes = [ctypes.c_int]
+    lib.wkv_poll_limit.restype = ctypes.c_int
+    lib.wkv_poll_limit.argtypes = []
     lib.wkv_status_string.restype = ctypes.c_char_p
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_last_error.restype = ctypes.c_char_p
@@ -119,6 +124,16 @@ def _status_name(status: int) -> str:
 def _check(status: int):
     if status != WKV_OK:
         raise WKVError(status, load_library().wkv_last_error().decode())
+
+
+def set_poll_limit(tries: int) -> int:
+    """Set how many times a look-back re-reads an unpublished window's flag before it
+    recomputes that window itself (results are bitwise the same either way); returns the
+    previous setting."""
+    lib = load_library()
+    old = lib.wkv_poll_limit()
+    _check(lib.wkv_set_poll_limit(int(tries)))
+    return old
 
 
 def _ptr(t):

@@ -181,8 +181,10 @@ std::once_flag g_epoch_once;
 uint64_t next_epoch() {
     std::call_once(g_epoch_once, [] {
         std::random_device rd;
-        const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
-        const uint64_t seed = (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull));
+        const uint64_t t =
+            (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+        const uint64_t seed =
+            (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull));
         g_epoch.store(seed & ((uint64_t(1) << 60) - 1));
     });
     return (g_epoch.fetch_add(1) + 1) & ((uint64_t(1) << 61) - 1);
@@ -219,9 +221,26 @@ bool bwd_grid_ok(int64_t B, int64_t T, int64_t C, const char *fn) {
 
 }  // namespace
 
+namespace wkvdev {
+
+static std::atomic<int> g_poll_limit{kPollTries};
+
+int poll_limit() { return g_poll_limit.load(std::memory_order_relaxed); }
+
+}  // namespace wkvdev
+
 extern "C" {
 
 int wkv_version(void) { return 100; }  // 0.1.0
+
+int wkv_set_poll_limit(int tries) {
+    g_err[0] = '\0';
+    if (tries < 0) return fail(WKV_ERR_INVALID_ARG, "wkv_set_poll_limit: negative count %d", tries);
+    wkvdev::g_poll_limit.store(tries, std::memory_order_relaxed);
+    return WKV_OK;
+}
+
+int wkv_poll_limit(void) { return wkvdev::poll_limit(); }
 
 const char *wkv_status_string(int status) {
     switch (status) {

@@ -97,25 +97,33 @@ __device__ __forceinline__ RevCarry get_rrec(const double *p, int64_t n, int64_t
 // fixed frame would under- or overflow (a dominant key next to much smaller ones, extreme
 // u). Everything is fp64 with library exponentials. It reads k, v, dy straight from
 // memory in loops that are not unrolled (per-token values of the forward sweep go to
-// private arrays), so that this rare path holds few registers wherever it is inlined. `fin` is the forward carry
-// entering the chunk, `rin` the future sums at the chunk's nominal end (CH tokens on).
-// The forward sweep adds the chunk's dw, du terms if FG; the reverse sweep stores dk, dv
-// if OUT. With `r` the cotangent is gated (dy = dout sigma(r), dout read from `dy`), and
-// with `dr` the forward sweep also stores dr = dout sigma(r) (1 - sigma(r)) y. Returns the
-// future sums at the chunk start.
+// private arrays), so that this rare path holds few registers of its own. `fin` is the
+// forward carry entering the chunk, `rin` the future sums at the chunk's nominal end (CH
+// tokens on). The forward sweep sums the chunk's dw, du terms if FG; the reverse sweep
+// stores dk, dv if OUT. With `r` the cotangent is gated (dy = dout sigma(r), dout read from
+// `dy`), and with `dr` the forward sweep also stores dr = dout sigma(r) (1 - sigma(r)) y.
+// Returns the future sums at the chunk start and the dw, du terms.
 // ---------------------------------------------------------------------------------
 struct RevState64 {  // (G, H) = (g, h) e^{r - ref}
     double g, h, r;
 };
 
+// What exact_chunk returns: the future sums at the chunk start and (FG) the chunk's du, dw
+// terms. (Results are returned, not written through references, so that the function needs
+// no stack object when it is not inlined.)
+struct ExactResult {
+    RevCarry fut;
+    double du, dw;
+};
+
 template <int CH, bool OUT, bool FG, Io IO>
-__device__ __forceinline__ RevCarry exact_chunk(
+__device__ __noinline__ ExactResult exact_chunk(
     const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
     const io_t<IO> *__restrict__ dy, io_t<IO> *__restrict__ dk, io_t<IO> *__restrict__ dv,
     int64_t row0, int64_t t0, int Lv,
-    int64_t C, int cl, bool st_ok, float ref, const Carry &fin, RevCarry rin, float uc,
-    float wc, double &du_acc, double &dw_acc, const io_t<IO> *__restrict__ r = nullptr,
-    io_t<IO> *__restrict__ dr = nullptr) {
+    int64_t C, int cl, bool st_ok, float ref, const Carry fin, RevCarry rin, float uc,
+    float wc, const io_t<IO> *__restrict__ r = nullptr, io_t<IO> *__restrict__ dr = nullptr) {
+    double du_acc = 0.0, dw_acc = 0.0;
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;  // the frame 2^{ref2} the carries refer to
     // the carries are relative to 2^{ref2}; the per-token path works relative to e^{ref}
@@ -173,7 +181,7 @@ __device__ __forceinline__ RevCarry exact_chunk(
         rs.r = rn;
     }
     // G = g e^{r - ref} at the chunk start
-    return RevCarry{rs.g, rs.h, (rs.r - refd) * kLog2eD};
+    return ExactResult{RevCarry{rs.g, rs.h, (rs.r - refd) * kLog2eD}, du_acc, dw_acc};
 }
 
 // LDS of a backward unit: staging for the window's reverse summaries and the dw/du
@@ -191,13 +199,32 @@ struct BwdShared {
 
 // Per-channel constants of a backward lane.
 struct BwdConst {
-    double w;        // the decay rate
     double dwf;      // e^{-w}
     double eu;       // e^{u}
-    double w2;       // w log2 e
+    float wc;        // the decay rate
     float uc;
     bool slow_wave;  // some lane has |u| > 60: exact path throughout
+    // w log2 e, recomputed where used (the asm keeps it from being held across the kernel)
+    __device__ __forceinline__ double w2() const {
+        float x = wc;
+        asm volatile("" : "+v"(x));
+        return (double)x * kLog2eD;
+    }
 };
+
+// Register budget. The plain backward runs at three waves per SIMD (at most 168 VGPRs; its
+// hot path needs ~162), which only holds if the chunk's 96 registers (kc, vc, gc) are not
+// also live inside the rare paths: the per-token path and the look-back's recomputation of
+// another window are functions that are not inlined (their stack and registers are touched
+// only when they run), and after either the chunk's registers are redefined here, so that
+// the compiler sees their old values die before the call. A chunk that took the per-token
+// path takes it for dk, dv too; a look-back that recomputed a window reloads and recomputes
+// the unit's own chunk afterwards (bitwise the same).
+template <int CH>
+__device__ __forceinline__ void kill_chunk(float (&kc)[CH], float (&vc)[CH], float (&gc)[CH]) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) kc[j] = vc[j] = gc[j] = 0.0f;
+}
 
 // One lane's chunk ci (tokens t0 = ci*CH ...): the forward recomputation from the chunk's
 // entering carry (read from the forward's workspace) and, in the same sweep, the chunk's
@@ -248,19 +275,19 @@ __device__ __forceinline__ RevCarry chunk_pass(
             Pz = fin.bp * s0 / K.dwf;
         }
         double pw = 1.0;
-        double dmin = __builtin_inf();
+        bool tiny = false;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             // padded tokens (k = -inf, v = dy = 0) contribute e = sigma = 0; the clamp on den
             // keeps 1/den finite where a padded token's den (the decayed carry alone) falls
-            // below the fp32 range, so that its sigma is 0 and not NaN. Their den enters dmin
-            // too: at worst a ragged last chunk takes the per-token path.
+            // below the fp32 range, so that its sigma is 0 and not NaN. Their den enters the
+            // test too: at worst a ragged last chunk takes the per-token path.
             const double e = exp2_64(fma((double)kc[j], kLog2eD, -ref2));
             const double vv = (double)vc[j];
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            dmin = fmin(dmin, den);
+            tiny = tiny || !(den >= (double)kTinyDen);
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
             double gd = (double)gc[j];
@@ -289,7 +316,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
         }
         dw_acc *= K.dwf;
         du_acc *= K.eu;
-        fx = wave_any(!(dmin >= (double)kTinyDen));
+        fx = wave_any(tiny);
     }
     if (!fx) {
         if constexpr (GATE) {
@@ -302,24 +329,25 @@ __device__ __forceinline__ RevCarry chunk_pass(
         }
         return RevCarry{R, Q, -ref2};
     }
-    du_acc = 0.0;
-    dw_acc = 0.0;
-    return exact_chunk<CH, false, true, IO>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false,
-                                       ref, fin, rev_zero(), K.uc, (float)K.w, du_acc, dw_acc,
-                                       GATE ? rgate : nullptr, GATE && cval ? dr : nullptr);
+    const ExactResult xr = exact_chunk<CH, false, true, IO>(
+        k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false, ref, fin, rev_zero(), K.uc,
+        K.wc, GATE ? rgate : nullptr, GATE && cval ? dr : nullptr);
+    du_acc = xr.du;
+    dw_acc = xr.dw;
+    kill_chunk<CH>(kc, vc, gc);
+    return xr.fut;
 }
 
 // Reverse summary of another unit's chunk, for the look-back's recomputation of a window
 // whose aggregate was not published in time: the summary arithmetic of chunk_pass, op
-// for op and in the same order (so the bits are those the owner publishes), but streaming
-// k, v, dy from memory in a loop that is not unrolled, so that the unit's own chunk stays
-// in registers across the look-back.
+// for op and in the same order, the per-token-path decision included (so the bits are those
+// the owner publishes), streaming k, v, dy from memory in a loop that is not unrolled.
 template <int CH, Io IO>
-__device__ __forceinline__ RevCarry helper_summary(
-    int64_t ci, int64_t T, int64_t C, const FwdCarries &F, int64_t bidx, int64_t row0,
+__device__ __noinline__ RevCarry helper_summary(
+    int64_t ci, int64_t T, int64_t C, const FwdCarries F, int64_t bidx, int64_t row0,
     int cl, const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
     const io_t<IO> *__restrict__ dy, const io_t<IO> *__restrict__ rg,
-    const BwdConst &K) {
+    const BwdConst K) {
     const int64_t t0 = ci * CH;
     const int Lv = chunk_len(t0, T, CH);
     if (Lv == 0) return rev_zero();
@@ -338,7 +366,7 @@ __device__ __forceinline__ RevCarry helper_summary(
         const double s0 = exp2_64(gap);
         double Sx = fin.a * s0, Zx = fin.b * s0;
         double pw = 1.0, R = 0.0, Q = 0.0;
-        double dmin = __builtin_inf();
+        bool tiny = false;
 #pragma unroll 1
         for (int j = 0; j < CH; ++j) {
             const bool in = j < Lv;
@@ -348,7 +376,7 @@ __device__ __forceinline__ RevCarry helper_summary(
             const double ev = e * vv;
             const double num = fma(K.eu, ev, Sx);
             const double den = fma(K.eu, e, Zx);
-            dmin = in ? fmin(dmin, den) : dmin;
+            tiny = tiny || !(den >= (double)kTinyDen);  // padded tokens too, as the owner
             const double r = rcpd(fmax(den, 0x1p-120));
             const double yv = num * r;
             double g = in ? (double)io_ld<IO>(gp, (int64_t)j * C) : 0.0;
@@ -361,13 +389,12 @@ __device__ __forceinline__ RevCarry helper_summary(
             Sx = fma(Sx, K.dwf, ev);
             Zx = fma(Zx, K.dwf, e);
         }
-        fx = wave_any(!(dmin >= (double)kTinyDen));
+        fx = wave_any(tiny);
         if (!fx) return RevCarry{R, Q, -ref2};
     }
-    double du, dw;
     return exact_chunk<CH, false, false, IO>(k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl,
-                                             false, ref, fin, rev_zero(), K.uc, (float)K.w, du,
-                                             dw, rg);
+                                             false, ref, fin, rev_zero(), K.uc, K.wc, rg)
+        .fut;
 }
 
 // Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
@@ -392,11 +419,13 @@ __device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const Rev
 }
 
 // GATE: the output was sigma(r) * y; `dy` holds the cotangent of that gated output, and dr
-// is written too. IO: the storage format of k, v, dy, r, dk, dv and dr.
+// is written too (r's chunk takes 32 more registers: two waves per SIMD). IO: the storage
+// format of k, v, dy, r, dk, dv and dr. `tries`: polls before a missing window is
+// recomputed.
 template <int NW, int CH, bool GATE, Io IO>
-__global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
+__global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
     int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg,
-    uint64_t epoch, const float *__restrict__ w, const float *__restrict__ u,
+    uint64_t epoch, int tries, const float *__restrict__ w, const float *__restrict__ u,
     const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
     const io_t<IO> *__restrict__ dy, const io_t<IO> *__restrict__ r, const FwdCarries F,
     io_t<IO> *__restrict__ dk, io_t<IO> *__restrict__ dv, io_t<IO> *__restrict__ dr,
@@ -423,10 +452,9 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     const float wc = w[cl];
     BwdConst K;
     K.uc = u[cl];
-    K.w = (double)wc;
-    K.dwf = exp(-K.w);
+    K.wc = wc;
+    K.dwf = exp(-(double)wc);
     K.eu = exp((double)K.uc);
-    K.w2 = K.w * kLog2eD;
     K.slow_wave = wave_any(!(fabsf(K.uc) <= 60.0f));
     const int64_t row0 = bidx * T;
     const int64_t ci = s * NW + q;
@@ -444,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     sh.pu[q][lane] = du_acc;
     sh.pw[q][lane] = dw_acc;
     RevCarry agg, lfut;
-    window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2, agg, lfut);
+    window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2(), agg, lfut);
     const int64_t rec = (bidx * nseg + s) * C + cl;
     const int64_t nrec = B * nseg * C;
     uint64_t *myflag = flags + sidx * nbg + bg;
@@ -476,13 +504,14 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
     if (s < nseg - 1) {
         int64_t j = s + 1;
         int it = 0;
+        bool redo = false;
         for (;;) {
             if (q == 0) {
                 int st = it == 0 ? flag_status(next, epoch) : 0;
                 if (st != 0)
                     consume_fence();
                 else
-                    st = poll_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kPollTries);
+                    st = poll_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, tries);
                 if (lane == 0) sh.status[it & 1] = st;
             }
             __syncthreads();
@@ -495,11 +524,15 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
                 const RevCarry rs_j = helper_summary<CH, IO>(j * NW + q, T, C, F, bidx, row0, cl,
                                                          k, v, dy, GATE ? r : nullptr, K);
                 RevCarry agg_j, lf_j;
-                window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2, agg_j, lf_j);
+                window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2(), agg_j, lf_j);
                 if (q == 0) {
                     if (cval) put_rrec(ragg, nrec, (bidx * nseg + j) * C + cl, agg_j);
                     raise_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kAggregate);
                 }
+                // the unit's own chunk and window fold are redone after the walk
+                kill_chunk<CH>(kc, vc, gc);
+                agg = lfut = rev_zero();
+                redo = true;
             }
             if (j == nseg - 1) {
                 j = nseg;
@@ -507,17 +540,24 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
             }
             ++j;
         }
+        if (redo) {  // the same for every wave of the unit (the status is shared)
+            double du_x, dw_x;
+            const RevCarry rs2 = chunk_pass<CH, GATE, IO>(ci, T, C, F, bidx, row0, cl, cval, voff,
+                                                          stride, r, dr, k, v, dy, K, kc, vc, gc,
+                                                          sh.sy[q], lane, fx, ref, Lv, du_x, dw_x);
+            window_rev_fold<NW, CH>(sh, rs2, q, lane, K.w2(), agg, lfut);
+        }
         if (j < nseg) fut = get_rrec(rincl, nrec, (bidx * nseg + j) * C + cl);
         for (int64_t m = j - 1; m > s; --m)
             fut = rfollow(fut, get_rrec(ragg, nrec, (bidx * nseg + m) * C + cl),
-                          (double)WIN * K.w2);
+                          (double)WIN * K.w2());
     }
-    if (q == 0 && cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2));
+    if (q == 0 && cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2()));
 
     // ---- R3: dk, dv of this chunk ----
     const rsrc_t rdk = make_rsrc(dk + (row0 + (t0 < T ? t0 : 0)) * C);
     const rsrc_t rdv = make_rsrc(dv + (row0 + (t0 < T ? t0 : 0)) * C);
-    RevCarry rc = rfollow(fut, lfut, (double)((NW - 1 - q) * CH) * K.w2);
+    RevCarry rc = rfollow(fut, lfut, (double)((NW - 1 - q) * CH) * K.w2());
     rnormalize(rc);
     const double rgap = (double)ref * kLog2eD + rc.r;
     const bool rx = fx || wave_any(rgap > (double)kCarryGap);
@@ -556,9 +596,8 @@ __global__ __launch_bounds__(NW * 64, 2) void wkv_backward_kernel(
         }
     } else {
         const Carry fin = chunk_carry(F, bidx, ci, C, cl);
-        double d0 = 0.0, d1 = 0.0;
         exact_chunk<CH, true, false, IO>(k, v, dy, dk, dv, row0, t0, Lv, C, cl, cval, ref, fin, rc,
-                                     K.uc, wc, d0, d1, GATE ? r : nullptr);
+                                         K.uc, wc, GATE ? r : nullptr);
     }
 }
 
@@ -635,13 +674,13 @@ static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int
     if (r != nullptr)
         hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, true, IO>),
                            dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, kk, vv, gg, rr, fc, ddk, ddv, ddr, dw, du,
-                           L.flags, L.ragg, L.rincl, L.part);
+                           nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, gg, rr, fc, ddk, ddv,
+                           ddr, dw, du, L.flags, L.ragg, L.rincl, L.part);
     else
         hipLaunchKernelGGL((wkv_backward_kernel<kBwdWaves, kCinChunk, false, IO>),
                            dim3((unsigned)units), dim3(kBwdWaves * 64), 0, stream, B, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, kk, vv, gg, rr, fc, ddk, ddv, ddr, dw, du,
-                           L.flags, L.ragg, L.rincl, L.part);
+                           nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, gg, rr, fc, ddk, ddv,
+                           ddr, dw, du, L.flags, L.ragg, L.rincl, L.part);
 }
 
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,

@@ -213,7 +213,7 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
 // v, r and y.
 template <int NW, int CH, bool GATE, Io F>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
-    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch,
+    int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch, int tries,
     const float *__restrict__ w, const float *__restrict__ u, const io_t<F> *__restrict__ k,
     const io_t<F> *__restrict__ v, const io_t<F> *__restrict__ r, io_t<F> *__restrict__ y,
     uint64_t *__restrict__ flags,
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             int it = 0;
             for (;;) {
                 if (q == 0) {
-                    const int st = poll_flag(flags + j * nbg + bg, epoch, kPollTries);
+                    const int st = poll_flag(flags + j * nbg + bg, epoch, tries);
                     if (lane == 0) sh.status[it & 1] = st;
                 }
                 __syncthreads();
@@ -438,13 +438,13 @@ static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int6
     if (r != nullptr)
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, kk, vv, rr, yy, L.flags, L.agg, L.incl,
-                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+                           nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
     else
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
-                           nbg, L.nseg, epoch, w, u, kk, vv, rr, yy, L.flags, L.agg, L.incl,
-                           B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+                           nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
 }
 
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,

@@ -29,6 +29,10 @@ constexpr uint64_t kAggregate = 1;
 constexpr uint64_t kInclusive = 2;
 constexpr int kPollTries = 2000;  // bounded wait before a missing aggregate is recomputed
 
+// The polls of a predecessor's flag a look-back makes before it recomputes that window's
+// aggregate itself (kPollTries unless changed through wkv_set_poll_limit).
+int poll_limit();
+
 // Published carries and summaries are stored one fp64 array per field (field f of
 // record i at f * n + i, n records), so that a wave's 64 channels write and read 512
 // contiguous bytes per field. A forward record has the fields (a, b, a', b', P):

@@ -31,6 +31,19 @@ def test_every_declared_symbol_is_exported(pkg):
         assert hasattr(lib, name), name
 
 
+def test_poll_limit_setting(pkg):
+    lib = pkg.load_library()
+    assert lib.wkv_poll_limit() == 2000
+    assert lib.wkv_set_poll_limit(-1) == pkg.WKV_ERR_INVALID_ARG
+    assert b"negative" in lib.wkv_last_error()
+    assert pkg.set_poll_limit(0) == 2000
+    assert lib.wkv_poll_limit() == 0
+    assert pkg.set_poll_limit(2000) == 0
+    with pytest.raises(pkg.WKVError):
+        pkg.set_poll_limit(-5)
+    assert lib.wkv_poll_limit() == 2000
+
+
 def test_status_strings_and_version(pkg):
     lib = pkg.load_library()
     assert lib.wkv_version() >= 100
