@@ -35,6 +35,9 @@ Helpers for the counter summaries:
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
         reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` output folders of a
         `--with-copy` run and prints the summary JSON (per-dispatch KiB, copy scaling).
+    python bench.py --summarize-trace TRACE_DIR [--warmup W --steps K]
+        prints the step's kernel durations from a `rocprofv3 --kernel-trace` folder of a run
+        with the same W and K (all dispatches, and the timed ones alone).
 """
 from __future__ import annotations
 
@@ -56,7 +59,11 @@ METRIC = ("WKV fwd+bwd elements/sec (B·T·C) and achieved HBM GB/s vs peak, "
           "T=4096 C=2560")
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30
-KERNELS = {"forward": "wkv_forward_kernel", "backward": "wkv_backward_kernel"}
+# The step's kernels as rocprofv3 names them (the fp32, ungated instances; the other legs run
+# other instances, or come after the step's dispatches).
+KERNELS = {"forward": "wkv_forward_kernel<2, 32, false, (wkvdev::Io)0>",
+           "backward": "wkv_backward_kernel<2, 32, false, (wkvdev::Io)0>"}
+REDUCE_KERNEL = "wkv_reduce_kernel"
 BYTES_PER_ELEM = {"forward": 12, "backward": 20}
 
 
@@ -140,6 +147,44 @@ def counter_traffic(op):
         return None
     k = rec.get("kernels", {}).get(op)
     return None if k is None else k["traffic_bytes"]
+
+
+def summarize_trace(folder, warmup, steps):
+    """Markdown table of the step's kernel durations from a `rocprofv3 --kernel-trace` folder
+    of a bench.py run with the same --warmup and --steps: every dispatch of each kernel, and
+    the timed ones alone (the step runs first, so they are dispatches warmup .. warmup+steps-1
+    of each of its kernels, in launch order)."""
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit("no *kernel_trace.csv under %s" % folder)
+    import wkv_inputs
+    wl = wkv_inputs.WORKLOADS["l3b"]
+    n = wl["B"] * wl["T"] * wl["C"]
+    lines = ["| kernel | dispatches | mean us (all) | timed dispatches | mean us (timed) | "
+             "min us (timed) | max us (timed) | algorithmic GB/s (timed mean) |",
+             "|---|---|---|---|---|---|---|---|"]
+    timed_sum = 0.0
+    for op, needle in (("forward", KERNELS["forward"]), ("backward", KERNELS["backward"]),
+                       ("reduce", REDUCE_KERNEL)):
+        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                   if needle in r["Kernel_Name"])
+        if not d:
+            continue
+        us = [(e - s0) / 1e3 for s0, e in d]
+        tw = us[warmup:warmup + steps]
+        if op != "forward":
+            timed_sum += statistics.mean(tw)
+        gbs = ("%.0f" % (BYTES_PER_ELEM[op] * n / (statistics.mean(tw) * 1e-6) / 1e9)
+               if op in BYTES_PER_ELEM else "-")
+        lines.append("| `%s` | %d | %.1f | %d | %.1f | %.1f | %.1f | %s |" % (
+            needle, len(us), statistics.mean(us), len(tw), statistics.mean(tw), min(tw),
+            max(tw), gbs))
+    lines.append("")
+    lines.append("backward call (backward kernel + reduce kernel), timed means: %.1f us" % timed_sum)
+    return "\n".join(lines)
 
 
 # ---------------------------------------------------------------------------------------
@@ -439,8 +484,14 @@ def main(argv=None):
     ap.add_argument("--with-copy", action="store_true",
                     help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the step's kernel durations from a rocprofv3 --kernel-trace "
+                         "folder of a run with the same --warmup/--steps")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
+        return
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
         return 0

@@ -194,6 +194,7 @@ struct BwdShared {
     double r[NW][64];
     double pu[NW][64], pw[NW][64];  // each wave's du, dw terms
     float sy[NW][CH][64];
+    float ref[NW][64];  // each lane's chunk frame, kept here across the look-back
     int status[2];
 };
 
@@ -397,18 +398,24 @@ __device__ __noinline__ RevCarry helper_summary(
         .fut;
 }
 
-// Stage this wave's chunk reverse summary and fold the window's NW summaries (last chunk
-// first) from a zero future: `agg` is the window's reverse aggregate, `lfut` the part of it
-// that lies after this wave's chunk. Contains barriers (all waves call it together).
+// Stage this wave's chunk reverse summary for window_rev_sums. Contains barriers (all waves
+// call it together).
 template <int NW, int CH>
-__device__ __forceinline__ void window_rev_fold(BwdShared<NW, CH> &sh, const RevCarry &rsum, int q,
-                                                int lane, double w2, RevCarry &agg,
-                                                RevCarry &lfut) {
+__device__ __forceinline__ void window_rev_stage(BwdShared<NW, CH> &sh, const RevCarry &rsum,
+                                                 int q, int lane) {
     __syncthreads();
     sh.a[q][lane] = rsum.g;
     sh.b[q][lane] = rsum.h;
     sh.r[q][lane] = rsum.r;
     __syncthreads();
+}
+
+// Fold the window's NW staged summaries (last chunk first) from a zero future: `agg` is the
+// window's reverse aggregate, `lfut` the part of it that lies after this wave's chunk. (Cheap
+// enough to redo from the staged values rather than hold 12 registers across the look-back.)
+template <int NW, int CH>
+__device__ __forceinline__ void window_rev_sums(const BwdShared<NW, CH> &sh, int q, int lane,
+                                                double w2, RevCarry &agg, RevCarry &lfut) {
     agg = rev_zero();
     lfut = agg;
 #pragma unroll
@@ -468,12 +475,12 @@ __global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
     RevCarry rsum = chunk_pass<CH, GATE, IO>(ci, T, C, F, bidx, row0, cl, cval, voff, stride, r,
                                          dr, k, v, dy, K, kc, vc, gc, sh.sy[q], lane, fx, ref,
                                          Lv, du_acc, dw_acc);
-    // the dw, du terms are staged with the reverse summaries (the fold's barrier covers both)
+    // the dw, du terms and the frame are staged with the reverse summaries (the fold's
+    // barrier covers them)
     sh.pu[q][lane] = du_acc;
     sh.pw[q][lane] = dw_acc;
-    RevCarry agg, lfut;
-    window_rev_fold<NW, CH>(sh, rsum, q, lane, K.w2(), agg, lfut);
-    const int64_t rec = (bidx * nseg + s) * C + cl;
+    sh.ref[q][lane] = ref;
+    window_rev_stage<NW, CH>(sh, rsum, q, lane);
     const int64_t nrec = B * nseg * C;
     uint64_t *myflag = flags + sidx * nbg + bg;
     // the next window's flag is read before this unit's flag store, so that one wait
@@ -481,6 +488,9 @@ __global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
     uint64_t next = 0;
     if (q == 0) {
         if (cval) {
+            const int64_t rec = (bidx * nseg + s) * C + cl;
+            RevCarry agg, lf;
+            window_rev_sums<NW, CH>(sh, q, lane, K.w2(), agg, lf);
             put_rrec(ragg, nrec, rec, agg);
             // this window's dw, du partial: its chunks' terms summed in a fixed order
             double su = 0.0, sw = 0.0;
@@ -524,14 +534,14 @@ __global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
                 const RevCarry rs_j = helper_summary<CH, IO>(j * NW + q, T, C, F, bidx, row0, cl,
                                                          k, v, dy, GATE ? r : nullptr, K);
                 RevCarry agg_j, lf_j;
-                window_rev_fold<NW, CH>(sh, rs_j, q, lane, K.w2(), agg_j, lf_j);
+                window_rev_stage<NW, CH>(sh, rs_j, q, lane);
+                window_rev_sums<NW, CH>(sh, q, lane, K.w2(), agg_j, lf_j);
                 if (q == 0) {
                     if (cval) put_rrec(ragg, nrec, (bidx * nseg + j) * C + cl, agg_j);
                     raise_flag(flags + (nseg - 1 - j) * nbg + bg, epoch, kAggregate);
                 }
-                // the unit's own chunk and window fold are redone after the walk
+                // the unit's own chunk and staged summaries are redone after the walk
                 kill_chunk<CH>(kc, vc, gc);
-                agg = lfut = rev_zero();
                 redo = true;
             }
             if (j == nseg - 1) {
@@ -542,23 +552,29 @@ __global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
         }
         if (redo) {  // the same for every wave of the unit (the status is shared)
             double du_x, dw_x;
+            float ref_x;
             const RevCarry rs2 = chunk_pass<CH, GATE, IO>(ci, T, C, F, bidx, row0, cl, cval, voff,
                                                           stride, r, dr, k, v, dy, K, kc, vc, gc,
-                                                          sh.sy[q], lane, fx, ref, Lv, du_x, dw_x);
-            window_rev_fold<NW, CH>(sh, rs2, q, lane, K.w2(), agg, lfut);
+                                                          sh.sy[q], lane, fx, ref_x, Lv, du_x,
+                                                          dw_x);
+            window_rev_stage<NW, CH>(sh, rs2, q, lane);
         }
         if (j < nseg) fut = get_rrec(rincl, nrec, (bidx * nseg + j) * C + cl);
         for (int64_t m = j - 1; m > s; --m)
             fut = rfollow(fut, get_rrec(ragg, nrec, (bidx * nseg + m) * C + cl),
                           (double)WIN * K.w2());
     }
-    if (q == 0 && cval) put_rrec(rincl, nrec, rec, rfollow(fut, agg, (double)WIN * K.w2()));
+    RevCarry agg, lfut;
+    window_rev_sums<NW, CH>(sh, q, lane, K.w2(), agg, lfut);
+    if (q == 0 && cval)
+        put_rrec(rincl, nrec, (bidx * nseg + s) * C + cl, rfollow(fut, agg, (double)WIN * K.w2()));
 
     // ---- R3: dk, dv of this chunk ----
     const rsrc_t rdk = make_rsrc(dk + (row0 + (t0 < T ? t0 : 0)) * C);
     const rsrc_t rdv = make_rsrc(dv + (row0 + (t0 < T ? t0 : 0)) * C);
     RevCarry rc = rfollow(fut, lfut, (double)((NW - 1 - q) * CH) * K.w2());
     rnormalize(rc);
+    ref = sh.ref[q][lane];
     const double rgap = (double)ref * kLog2eD + rc.r;
     const bool rx = fx || wave_any(rgap > (double)kCarryGap);
     // The sweep's arithmetic runs before wave 0 stores the inclusive flag, so that the wait
