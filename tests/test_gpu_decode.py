@@ -135,11 +135,11 @@ def _decode_inputs(torch, dev, B, C, seed):
 
 
 def test_decode_grid_stride_pass(wkv, dev):
-    # B*C past 2^28 elements: the launch caps its grid and lanes loop; the result is bitwise
+    # B*C past 2^29 elements: the launch caps its grid and lanes loop; the result is bitwise
     # that of the same rows decoded in two calls of one pass each
     import torch
-    B, C = 65600, 4099
-    assert B * C > (1 << 28)
+    B, C = 131200, 4099
+    assert B * C > (1 << 29)
     w, u, k, v, a, b, p = _decode_inputs(torch, dev, B, C, 32)
     st = [t.clone() for t in (a, b, p)]
     y = wkv.decode_step(w, u, k, v, *st)
