@@ -67,10 +67,16 @@ REDUCE_KERNEL = "wkv_reduce_kernel"
 BYTES_PER_ELEM = {"forward": 12, "backward": 20}
 
 
+# Sources the forward and backward kernels (and their workspace layout) are built from; the
+# decode and token-shift kernels do not change their traffic.
+TRAFFIC_SOURCES = ("wkv_api.hip", "wkv_backward.hip", "wkv_chunk.h", "wkv_device.h",
+                   "wkv_forward.hip", "wkv_launch.h")
+
+
 def source_hash() -> str:
-    """sha256 over the kernel sources (csrc/*.hip, *.h), in name order."""
+    """sha256 over the sources of the forward and backward kernels, in name order."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+    for path in sorted(os.path.join(CSRC, f) for f in TRAFFIC_SOURCES):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
