@@ -327,29 +327,42 @@ def bench_decode(wkv, torch, dev, steps=20, warmup=3):
 def bench_forward_state(wkv, torch, dev, x, steps=100, warmup=100):
     """The forward from a state on the benchmark layer (prompt prefill), back to back as the
     step is timed: each call starts from the state the previous one left (random at first)
-    and leaves y and the final state; 12 B per element plus 24 B of state per (b, c)."""
+    and leaves y and the final state; 12 B per element plus 24 B of state per (b, c). Timed
+    for the training entry point (wkv_forward_state, whose workspace serves a backward) and
+    for the inference one (wkv_forward_infer, which keeps no states for a backward)."""
     import wkv_inputs
     t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v")}
     B, T, C = t["k"].shape
     st = [torch.from_numpy(a).to(dev) for a in wkv_inputs.random_state(B, C, seed=1006)]
     ws = wkv.forward_workspace(B, T, C, dev)
     y = torch.empty_like(t["k"])
-    for _ in range(warmup):
-        wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws, out=y)
-    torch.cuda.synchronize(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for e0, e1 in evs:
-        e0.record()
-        wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws, out=y)
-        e1.record()
-    torch.cuda.synchronize(dev)
-    us = statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize(dev)
+        return statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+
+    us = timed(lambda: wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws,
+                                         out=y))
+    us_inf = timed(lambda: wkv.forward_infer(t["w"], t["u"], t["k"], t["v"], state=st,
+                                             workspace=ws, out=y))
     ok = bool(torch.isfinite(y).all()) and all(bool(torch.isfinite(a).all()) for a in st)
-    gbps = (12 * B * T * C + 24 * B * C) / (us * 1e-6) / 1e9
+    alg = 12 * B * T * C + 24 * B * C
+    gbps = alg / (us * 1e-6) / 1e9
+    gbps_inf = alg / (us_inf * 1e-6) / 1e9
     return {"workload": "forward from a state, B=%d T=%d C=%d" % (B, T, C),
             "us": us, "elem_per_s": B * T * C / (us * 1e-6), "algorithmic_gbps": gbps,
-            "frac_of_peak": gbps / PEAK_GBPS, "steps": steps, "outputs_finite": ok}
+            "frac_of_peak": gbps / PEAK_GBPS, "infer_us": us_inf,
+            "infer_elem_per_s": B * T * C / (us_inf * 1e-6),
+            "infer_frac_of_peak": gbps_inf / PEAK_GBPS, "steps": steps, "outputs_finite": ok}
 
 
 def bench_gated(wkv, torch, dev, x, steps=100, warmup=100):

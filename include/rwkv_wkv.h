@@ -125,6 +125,21 @@ int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w
                       const float *u, const void *k, const void *v, const void *r, void *y,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* The forward for inference, where no backward follows: wkv_forward_typed (r == NULL) or
+ * its gated form (r != NULL), from a given state if a, b, p are given (all three, as in
+ * wkv_forward_state, overwritten with the state after token T-1) or from the empty state if
+ * all three are NULL. Outputs and final state are bitwise those of the training entry
+ * points; the workspace (wkv_forward_workspace_size bytes) is left without the states a
+ * backward reads (their age-weighted sums are never formed and the carries entering the
+ * windows' second chunks and token 0 are not stored), so it must not be passed to
+ * wkv_backward. This is the prompt prefill of "RWKV についての調査記録", section
+ * "コードを見ながらRWKVの構造を把握" (the prompt's tokens update the state in order) run in
+ * parallel, with 1.1 bytes per element less workspace traffic than wkv_forward_state. */
+int wkv_forward_infer(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                      const float *u, const void *k, const void *v, const void *r, void *y,
+                      float *a, float *b, float *p, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* Bytes of device scratch that wkv_backward and wkv_backward_gated need. With have_fwd_workspace != 0 the caller
  * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
  * window states are recomputed into this workspace, which then also covers

@@ -40,6 +40,7 @@ WKV_ERR_HIP = 3
 EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_string",
            "wkv_last_error", "wkv_forward_workspace_size",
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
+           "wkv_forward_infer",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
            "wkv_backward_typed", "wkv_decode_step", "wkv_token_shift",
            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
@@ -79,6 +80,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_typed.restype = ctypes.c_int
     lib.wkv_forward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
+    lib.wkv_forward_infer.restype = ctypes.c_int
+    lib.wkv_forward_infer.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_backward_typed.restype = ctypes.c_int
     lib.wkv_backward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -309,6 +313,40 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
     preallocated (dk, dv, dw, du). k, v, dy (and dk, dv) share one of float32, bfloat16,
     float16; w, u, dw, du are float32."""
     return _backward_common(w, u, k, v, dy, None, fwd_workspace, workspace, out)
+
+
+def forward_infer(w, u, k, v, r=None, state=None, workspace=None, out=None):
+    """The forward for inference (no backward follows): y, or sigma(r) * y with r, from the
+    empty state or from `state` = (a, b, p) [B, C] float32, which is overwritten with the
+    state after the last token. k, v, r, out share one of float32, bfloat16, float16. The
+    results equal forward() / forward_gated() / forward_state(); the workspace keeps no
+    states for backward()."""
+    B, T, C, dev = _check_btc(w, u, k, v, typed=True)
+    if r is not None:
+        _need(r, "r", 3, dev, dtype=k.dtype)
+        if r.shape != k.shape:
+            raise ValueError("r has the wrong shape")
+    st = (None, None, None)
+    if state is not None:
+        st = tuple(state)
+        if len(st) != 3:
+            raise ValueError("state must be (a, b, p)")
+        for t, n in zip(st, ("a", "b", "p")):
+            _need(t, n, 2, dev)
+            if tuple(t.shape) != (B, C):
+                raise ValueError("%s must have shape %s, got %s" % (n, (B, C), tuple(t.shape)))
+    y = torch.empty_like(k) if out is None else out
+    _need(y, "out", 3, dev, dtype=k.dtype)
+    if y.shape != k.shape:
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = forward_workspace(B, T, C, dev)
+    _check_ws(workspace, dev, "workspace")
+    _check(load_library().wkv_forward_infer(_DTYPE_CODE[k.dtype], B, T, C, _ptr(w), _ptr(u),
+                                            _ptr(k), _ptr(v), _ptr(r), _ptr(y), _ptr(st[0]),
+                                            _ptr(st[1]), _ptr(st[2]), _ptr(workspace),
+                                            workspace.numel(), _stream(dev)))
+    return y
 
 
 def forward_gated(w, u, k, v, r, workspace=None, out=None):

@@ -269,7 +269,7 @@ namespace {
 int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt,
                  const float *w, const float *u, const void *k, const void *v, const void *r,
                  void *y, float *sa, float *sb, float *sp, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+                 size_t workspace_bytes, void *stream, bool keep = true) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
@@ -319,7 +319,7 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
     hipError_t e = wkvdev::launch_forward(B, T, C, fmt, w, u, k, v, r, y, sa, sb, sp,
-                                          fwd_layout(B, T, C, workspace), next_epoch(),
+                                          fwd_layout(B, T, C, workspace), next_epoch(), keep,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
@@ -347,6 +347,21 @@ int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const flo
     }
     return forward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, a, b, p,
                         workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_infer(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                      const float *u, const void *k, const void *v, const void *r, void *y,
+                      float *a, float *b, float *p, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    static const char *fn = "wkv_forward_infer";
+    g_err[0] = '\0';
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    const int given = (a != nullptr) + (b != nullptr) + (p != nullptr);
+    if (given != 0 && given != 3)
+        return fail(WKV_ERR_INVALID_ARG, "%s: give all of a, b, p or none", fn);
+    return forward_call(fn, B, T, C, fmt, w, u, k, v, r, y, a, b, p, workspace,
+                        workspace_bytes, stream, false);
 }
 
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -444,7 +459,8 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
     } else {
         F = fwd_layout(B, T, C, own + bwd_own_bytes(B, T, C));
         hipError_t e = wkvdev::launch_forward(B, T, C, fmt, w, u, k, v, nullptr, nullptr,
-                                              nullptr, nullptr, nullptr, F, next_epoch(), st);
+                                              nullptr, nullptr, nullptr, F, next_epoch(), true,
+                                              st);
         if (e != hipSuccess) return fail_hip(e, fn);
     }
     hipError_t e = wkvdev::launch_backward(B, T, C, fmt, w, u, k, v, dy, r, F, dk, dv, dr, dw,

@@ -210,8 +210,10 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
 }
 
 // GATE: the output is sigma(r) * y (r [B][T][C]) instead of y. F: the storage format of k,
-// v, r and y.
-template <int NW, int CH, bool GATE, Io F>
+// v, r and y. KEEP: the workspace keeps what the backward reads (the age-weighted fields of
+// the records, the carry entering each window's second chunk and token 0); without it the
+// records hold a, b, P only, and the sums they would have come from are never formed.
+template <int NW, int CH, bool GATE, Io F, bool KEEP>
 __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg, uint64_t epoch, int tries,
     const float *__restrict__ w, const float *__restrict__ u, const io_t<F> *__restrict__ k,
@@ -233,6 +235,18 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     const bool cval = c < C;
     const int cl = (int)(cval ? c : C - 1);
     const int voff = cl * kIoBytes<F>;
+    auto put_r = [&](double *base, int64_t i, const Carry &x) {
+        if constexpr (KEEP)
+            put_rec(base, nrec, i, x);
+        else
+            put_rec3(base, nrec, i, x);
+    };
+    auto get_r = [&](const double *base, int64_t i) {
+        if constexpr (KEEP)
+            return get_rec(base, nrec, i);
+        else
+            return get_rec3(base, nrec, i);
+    };
 
     const float wc = w[cl];
     const float uc = u[cl];
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     // the flags of the previous kPeekDepth windows are read before this unit's flag store,
     // so that one wait covers the aggregate's stores and those reads
     if (q == 0) {
-        if (cval) put_rec(agg, nrec, rec, run);
+        if (cval) put_r(agg, rec, run);
         uint64_t pk = 0;
         if (lane < kPeekDepth && lane < s) pk = peek_flag(myflag - (int64_t)(lane + 1) * nbg);
         put_flag(myflag, epoch, kAggregate);
@@ -315,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
                     const Carry X = window_aggregate<NW, CH, F>(sh, j, q, lane, T, C, row0, cl, k,
                                                              v, slow_wave, dwfd, wd, cw2);
                     if (q == 0) {
-                        if (cval) put_rec(agg, nrec, (bidx * nseg + j) * C + cl, X);
+                        if (cval) put_r(agg, (bidx * nseg + j) * C + cl, X);
                         raise_flag(flags + j * nbg + bg, epoch, kAggregate);
                     }
                 }
@@ -328,20 +342,19 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         }
         // j is the window with a published inclusive carry, or -1; the records are read
         // two at a time so that their round trips overlap
-        prefix = j >= 0 ? get_rec(incl, nrec, (bidx * nseg + j) * C + cl) : start_carry();
+        prefix = j >= 0 ? get_r(incl, (bidx * nseg + j) * C + cl) : start_carry();
         int64_t m = j + 1;
         for (; m + 1 < s; m += 2) {
-            const Carry a0 = get_rec(agg, nrec, (bidx * nseg + m) * C + cl);
-            const Carry a1 = get_rec(agg, nrec, (bidx * nseg + m + 1) * C + cl);
+            const Carry a0 = get_r(agg, (bidx * nseg + m) * C + cl);
+            const Carry a1 = get_r(agg, (bidx * nseg + m + 1) * C + cl);
             prefix = follow(follow(prefix, a0, ww2, (double)WIN), a1, ww2, (double)WIN);
         }
         if (m < s)
-            prefix = follow(prefix, get_rec(agg, nrec, (bidx * nseg + m) * C + cl), ww2,
-                            (double)WIN);
+            prefix = follow(prefix, get_r(agg, (bidx * nseg + m) * C + cl), ww2, (double)WIN);
     }
     // The inclusive record is stored now; wave 0 stores its flag after the output sweep
     // below, so that the wait for the record's stores to complete overlaps the sweep.
-    if (q == 0 && cval) put_rec(incl, nrec, rec, follow(prefix, run, ww2, (double)WIN));
+    if (q == 0 && cval) put_r(incl, rec, follow(prefix, run, ww2, (double)WIN));
     // ---- the carry entering this wave's chunk, kept for the backward pass ----
     Carry mine = follow(prefix, lexcl, (double)(q * CH) * wd * kLog2eD, (double)(q * CH));
     normalize(mine);
@@ -350,12 +363,12 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         // one is the previous window's inclusive carry) is kept
         constexpr int CPC = kCinChunk / CH;
         const int r = q / CPC;
-        if (Lv > 0 && cval && q % CPC == 0 && r > 0)
+        if (KEEP && Lv > 0 && cval && q % CPC == 0 && r > 0)
             put_cin(cin, nrec * kCinCarries, ((bidx * nseg + s) * kCinCarries + r - 1) * C + cl,
                     mine);
     }
     // the carry entering token 0 is kept too (the backward's first chunk starts from it)
-    if (s == 0 && q == 0 && cval) put_cin(init, nrec / nseg, bidx * C + cl, mine);
+    if (KEEP && s == 0 && q == 0 && cval) put_cin(init, nrec / nseg, bidx * C + cl, mine);
     // the wave that holds token T-1 gives the state after it, when asked for
     if (fin != nullptr && t0 < T && T <= t0 + CH && cval) {
         if (exact)
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(256) void wkv_state_out_kernel(const float *__restr
     }
 }
 
-template <Io F>
+template <Io F, bool KEEP>
 static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int64_t C, int ngrp,
                               int64_t nbg, uint64_t epoch, const float *w, const float *u,
                               const void *k, const void *v, const void *r, void *y, float *sa,
@@ -436,34 +449,48 @@ static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int6
                   *rr = static_cast<const io_t<F> *>(r);
     io_t<F> *yy = static_cast<io_t<F> *>(y);
     if (r != nullptr)
-        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F>),
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
                            L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
     else
-        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F>),
+        hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
                            L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
 }
 
+template <Io F>
+static void launch_forward_fmt(bool keep, int64_t units, hipStream_t stream, int64_t T,
+                               int64_t C, int ngrp, int64_t nbg, uint64_t epoch, const float *w,
+                               const float *u, const void *k, const void *v, const void *r,
+                               void *y, float *sa, float *sb, float *sp, float *fin,
+                               const FwdLayout &L, int64_t B) {
+    if (keep)
+        launch_forward_io<F, true>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa, sb,
+                                   sp, fin, L, B);
+    else
+        launch_forward_io<F, false>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
+                                    sb, sp, fin, L, B);
+}
+
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                           const float *u, const void *k, const void *v, const void *r, void *y,
                           float *sa, float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
-                          hipStream_t stream) {
+                          bool keep, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
     float *fin = sa != nullptr ? L.fin : nullptr;
     if (fmt == Io::BF16)
-        launch_forward_io<Io::BF16>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
-                                    sb, sp, fin, L, B);
+        launch_forward_fmt<Io::BF16>(keep, units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r,
+                                     y, sa, sb, sp, fin, L, B);
     else if (fmt == Io::F16)
-        launch_forward_io<Io::F16>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
-                                   sb, sp, fin, L, B);
+        launch_forward_fmt<Io::F16>(keep, units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y,
+                                    sa, sb, sp, fin, L, B);
     else
-        launch_forward_io<Io::F32>(units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y, sa,
-                                   sb, sp, fin, L, B);
+        launch_forward_fmt<Io::F32>(keep, units, stream, T, C, ngrp, nbg, epoch, w, u, k, v, r, y,
+                                    sa, sb, sp, fin, L, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sa == nullptr) return e;
     const int64_t n = B * C;

@@ -87,11 +87,12 @@ struct BwdLayout {
 // token T-1 (through L.fin, by a second kernel, so that no workgroup can read a state that
 // another has already replaced). Without them the scan starts from the empty state.
 // `r` ([B][T][C]) or null: with it the output is sigma(r) * y, the receptance gate. k, v, r
-// and y are in storage format `fmt` (the state sa, sb, sp stays fp32).
+// and y are in storage format `fmt` (the state sa, sb, sp stays fp32). `keep`: the workspace
+// is left with the states the backward reads (otherwise only what the scan itself needs).
 hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                           const float *u, const void *k, const void *v, const void *r, void *y,
                           float *sa, float *sb, float *sp, const FwdLayout &L, uint64_t epoch,
-                          hipStream_t stream);
+                          bool keep, hipStream_t stream);
 
 // `F` is the forward workspace filled for the same inputs (its chunk carries are read).
 // With `r` (and `dr`) the forward output was sigma(r) * y and `dy` is its cotangent. k, v,

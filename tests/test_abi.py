@@ -199,6 +199,25 @@ def test_zero_sized_forward_is_a_noop(pkg):
     assert lib.wkv_last_error() == b""
 
 
+def test_forward_infer_rejects_bad_arguments(pkg):
+    lib = pkg.load_library()
+    f = FAKE
+
+    def call(dtype=0, a=f[7], b=f[8], p=f[9], B=2, T=3, C=4, ws=f[6]):
+        return lib.wkv_forward_infer(dtype, B, T, C, f[0], f[1], f[2], f[3], None, f[4], a, b, p,
+                                     ws, 1 << 40, None)
+
+    assert call(dtype=7) == pkg.WKV_ERR_INVALID_ARG
+    assert b"unknown dtype" in lib.wkv_last_error()
+    assert call(b=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"all of a, b, p or none" in lib.wkv_last_error()
+    assert call(ws=None) == pkg.WKV_ERR_INVALID_ARG
+    assert call(B=0, ws=None, a=None, b=None, p=None) == pkg.WKV_OK
+    # the state overlapping the output
+    assert call(a=f[4]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"overlaps" in lib.wkv_last_error()
+
+
 def _bwd(lib, B, T, C, fws=None, ws=FAKE[11], wsbytes=1 << 40, dw=FAKE[9], du=FAKE[10]):
     f = FAKE
     return lib.wkv_backward(B, T, C, f[0], f[1], f[2], f[3], f[4], fws, f[5], f[6], dw, du, ws,
