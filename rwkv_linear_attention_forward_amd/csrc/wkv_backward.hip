@@ -250,8 +250,11 @@ __device__ __forceinline__ RevCarry chunk_pass(
     Lv = chunk_len(t0, T, CH);
     load_chunk<CH, IO>(kc, vc, k, v, row0, t0, T, C, voff);
     load_chunk1<CH, IO>(gc, dy, row0, t0, T, C, voff);
-    float rr[GATE ? CH : 1];  // r, then dr (gc holds dout)
-    if constexpr (GATE) load_chunk1<CH, IO>(rr, rgate, row0, t0, T, C, voff);
+    if constexpr (GATE) {
+        // r's chunk goes straight into the LDS rows that sigma y takes over token by token in
+        // the sweep (a dword per lane, a 16-bit format zero-extended), holding no registers
+        if (Lv > 0) load_chunk_lds<CH, IO>(sy, rgate, row0, t0, Lv, C, voff);
+    }
     ref = chunk_ref<CH>(kc, Lv);
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
@@ -266,6 +269,12 @@ __device__ __forceinline__ RevCarry chunk_pass(
     fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
     double R = 0.0, Q = 0.0;
     if (!fx) {
+        if constexpr (GATE) lds_load_fence();
+        // dr's stores carry no branch: a token past the sequence end (or a call without dr)
+        // stores through a record of size 0, which drops them; a lane past C repeats the
+        // store of the lane for channel C-1 (the same value: it computes the same inputs)
+        const rsrc_t rnull = make_rsrc_empty(dy);
+        const rsrc_t rdr = GATE && dr != nullptr ? make_rsrc(dr + (row0 + t0) * C) : rnull;
         const double s0 = exp2_64(gap);
         double Sx = fin.a * s0, Zx = fin.b * s0;
         // A'_j = d P_j with P_{j+1} = d P_j + A_j (d = e^{-w}; A'_{j+1} = d (A'_j + A_j));
@@ -293,10 +302,12 @@ __device__ __forceinline__ RevCarry chunk_pass(
             const double yv = num * r;
             double gd = (double)gc[j];
             if constexpr (GATE) {
-                // the gated cotangent dout sigma(r) in fp64, and dr = dout sigma (1 - sigma) y
-                const double sr = sigmoid64(rr[j]);
+                // the gated cotangent dout sigma(r) in fp64, and dr = dout sigma (1 - sigma) y,
+                // stored now (a chunk that then takes the per-token path stores it again)
+                const double sr = sigmoid64(lds_widen<IO>(sy[j][lane]));
                 gd *= sr;
-                rr[j] = (float)(gd * (1.0 - sr) * yv);
+                bstore_io<IO>(j < Lv ? rdr : rnull, (float)(gd * (1.0 - sr) * yv), voff,
+                              j * stride);
             }
             const double sg = gd * r;
             const double sgy = sg * yv;
@@ -319,17 +330,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
         du_acc *= K.eu;
         fx = wave_any(tiny);
     }
-    if (!fx) {
-        if constexpr (GATE) {
-            if (dr != nullptr && cval) {
-                const rsrc_t rdr = make_rsrc(dr + (row0 + t0) * C);
-#pragma unroll
-                for (int j = 0; j < CH; ++j)
-                    if (j < Lv) bstore_io<IO>(rdr, rr[j], voff, j * stride);
-            }
-        }
-        return RevCarry{R, Q, -ref2};
-    }
+    if (!fx) return RevCarry{R, Q, -ref2};
     const ExactResult xr = exact_chunk<CH, false, true, IO>(
         k, v, dy, nullptr, nullptr, row0, t0, Lv, C, cl, false, ref, fin, rev_zero(), K.uc,
         K.wc, GATE ? rgate : nullptr, GATE && cval ? dr : nullptr);
@@ -426,11 +427,10 @@ __device__ __forceinline__ void window_rev_sums(const BwdShared<NW, CH> &sh, int
 }
 
 // GATE: the output was sigma(r) * y; `dy` holds the cotangent of that gated output, and dr
-// is written too (r's chunk takes 32 more registers: two waves per SIMD). IO: the storage
-// format of k, v, dy, r, dk, dv and dr. `tries`: polls before a missing window is
-// recomputed.
+// is written too. IO: the storage format of k, v, dy, r, dk, dv and dr. `tries`: polls
+// before a missing window is recomputed.
 template <int NW, int CH, bool GATE, Io IO>
-__global__ __launch_bounds__(NW * 64, GATE ? 2 : 3) void wkv_backward_kernel(
+__global__ __launch_bounds__(NW * 64, 3) void wkv_backward_kernel(
     int64_t B, int64_t T, int64_t C, int ngrp, int64_t nbg, int64_t nseg,
     uint64_t epoch, int tries, const float *__restrict__ w, const float *__restrict__ u,
     const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,

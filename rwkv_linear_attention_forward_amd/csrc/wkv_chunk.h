@@ -107,6 +107,39 @@ __device__ __forceinline__ void load_chunk1(float (&gc)[CH], const io_t<F> *__re
     }
 }
 
+// Load one tensor's CH-token chunk straight into LDS: row j of `dst` ([CH][64] dwords, the
+// wave's own) gets token j's value of each lane's channel (a 16-bit format zero-extended in
+// the low half), tokens past the Lv valid ones repeating the last valid row. No registers
+// hold the data; lds_load_fence() must come before `dst` is read.
+template <int CH, Io F>
+__device__ __forceinline__ void load_chunk_lds(float (*dst)[64], const io_t<F> *__restrict__ g,
+                                               int64_t row0, int64_t t0, int Lv, int64_t C,
+                                               int voff) {
+    const rsrc_t rg = make_rsrc(g + (row0 + t0) * C);
+    const int stride = (int)(C * kIoBytes<F>);
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (__attribute__((address_space(3))) void *)dst[j], kIoBytes<F>, voff,
+            (j < Lv ? j : Lv - 1) * stride, 0, 2);
+}
+// Wait for this wave's direct-to-LDS loads (and every other load it has in flight).
+__device__ __forceinline__ void lds_load_fence() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// A value that load_chunk_lds left in a dword, widened to fp32.
+template <Io F>
+__device__ __forceinline__ float lds_widen(float x) {
+    if constexpr (F == Io::F32) {
+        return x;
+    } else if constexpr (F == Io::BF16) {
+        return __builtin_bit_cast(float, __builtin_bit_cast(unsigned, x) << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16,
+                                         (unsigned short)(__builtin_bit_cast(unsigned, x)));
+    }
+}
+
 // Valid tokens of the chunk starting at t0.
 __device__ __forceinline__ int chunk_len(int64_t t0, int64_t T, int CH) {
     return (int)(t0 >= T ? 0 : (T - t0 < CH ? T - t0 : CH));

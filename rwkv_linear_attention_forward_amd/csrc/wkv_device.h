@@ -56,6 +56,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
                                              0x00020000);
 }
+// A resource of 0 records: every access through it is out of range (loads return 0,
+// stores are dropped), whatever the offsets.
+__device__ __forceinline__ rsrc_t make_rsrc_empty(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0, 0x00020000);
+}
 __device__ __forceinline__ float bload(rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2));
 }
@@ -88,9 +93,12 @@ template <Io F> __device__ __forceinline__ io_t<F> io_narrow(float x) {
     if constexpr (F == Io::F32) {
         return x;
     } else if constexpr (F == Io::BF16) {
+        // round to nearest even; a NaN stays a NaN (quiet bit set). Branch-free, so that
+        // unrolled sweeps that store bf16 stay straight-line code.
         const unsigned u = __builtin_bit_cast(unsigned, x);
-        if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
-        return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        const unsigned rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        const unsigned nan = (u >> 16) | 0x40u;
+        return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
     } else {
         return __builtin_bit_cast(uint16_t, (_Float16)x);
     }
