@@ -17,20 +17,21 @@
 // the forward direction, formed where y_t and D_t are computed; only dk and dv need the
 // future sums.
 //
-// Work decomposition as in the forward (64 channels x one 256-token window per workgroup,
-// one CH-token chunk per wave), with units numbered from the last window backwards so that
+// Work decomposition as in the forward (64 channels x one 64-token window per workgroup,
+// one 32-token chunk per wave), with units numbered from the last window backwards so that
 // the future of a unit was launched first. Each unit reads k, v, dy once and writes dk, dv
-// once: 20 bytes per element. The forward state entering the window (with A', B') is read
+// once: 20 bytes per element. The forward state entering each chunk (with A', B') is read
 // from the forward's workspace, so no extra pass over k and v is needed.
 //
 // Per chunk, in the forward pass's chunk frame (ref = max k, e_j = e^{k_j - ref}):
-//   F1     forward summary of the chunk (fp64, as the forward computes it); the window's
-//          summaries are folded through LDS into the carry entering each chunk.
+//   F1     the carry entering the chunk: the previous window's inclusive carry or the
+//          window's kept chunk carry, from the forward's workspace.
 //   F3     y_j, den_j, sigma_j = dy_j / den_j (s_t in the frame) and the dw, du terms,
 //          all in fp64 from fp64 weights e_j: dw is a sum over B*T tokens whose terms
 //          cancel by factors of 10^4 on some channels (and its per-sequence parts cancel
 //          again over the batch), so any fp32 rounding of e_j, y_j or sigma_j inside it
-//          shows up. e_j, y_j, sigma_j are then kept in fp32 for dk, dv.
+//          shows up. e_j and sigma_j are then kept in fp32 registers and sigma_j y_j in
+//          LDS for dk, dv.
 //   R1     reverse summary of the chunk from a zero future, by Horner from the chunk end:
 //          R_{j-1} = e^{-w} R_j + sigma_j, Q likewise with sigma_j y_j (fp64).
 //   scan   reverse summaries are folded through LDS and across windows (decoupled

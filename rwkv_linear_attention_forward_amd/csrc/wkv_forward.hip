@@ -35,8 +35,8 @@
 // The fixed frame is exact in real arithmetic but can underflow when k varies by more
 // than ~70 inside one chunk, or overflow when the incoming carry exceeds the chunk frame
 // by 2^64. Such chunks (rare; only far outside the training distributions) are detected
-// per wave and recomputed with the per-token rescaled recursion (Rs in wkv_device.h),
-// which is safe for any finite k.
+// per wave and recomputed with the per-token rescaled recursion in fp64, which is safe
+// for any finite k.
 #include "wkv_chunk.h"
 
 namespace wkvdev {
