@@ -59,9 +59,10 @@ METRIC = ("WKV fwd+bwd elements/sec (B·T·C) and achieved HBM GB/s vs peak, "
           "T=4096 C=2560")
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30
-# The step's kernels as rocprofv3 names them (the fp32, ungated instances; the other legs run
-# other instances, or come after the step's dispatches).
-KERNELS = {"forward": "wkv_forward_kernel<2, 32, false, (wkvdev::Io)0>",
+# The step's kernels as rocprofv3 names them (the fp32, ungated instances that keep the
+# backward's states; the other legs run other instances, or come after the step's
+# dispatches).
+KERNELS = {"forward": "wkv_forward_kernel<2, 32, false, (wkvdev::Io)0, true>",
            "backward": "wkv_backward_kernel<2, 32, false, (wkvdev::Io)0>"}
 REDUCE_KERNEL = "wkv_reduce_kernel"
 BYTES_PER_ELEM = {"forward": 12, "backward": 20}
