@@ -159,6 +159,26 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream);
 
+/* wkv_backward that also gives the gradient of L with respect to the state the forward
+ * started from: da, db, dp [B][C] fp32 (overwritten), for the decode-convention state
+ * (A = a e^p, B = b e^p) passed to wkv_forward_state, whose workspace must be given as
+ * `fwd_workspace` (required here: it records that state, so a, b, p themselves, since
+ * overwritten with the final state, are not needed). This is the backward through the
+ * recursive form of formula (8) ("RWKV解读：在Transformer的时代的新RNN", section 二.3) run
+ * over a sequence split into pieces, each resuming from the state the previous piece
+ * left ("RWKV についての調査記録", section "RWKVとは？": the state carries the past).
+ * The state before token 0 reaches token t only through A0 e^{-t w} and B0 e^{-t w}, so
+ * with the future sums G = sum_t e^{-t w} dy_t / D_t and H = sum_t e^{-t w} dy_t y_t /
+ * D_t (D_t the denominator at token t): da = G e^p, db = -H e^p, dp = (a G - b H) e^p.
+ * A forward from the empty state (wkv_forward) gives zeros. dk, dv, dw, du are bitwise
+ * those of wkv_backward with the same arguments. T == 0 writes zeros. da, db, dp must not
+ * overlap each other or any other argument. */
+int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *dy,
+                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
+                       float *da, float *db, float *dp, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 /* Backward of the gated forward, L = sum dout * sigma(r) * y: as wkv_backward with the
  * cotangent dy = dout * sigma(r) formed on the fly, plus dr [B][T][C] =
  * dout * sigma(r) * (1 - sigma(r)) * y (y recomputed, never read). `fwd_workspace` is NULL

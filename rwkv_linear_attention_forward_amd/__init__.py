@@ -42,7 +42,7 @@ EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_st
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
            "wkv_forward_infer",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
-           "wkv_backward_typed", "wkv_decode_step", "wkv_token_shift",
+           "wkv_backward_typed", "wkv_backward_state", "wkv_decode_step", "wkv_token_shift",
            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
 
 # Storage formats of the [B, T, C] tensors (dtype codes of the *_typed entry points).
@@ -107,6 +107,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward.restype = ctypes.c_int
     lib.wkv_backward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, ctypes.c_size_t, _P]
+    lib.wkv_backward_state.restype = ctypes.c_int
+    lib.wkv_backward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_decode_step.restype = ctypes.c_int
     lib.wkv_decode_step.argtypes = [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = lib
@@ -313,6 +316,42 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
     preallocated (dk, dv, dw, du). k, v, dy (and dk, dv) share one of float32, bfloat16,
     float16; w, u, dw, du are float32."""
     return _backward_common(w, u, k, v, dy, None, fwd_workspace, workspace, out)
+
+
+def backward_state(w, u, k, v, dy, fwd_workspace, workspace=None, out=None):
+    """(dk, dv, dw, du, da, db, dp) of sum(dy * y) for a forward_state() call, whose
+    workspace `fwd_workspace` is required: da, db, dp [B, C] are the gradient with respect
+    to the state (a, b, p) that forward started from (it records that state, so the caller
+    need not keep it). float32 only; `out` may hold preallocated (dk, dv, dw, du, da, db,
+    dp)."""
+    B, T, C, dev = _check_btc(w, u, k, v)
+    _need(dy, "dy", 3, dev)
+    if dy.shape != k.shape:
+        raise ValueError("dy has the wrong shape")
+    if fwd_workspace is None:
+        raise ValueError("backward_state needs the workspace of the forward_state call")
+    _check_ws(fwd_workspace, dev, "fwd_workspace")
+    wsz = backward_workspace_size(B, T, C, True)
+    if workspace is None or workspace.numel() < wsz:
+        workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
+    _check_ws(workspace, dev, "workspace")
+    shapes = ((B, T, C), (B, T, C), (C,), (C,), (B, C), (B, C), (B, C))
+    names = ("dk", "dv", "dw", "du", "da", "db", "dp")
+    if out is None:
+        grads = tuple(torch.empty(sh, dtype=torch.float32, device=dev) for sh in shapes)
+    else:
+        grads = tuple(out)
+        if len(grads) != len(names):
+            raise ValueError("out must hold %d tensors" % len(names))
+        for t, n, sh in zip(grads, names, shapes):
+            _need(t, n, len(sh), dev)
+            if tuple(t.shape) != sh:
+                raise ValueError("%s has the wrong shape" % n)
+    _check(load_library().wkv_backward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                             _ptr(dy), _ptr(fwd_workspace),
+                                             *(_ptr(g) for g in grads), _ptr(workspace),
+                                             workspace.numel(), _stream(dev)))
+    return grads
 
 
 def forward_infer(w, u, k, v, r=None, state=None, workspace=None, out=None):

@@ -403,7 +403,8 @@ namespace {
 int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt,
                   const float *w, const float *u, const void *k, const void *v, const void *dy,
                   const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,
-                  float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream) {
+                  float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream,
+                  float *ga = nullptr, float *gb = nullptr, float *gp = nullptr) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (C == 0) return WKV_OK;
@@ -436,16 +437,20 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
     const size_t nb = (size_t)(B * T * C) * es, nc = (size_t)C * 4u;
-    const void *outs[6] = {dk, dv, dw, du, workspace, dr};
-    const size_t osz[6] = {nb, nb, nc, nc, need, dr ? nb : 0};
+    const size_t ns = ga ? (size_t)(B * C) * 4u : 0;
+    if (ga != nullptr && (!aligned(ga, 4, "da", fn) || !aligned(gb, 4, "db", fn) ||
+                          !aligned(gp, 4, "dp", fn)))
+        return WKV_ERR_INVALID_ARG;
+    const void *outs[9] = {dk, dv, dw, du, workspace, dr, ga, gb, gp};
+    const size_t osz[9] = {nb, nb, nc, nc, need, dr ? nb : 0, ns, ns, ns};
     const void *ins[7] = {w, u, k, v, dy, fwd_workspace, r};
     const size_t isz[7] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0,
                            r ? nb : 0};
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 9; ++i) {
         for (int j = 0; j < 7; ++j)
             if (overlap(outs[i], osz[i], ins[j], isz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
-        for (int j = i + 1; j < 6; ++j)
+        for (int j = i + 1; j < 9; ++j)
             if (overlap(outs[i], osz[i], outs[j], osz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
     }
@@ -464,7 +469,8 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
         if (e != hipSuccess) return fail_hip(e, fn);
     }
     hipError_t e = wkvdev::launch_backward(B, T, C, fmt, w, u, k, v, dy, r, F, dk, dv, dr, dw,
-                                           du, bwd_layout(B, T, C, own), next_epoch(), st);
+                                           du, ga, gb, gp, bwd_layout(B, T, C, own),
+                                           next_epoch(), st);
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
 }
@@ -480,6 +486,37 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
     return backward_call("wkv_backward", B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr,
                          fwd_workspace, dk, dv, nullptr, dw, du, workspace, workspace_bytes,
                          stream);
+}
+
+int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *dy,
+                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
+                       float *da, float *db, float *dp, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_backward_state";
+    g_err[0] = '\0';
+    if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (B > 0 && C > 0) {
+        if (!nonnull(fwd_workspace, "fwd_workspace", fn) || !nonnull(da, "da", fn) ||
+            !nonnull(db, "db", fn) || !nonnull(dp, "dp", fn))
+            return WKV_ERR_INVALID_ARG;
+        if (!aligned(da, 4, "da", fn) || !aligned(db, 4, "db", fn) || !aligned(dp, 4, "dp", fn))
+            return WKV_ERR_INVALID_ARG;
+        const size_t ns = (size_t)(B * C) * 4u;
+        if (overlap(da, ns, db, ns) || overlap(da, ns, dp, ns) || overlap(db, ns, dp, ns))
+            return fail(WKV_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+        if (T == 0) {
+            // no token: the state passes through unchanged, and L does not depend on it
+            int rc = check_device(fn);
+            if (rc != WKV_OK) return rc;
+            hipStream_t st = static_cast<hipStream_t>(stream);
+            hipError_t e = wkvdev::launch_zero2(da, db, B * C, st);
+            if (e == hipSuccess) e = wkvdev::launch_zero2(dp, dp, B * C, st);
+            if (e != hipSuccess) return fail_hip(e, fn);
+        }
+    }
+    return backward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr, fwd_workspace,
+                         dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream, da, db, dp);
 }
 
 int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -700,11 +700,31 @@ static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int
                            ddr, dw, du, L.flags, L.ragg, L.rincl, L.part);
 }
 
+// Gradient with respect to the state before token 0. That state holds A0 = a e^p and
+// B0 = b e^p, which reach token t as e^{-t w} A0 and e^{-t w} B0, so dL/dA0 = G_{-1} and
+// dL/dB0 = -H_{-1}: the future sums over the whole sequence, which the backward leaves as
+// window 0's reverse inclusive record. With the state (a, b, 2^P = e^p) as the forward
+// recorded it: da = G e^p, db = -H e^p, dp = (a G - b H) e^p. One lane per (b, c).
+__global__ __launch_bounds__(256) void wkv_state_grad_kernel(
+    int64_t n, int64_t C, int64_t nseg, const double *__restrict__ init,
+    const double *__restrict__ rincl, float *__restrict__ ga, float *__restrict__ gb,
+    float *__restrict__ gp) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t b = i / C, c = i - b * C;
+    const RevCarry fut = get_rrec(rincl, n * nseg, b * nseg * C + c);
+    const Carry st = get_cin(init, n, i);
+    const double sc = exp2_64(fut.r + st.P);
+    ga[i] = (float)(fut.g * sc);
+    gb[i] = (float)(-fut.h * sc);
+    gp[i] = (float)(fma(st.a, fut.g, -st.b * fut.h) * sc);
+}
+
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                            const float *u, const void *k, const void *v, const void *dy,
                            const void *r, const FwdLayout &F, void *dk, void *dv, void *dr,
-                           float *dw, float *du, const BwdLayout &L, uint64_t epoch,
-                           hipStream_t stream) {
+                           float *dw, float *du, float *ga, float *gb, float *gp,
+                           const BwdLayout &L, uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
@@ -723,6 +743,11 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),
                        dim3(kReduceCh * kReduceSlices), 0,
                        stream, B * L.nseg, C, L.part, dw, du);
+    e = hipGetLastError();
+    if (e != hipSuccess || ga == nullptr) return e;
+    const int64_t n = B * C;
+    hipLaunchKernelGGL(wkv_state_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, n, C, L.nseg, F.init, L.rincl, ga, gb, gp);
     return hipGetLastError();
 }
 

@@ -367,8 +367,9 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
             put_cin(cin, nrec * kCinCarries, ((bidx * nseg + s) * kCinCarries + r - 1) * C + cl,
                     mine);
     }
-    // the carry entering token 0 is kept too (the backward's first chunk starts from it)
-    if (KEEP && s == 0 && q == 0 && cval) put_cin(init, nrec / nseg, bidx * C + cl, mine);
+    // the carry entering token 0 is kept too, as given (the backward's first chunk starts
+    // from it, normalized; the gradient with respect to a given state needs its p)
+    if (KEEP && s == 0 && q == 0 && cval) put_cin(init, nrec / nseg, bidx * C + cl, prefix);
     // the wave that holds token T-1 gives the state after it, when asked for
     if (fin != nullptr && t0 < T && T <= t0 + CH && cval) {
         if (exact)

@@ -28,3 +28,16 @@ def backward_with_state(w, u, k, v, dy, state):
     g = np.concatenate([np.zeros_like(dy[:, :1]), dy], axis=1)
     dk, dv, dw, du = oracle.backward_direct(w, u, kk, vv, g)
     return dk[:, 1:], dv[:, 1:], dw, du
+
+
+def backward_state_grad(w, u, k, v, dy, state):
+    """backward_with_state plus (da, db, dp), the gradient of L with respect to the state
+    (b > 0): through the prepended token, k0 = p + ln b and v0 = a / b, so with that token's
+    own dk0, dv0: da = dv0 / b, db = dk0 / b - dv0 a / b^2, dp = dk0."""
+    a, b, p = (np.asarray(s, np.float64) for s in state)
+    kk, vv = prepend_state_token(state, k, v)
+    dy = np.asarray(dy, np.float64)
+    g = np.concatenate([np.zeros_like(dy[:, :1]), dy], axis=1)
+    dk, dv, dw, du = oracle.backward_direct(w, u, kk, vv, g)
+    dk0, dv0 = dk[:, 0], dv[:, 0]
+    return (dk[:, 1:], dv[:, 1:], dw, du, dv0 / b, dk0 / b - dv0 * a / (b * b), dk0)

@@ -241,6 +241,32 @@ def test_backward_rejects_bad_arguments(pkg):
     assert _bwd(lib, 2, 3, 0, dw=None, du=None) == pkg.WKV_OK
 
 
+def test_backward_state_rejects_bad_arguments(pkg):
+    # every call here fails validation (or has nothing to do) before any device call
+    lib = pkg.load_library()
+    g = [ctypes.c_void_p(0x4000000 + 0x100000 * i) for i in range(16)]
+
+    def call(B=2, T=3, C=4, fws=g[5], da=g[12], db=g[13], dp=g[14]):
+        return lib.wkv_backward_state(B, T, C, g[0], g[1], g[2], g[3], g[4], fws, g[6], g[7],
+                                      g[8], g[9], da, db, dp, g[11], 1 << 40, None)
+
+    assert call(T=-1) == pkg.WKV_ERR_INVALID_ARG
+    assert call(fws=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"fwd_workspace is NULL" in lib.wkv_last_error()
+    assert call(T=0, fws=None) == pkg.WKV_ERR_INVALID_ARG
+    assert call(db=None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"db is NULL" in lib.wkv_last_error()
+    assert call(dp=ctypes.c_void_p(g[14].value + 2)) == pkg.WKV_ERR_INVALID_ARG
+    assert call(db=ctypes.c_void_p(g[12].value + 16)) == pkg.WKV_ERR_INVALID_ARG
+    assert b"overlap" in lib.wkv_last_error()
+    # da on top of an input (k) and of another output (dk)
+    assert call(da=g[2]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"overlaps an input" in lib.wkv_last_error()
+    assert call(dp=g[6]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"two outputs overlap" in lib.wkv_last_error()
+    assert lib.wkv_backward_state(2, 3, 0, *([None] * 14), 0, None) == pkg.WKV_OK
+
+
 def test_decode_rejects_bad_arguments(pkg):
     lib = pkg.load_library()
     f = FAKE

@@ -1,0 +1,138 @@
+"""GPU parity of wkv_backward_state against the fp64 oracle (marked gpu).
+
+A sequence run in pieces, each resuming from the state the previous one left ("RWKV
+についての調査記録", section "RWKVとは？": the state is what carries the past), is trained
+through those states when the gradient reaches the state each piece started from. The
+reference is the oracle's direct backward of the piece with the state's token prepended
+(key p + ln b, value a / b), whose own dk, dv give da, db, dp by the chain rule
+(tests/state_ref.py, pinned against finite differences and a closed form in
+test_oracle_state.py). dk, dv, dw, du must be bitwise those of wkv_backward.
+"""
+import numpy as np
+import pytest
+
+import wkv_inputs
+from helpers import assert_wkv_close
+from state_ref import backward_state_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(dev, a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _forward_state(wkv, dev, t, state):
+    B, T, C = t["k"].shape
+    ws = wkv.forward_workspace(B, T, C, dev)
+    st = [_t(dev, s) for s in state]
+    wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws)
+    return ws
+
+
+def _log(name, v):
+    print("[backward_state] %s max_violation=%.3g" % (name, v), flush=True)
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 37, 70), (1, 64, 64), (3, 129, 130),
+                                   (2, 300, 65), (1, 1000, 256)])
+@pytest.mark.parametrize("prange", [(-3.0, 3.0), (20.0, 30.0), (-30.0, -20.0)])
+def test_state_gradient_parity(wkv, dev, B, T, C, prange):
+    """States on the keys' scale, far above it (they dominate the first tokens) and far
+    below it (their gradient is tiny but must still be right to the relative bar)."""
+    import torch
+    x = wkv_inputs.generate("l3b", seed=60 + B * T + C, B=B, T=T, C=C)
+    st = wkv_inputs.random_state(B, C, seed=T + C, p_range=prange)
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v", "dy")}
+    ws = _forward_state(wkv, dev, t, st)
+    got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)
+    torch.cuda.synchronize()
+    ref = backward_state_grad(x["w"], x["u"], x["k"], x["v"], x["dy"], st)
+    worst = 0.0
+    for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
+        r = np.asarray(r, np.float64)
+        # the state gradients scale with e^p: judged relative to their own largest entry
+        floor = 0.1 if n[1] in "kvwu" else 0.1 * max(float(np.max(np.abs(r))), 1e-300)
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s B=%d T=%d C=%d p in %s"
+                                            % (n, B, T, C, prange), floor=floor))
+    _log("B=%d T=%d C=%d p in %s" % (B, T, C, prange), worst)
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 37, 70), (3, 700, 200)])
+def test_other_gradients_bitwise_equal_backward(wkv, dev, B, T, C):
+    import torch
+    x = wkv_inputs.generate("l3b", seed=80 + T, B=B, T=T, C=C)
+    st = wkv_inputs.random_state(B, C, seed=81, p_range=(-3.0, 3.0))
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v", "dy")}
+    ws = _forward_state(wkv, dev, t, st)
+    got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)
+    base = wkv.backward(t["w"], t["u"], t["k"], t["v"], t["dy"], fwd_workspace=ws)
+    torch.cuda.synchronize()
+    for g, r, n in zip(got[:4], base, ("dk", "dv", "dw", "du")):
+        assert torch.equal(g, r), n
+
+
+def test_empty_state_gives_zero_state_gradient(wkv, dev):
+    """From the empty state (wkv_forward, or wkv_forward_state from a = b = 0, p = -1e38 or
+    -inf) the state gradient is zero: A = a e^p has no slope in a, b or p there."""
+    import torch
+    B, T, C = 2, 90, 130
+    x = wkv_inputs.generate("l3b", seed=90, B=B, T=T, C=C)
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v", "dy")}
+    ws = wkv.forward_workspace(B, T, C, dev)
+    wkv.forward(t["w"], t["u"], t["k"], t["v"], workspace=ws)
+    outs = [wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)]
+    e = wkv_inputs.empty_decode_state(B, C)
+    for p in (e[2], np.full_like(e[2], -np.inf)):
+        ws2 = _forward_state(wkv, dev, t, (e[0], e[1], p))
+        outs.append(wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws2))
+    torch.cuda.synchronize()
+    for o in outs:
+        for g in o[4:]:
+            assert torch.count_nonzero(g).item() == 0
+        for g, r in zip(o[:4], outs[0][:4]):
+            assert torch.equal(g, r)
+
+
+def test_zero_length_writes_zeros(wkv, dev):
+    import torch
+    B, C = 3, 70
+    w = torch.rand(C, device=dev)
+    k = torch.zeros(B, 0, C, device=dev)
+    ws = wkv.forward_workspace(B, 0, C, dev)
+    out = [torch.full(s, 7.0, device=dev) for s in ((B, 0, C), (B, 0, C), (C,), (C,),
+                                                    (B, C), (B, C), (B, C))]
+    got = wkv.backward_state(w, w, k, k, k, ws, out=out)
+    torch.cuda.synchronize()
+    for g in got[2:]:
+        assert torch.count_nonzero(g).item() == 0
+
+
+def test_full_layer_state_gradient(wkv, dev):
+    """The 3B-class layer shape (B=8, T=4096, C=2560) from a random state; da, db, dp in
+    full and dk, dv on the first 96 tokens, where the state still counts (the oracle's
+    direct form is O(T^2) per channel, so it runs on that prefix: the gradients of the
+    prefix's loss only, with dy zero beyond it)."""
+    import torch
+    x = wkv_inputs.generate("l3b")
+    B, T, C = x["k"].shape
+    Tp = 96
+    dy = x["dy"].copy()
+    dy[:, Tp:] = 0
+    st = wkv_inputs.random_state(B, C, seed=91)
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v")}
+    t["dy"] = _t(dev, dy)
+    ws = _forward_state(wkv, dev, t, st)
+    got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)
+    torch.cuda.synchronize()
+    ref = backward_state_grad(x["w"], x["u"], x["k"][:, :Tp], x["v"][:, :Tp], dy[:, :Tp], st)
+    worst = 0.0
+    for g, r, n in ((got[0][:, :Tp], ref[0], "dk"), (got[1][:, :Tp], ref[1], "dv"),
+                    (got[2], ref[2], "dw"), (got[3], ref[3], "du"), (got[4], ref[4], "da"),
+                    (got[5], ref[5], "db"), (got[6], ref[6], "dp")):
+        r = np.asarray(r, np.float64)
+        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "l3b " + n, floor=floor))
+    assert torch.count_nonzero(got[0][:, Tp:]).item() == 0
+    _log("l3b (loss on the first %d tokens)" % Tp, worst)

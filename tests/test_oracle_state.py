@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from state_ref import backward_with_state, prepend_state_token as _prepend
+from state_ref import backward_state_grad, backward_with_state, prepend_state_token as _prepend
 
 
 def _rand(B, T, C, seed, kscale=1.0):
@@ -97,3 +97,46 @@ def test_backward_with_state_finite_differences():
             ap[i], am[i] = xp, xm
             fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
         np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("T", [1, 6])
+def test_state_gradient_finite_differences(T):
+    # da, db, dp of L = sum(dy * y) against central differences of the state-in forward
+    rng, w, u, k, v = _rand(2, T, 3, 50 + T, kscale=1.5)
+    st = _state(rng, 2, 3)
+    dy = rng.standard_normal(k.shape)
+    got = backward_state_grad(w, u, k, v, dy, st)
+    base = backward_with_state(w, u, k, v, dy, st)
+    for g, r in zip(got[:4], base):
+        np.testing.assert_allclose(g, r, rtol=1e-12, atol=1e-14)
+
+    def loss(s_):
+        return float(np.sum(dy * oracle.forward_rescaled(w, u, k, v, s_)[0]))
+
+    for i, name in enumerate(("a", "b", "p")):
+        x = st[i]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-6 * max(1.0, abs(x[idx]))
+            sp, sm = [s_.copy() for s_ in st], [s_.copy() for s_ in st]
+            sp[i][idx] += h
+            sm[i][idx] -= h
+            fd[idx] = (loss(sp) - loss(sm)) / (2 * h)
+        np.testing.assert_allclose(got[4 + i], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_state_gradient_closed_form_single_token():
+    # T = 1: y_0 = (A + e^{u+k} v) / (B + e^{u+k}) with A = a e^p, B = b e^p, so
+    # dL/dA = dy / D and dL/dB = -dy y / D, D = B + e^{u+k}
+    rng, w, u, k, v = _rand(2, 1, 4, 55)
+    a, b, p = _state(rng, 2, 4)
+    dy = rng.standard_normal(k.shape)
+    got = backward_state_grad(w, u, k, v, dy, (a, b, p))
+    ep = np.exp(p)
+    e = np.exp(u + k[:, 0])
+    D = b * ep + e
+    y = (a * ep + e * v[:, 0]) / D
+    g, hh = dy[:, 0] / D, dy[:, 0] * y / D
+    np.testing.assert_allclose(got[4], g * ep, rtol=1e-12)
+    np.testing.assert_allclose(got[5], -hh * ep, rtol=1e-12)
+    np.testing.assert_allclose(got[6], (a * g - b * hh) * ep, rtol=1e-10, atol=1e-14)
