@@ -159,25 +159,34 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
                  float *dk, float *dv, float *dw, float *du, void *workspace,
                  size_t workspace_bytes, void *stream);
 
-/* wkv_backward that also gives the gradient of L with respect to the state the forward
- * started from: da, db, dp [B][C] fp32 (overwritten), for the decode-convention state
- * (A = a e^p, B = b e^p) passed to wkv_forward_state, whose workspace must be given as
- * `fwd_workspace` (required here: it records that state, so a, b, p themselves, since
- * overwritten with the final state, are not needed). This is the backward through the
- * recursive form of formula (8) ("RWKV解读：在Transformer的时代的新RNN", section 二.3) run
- * over a sequence split into pieces, each resuming from the state the previous piece
- * left ("RWKV についての調査記録", section "RWKVとは？": the state carries the past).
- * The state before token 0 reaches token t only through A0 e^{-t w} and B0 e^{-t w}, so
- * with the future sums G = sum_t e^{-t w} dy_t / D_t and H = sum_t e^{-t w} dy_t y_t /
- * D_t (D_t the denominator at token t): da = G e^p, db = -H e^p, dp = (a G - b H) e^p.
- * A forward from the empty state (wkv_forward) gives zeros. dk, dv, dw, du are bitwise
- * those of wkv_backward with the same arguments. T == 0 writes zeros. da, db, dp must not
- * overlap each other or any other argument. */
+/* wkv_backward for a forward from a state (wkv_forward_state, whose workspace must be
+ * given as `fwd_workspace`: it records the state the forward started from and the one it
+ * returned, so the caller need not keep them), for a sequence trained in pieces, each
+ * resuming from the state the previous one left ("RWKV についての調査記録", section
+ * "RWKVとは？": the state carries the past; the recursive form of formula (8) of
+ * "RWKV解读：在Transformer的时代的新RNN", section 二.3, run over the pieces in turn).
+ *
+ * L = sum_{b,t,c} dy[b,t,c] y[b,t,c] + sum_{b,c} (dfa[b,c] a_T[b,c] + dfb[b,c] b_T[b,c]),
+ * where (a_T, b_T, p_T) is the state the forward returned (p_T held fixed; A_T = a_T e^{p_T})
+ * and dfa, dfb [B][C] its cotangent from the next piece (that piece's da, db), or both NULL
+ * (then L is wkv_backward's). Outputs: dk, dv, dw, du as in wkv_backward, and da, db, dp
+ * [B][C] fp32 (overwritten), the gradient with respect to the state (a, b, p) the forward
+ * started from. The state before token 0 reaches token t only through A0 e^{-t w} and
+ * B0 e^{-t w}, so with the future sums G = sum_t e^{-t w} dy_t / D_t and H = sum_t e^{-t w}
+ * dy_t y_t / D_t (D_t the denominator at token t): da = G e^p, db = -H e^p, dp = (a G -
+ * b H) e^p, plus with dfa, dfb the path through the final state (A_T holds e^{-T w} A0).
+ * dp = a da + b db always (L depends on a, p only through a e^p). A forward from the empty
+ * state (wkv_forward, or a = b = 0) gives da = db = dp = 0. Without dfa, dfb: dk, dv, dw,
+ * du are bitwise those of wkv_backward with the same arguments; with them the final
+ * state's terms are added by a second pass over k, v, dk, dv. T == 0 writes zero da, db,
+ * dp, dw, du, but is refused with dfa, dfb (a zero-length piece records no state: its
+ * final state's cotangent is its initial state's, which the caller passes on). Outputs
+ * must not overlap each other or any input. fp32 only. */
 int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                       const float *k, const float *v, const float *dy,
-                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
-                       float *da, float *db, float *dp, void *workspace,
-                       size_t workspace_bytes, void *stream);
+                       const float *k, const float *v, const float *dy, const float *dfa,
+                       const float *dfb, const void *fwd_workspace, float *dk, float *dv,
+                       float *dw, float *du, float *da, float *db, float *dp,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward of the gated forward, L = sum dout * sigma(r) * y: as wkv_backward with the
  * cotangent dy = dout * sigma(r) formed on the fly, plus dr [B][T][C] =

@@ -109,7 +109,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  _P, ctypes.c_size_t, _P]
     lib.wkv_backward_state.restype = ctypes.c_int
     lib.wkv_backward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                       _P, _P, _P, _P, ctypes.c_size_t, _P]
+                                       _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.wkv_decode_step.restype = ctypes.c_int
     lib.wkv_decode_step.argtypes = [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = lib
@@ -318,16 +318,25 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
     return _backward_common(w, u, k, v, dy, None, fwd_workspace, workspace, out)
 
 
-def backward_state(w, u, k, v, dy, fwd_workspace, workspace=None, out=None):
-    """(dk, dv, dw, du, da, db, dp) of sum(dy * y) for a forward_state() call, whose
-    workspace `fwd_workspace` is required: da, db, dp [B, C] are the gradient with respect
-    to the state (a, b, p) that forward started from (it records that state, so the caller
-    need not keep it). float32 only; `out` may hold preallocated (dk, dv, dw, du, da, db,
-    dp)."""
+def backward_state(w, u, k, v, dy, fwd_workspace, dstate=None, workspace=None, out=None):
+    """(dk, dv, dw, du, da, db, dp) for a forward_state() call, whose workspace
+    `fwd_workspace` is required: the gradients of sum(dy * y) plus, with `dstate` = (da_T,
+    db_T) [B, C], of sum(da_T * a_T + db_T * b_T) for the final state (a_T, b_T, p_T) that
+    call returned (the next piece's da, db). da, db, dp [B, C] are the gradient with
+    respect to the state (a, b, p) the forward started from (it records both states, so the
+    caller need not keep them). float32 only; `out` may hold preallocated (dk, dv, dw, du,
+    da, db, dp)."""
     B, T, C, dev = _check_btc(w, u, k, v)
     _need(dy, "dy", 3, dev)
     if dy.shape != k.shape:
         raise ValueError("dy has the wrong shape")
+    dfa = dfb = None
+    if dstate is not None:
+        dfa, dfb = tuple(dstate)
+        for t, n in ((dfa, "da_T"), (dfb, "db_T")):
+            _need(t, n, 2, dev)
+            if tuple(t.shape) != (B, C):
+                raise ValueError("%s must have shape %s, got %s" % (n, (B, C), tuple(t.shape)))
     if fwd_workspace is None:
         raise ValueError("backward_state needs the workspace of the forward_state call")
     _check_ws(fwd_workspace, dev, "fwd_workspace")
@@ -348,8 +357,9 @@ def backward_state(w, u, k, v, dy, fwd_workspace, workspace=None, out=None):
             if tuple(t.shape) != sh:
                 raise ValueError("%s has the wrong shape" % n)
     _check(load_library().wkv_backward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
-                                             _ptr(dy), _ptr(fwd_workspace),
-                                             *(_ptr(g) for g in grads), _ptr(workspace),
+                                             _ptr(dy), _ptr(dfa), _ptr(dfb),
+                                             _ptr(fwd_workspace), *(_ptr(g) for g in grads),
+                                             _ptr(workspace),
                                              workspace.numel(), _stream(dev)))
     return grads
 

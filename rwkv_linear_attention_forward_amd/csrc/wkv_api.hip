@@ -404,7 +404,8 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
                   const float *w, const float *u, const void *k, const void *v, const void *dy,
                   const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,
                   float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream,
-                  float *ga = nullptr, float *gb = nullptr, float *gp = nullptr) {
+                  float *ga = nullptr, float *gb = nullptr, float *gp = nullptr,
+                  const float *dfa = nullptr, const float *dfb = nullptr) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (C == 0) return WKV_OK;
@@ -443,11 +444,14 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
         return WKV_ERR_INVALID_ARG;
     const void *outs[9] = {dk, dv, dw, du, workspace, dr, ga, gb, gp};
     const size_t osz[9] = {nb, nb, nc, nc, need, dr ? nb : 0, ns, ns, ns};
-    const void *ins[7] = {w, u, k, v, dy, fwd_workspace, r};
-    const size_t isz[7] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0,
-                           r ? nb : 0};
+    if (dfa != nullptr && (!aligned(dfa, 4, "dfa", fn) || !aligned(dfb, 4, "dfb", fn)))
+        return WKV_ERR_INVALID_ARG;
+    const size_t nf = dfa ? (size_t)(B * C) * 4u : 0;
+    const void *ins[9] = {w, u, k, v, dy, fwd_workspace, r, dfa, dfb};
+    const size_t isz[9] = {nc, nc, nb, nb, nb, fwd_workspace ? fwd_ws_bytes(B, T, C) : 0,
+                           r ? nb : 0, nf, nf};
     for (int i = 0; i < 9; ++i) {
-        for (int j = 0; j < 7; ++j)
+        for (int j = 0; j < 9; ++j)
             if (overlap(outs[i], osz[i], ins[j], isz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
         for (int j = i + 1; j < 9; ++j)
@@ -469,8 +473,8 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
         if (e != hipSuccess) return fail_hip(e, fn);
     }
     hipError_t e = wkvdev::launch_backward(B, T, C, fmt, w, u, k, v, dy, r, F, dk, dv, dr, dw,
-                                           du, ga, gb, gp, bwd_layout(B, T, C, own),
-                                           next_epoch(), st);
+                                           du, ga, gb, gp, dfa, dfb,
+                                           bwd_layout(B, T, C, own), next_epoch(), st);
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
 }
@@ -489,10 +493,10 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
 }
 
 int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                       const float *k, const float *v, const float *dy,
-                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
-                       float *da, float *db, float *dp, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       const float *k, const float *v, const float *dy, const float *dfa,
+                       const float *dfb, const void *fwd_workspace, float *dk, float *dv,
+                       float *dw, float *du, float *da, float *db, float *dp,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     static const char *fn = "wkv_backward_state";
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
@@ -500,6 +504,12 @@ int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const fl
         if (!nonnull(fwd_workspace, "fwd_workspace", fn) || !nonnull(da, "da", fn) ||
             !nonnull(db, "db", fn) || !nonnull(dp, "dp", fn))
             return WKV_ERR_INVALID_ARG;
+        if ((dfa == nullptr) != (dfb == nullptr))
+            return fail(WKV_ERR_INVALID_ARG, "%s: give both of dfa, dfb or neither", fn);
+        if (T == 0 && dfa != nullptr)
+            return fail(WKV_ERR_INVALID_ARG,
+                        "%s: T = 0 records no state; the final state's cotangent is the "
+                        "initial state's", fn);
         if (!aligned(da, 4, "da", fn) || !aligned(db, 4, "db", fn) || !aligned(dp, 4, "dp", fn))
             return WKV_ERR_INVALID_ARG;
         const size_t ns = (size_t)(B * C) * 4u;
@@ -516,7 +526,8 @@ int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const fl
         }
     }
     return backward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr, fwd_workspace,
-                         dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream, da, db, dp);
+                         dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream, da, db, dp,
+                         dfa, dfb);
 }
 
 int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -700,31 +700,90 @@ static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int
                            ddr, dw, du, L.flags, L.ragg, L.rincl, L.part);
 }
 
+// Cotangent of the final state. With (a_T, b_T, p_T) the state the forward returned after
+// token T-1 (A_T = a_T e^{p_T}, B_T = b_T e^{p_T}) and da_T, db_T the gradient of L with
+// respect to a_T, b_T, dL/dA_T = da_T e^{-p_T} (B alike). Since A_T = sum_i e^{k_i - (T-1-i) w}
+// v_i + e^{-T w} A_0 (B_T without the v_i), token i gains, with c_i = e^{k_i - (T-1-i) w - p_T},
+//   dv_i += c_i da_T,   dk_i += c_i (da_T v_i + db_T),   dw -= (T-1-i) c_i (da_T v_i + db_T),
+// and the state before token 0 adds -T e^{-T w} (dA_T A_0 + dB_T B_0) to dw. One wave per
+// 64 channels x one 64-token window; the window's dw term is added to the backward's partial
+// for the same window, which is then summed in the usual fixed order. (c_i <= b_T: b_T is the
+// sum of all of them, so no exponential overflows.)
+constexpr int kCotWindow = kBwdWindow;
+__global__ __launch_bounds__(256) void wkv_final_cot_kernel(
+    int64_t B, int64_t T, int64_t C, int64_t ngrp, int64_t nseg, const float *__restrict__ w,
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dfa,
+    const float *__restrict__ dfb, const float *__restrict__ fin, const double *__restrict__ init,
+    float *__restrict__ dk, float *__restrict__ dv, double *__restrict__ part) {
+    const int lane = (int)threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+    if (unit >= B * ngrp * nseg) return;
+    const int64_t s = unit % nseg, bg = unit / nseg;
+    const int64_t b = bg / ngrp, c = (bg - b * ngrp) * 64 + lane;
+    if (c >= C) return;
+    const int64_t n = B * C, ic = b * C + c;
+    const double dA = (double)dfa[ic], dB = (double)dfb[ic], pT = (double)fin[2 * n + ic];
+    const double wd = (double)w[c];
+    const int64_t t0 = s * kCotWindow, t1 = t0 + kCotWindow < T ? t0 + kCotWindow : T;
+    double acc = 0.0;
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t i = (b * T + t) * C + c;
+        const double age = (double)(T - 1 - t);
+        const double cf = exp2_64(((double)k[i] - fma(age, wd, pT)) * kLog2eD);
+        const double q = fma(dA, (double)v[i], dB) * cf;
+        dv[i] = (float)fma(cf, dA, (double)dv[i]);
+        dk[i] = (float)((double)dk[i] + q);
+        acc = fma(age, q, acc);
+    }
+    double dwt = -acc;
+    if (s == 0) {
+        const Carry st = get_cin(init, n, ic);
+        const double f = exp2_64(-fma((double)T, wd, pT) * kLog2eD + st.P);
+        dwt -= (double)T * f * fma(dA, st.a, dB * st.b);
+    }
+    part[(b * nseg + s) * C + c] += dwt;
+}
+
 // Gradient with respect to the state before token 0. That state holds A0 = a e^p and
 // B0 = b e^p, which reach token t as e^{-t w} A0 and e^{-t w} B0, so dL/dA0 = G_{-1} and
 // dL/dB0 = -H_{-1}: the future sums over the whole sequence, which the backward leaves as
 // window 0's reverse inclusive record. With the state (a, b, 2^P = e^p) as the forward
-// recorded it: da = G e^p, db = -H e^p, dp = (a G - b H) e^p. One lane per (b, c).
+// recorded it: da = G e^p, db = -H e^p, dp = (a G - b H) e^p. A cotangent (da_T, db_T) of
+// the final state reaches A0 as e^{-T w} dA_T: da gains da_T e^{-T w + p - p_T} (db alike),
+// dp gains a times that plus b times db's. One lane per (b, c).
 __global__ __launch_bounds__(256) void wkv_state_grad_kernel(
-    int64_t n, int64_t C, int64_t nseg, const double *__restrict__ init,
-    const double *__restrict__ rincl, float *__restrict__ ga, float *__restrict__ gb,
-    float *__restrict__ gp) {
+    int64_t n, int64_t T, int64_t C, int64_t nseg, const double *__restrict__ init,
+    const double *__restrict__ rincl, const float *__restrict__ w,
+    const float *__restrict__ dfa, const float *__restrict__ dfb, const float *__restrict__ fin,
+    float *__restrict__ ga, float *__restrict__ gb, float *__restrict__ gp) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int64_t b = i / C, c = i - b * C;
     const RevCarry fut = get_rrec(rincl, n * nseg, b * nseg * C + c);
     const Carry st = get_cin(init, n, i);
     const double sc = exp2_64(fut.r + st.P);
-    ga[i] = (float)(fut.g * sc);
-    gb[i] = (float)(-fut.h * sc);
-    gp[i] = (float)(fma(st.a, fut.g, -st.b * fut.h) * sc);
+    double da = fut.g * sc, db = -fut.h * sc;
+    double dp = fma(st.a, fut.g, -st.b * fut.h) * sc;
+    if (dfa != nullptr) {
+        const double f =
+            exp2_64(-fma((double)T, (double)w[c], (double)fin[2 * n + i]) * kLog2eD + st.P);
+        const double xa = (double)dfa[i] * f, xb = (double)dfb[i] * f;
+        da += xa;
+        db += xb;
+        dp += fma(st.a, xa, st.b * xb);
+    }
+    ga[i] = (float)da;
+    gb[i] = (float)db;
+    gp[i] = (float)dp;
 }
 
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                            const float *u, const void *k, const void *v, const void *dy,
                            const void *r, const FwdLayout &F, void *dk, void *dv, void *dr,
                            float *dw, float *du, float *ga, float *gb, float *gp,
-                           const BwdLayout &L, uint64_t epoch, hipStream_t stream) {
+                           const float *dfa, const float *dfb, const BwdLayout &L,
+                           uint64_t epoch, hipStream_t stream) {
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
@@ -740,6 +799,16 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
                                     r, fc, dk, dv, dr, dw, du);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (dfa != nullptr) {  // fp32 only (the caller checks)
+        const int64_t cunits = nbg * L.nseg;
+        hipLaunchKernelGGL(wkv_final_cot_kernel, dim3((unsigned)((cunits + 3) / 4)), dim3(256), 0,
+                           stream, B, T, C, (int64_t)ngrp, L.nseg, w,
+                           static_cast<const float *>(k), static_cast<const float *>(v), dfa,
+                           dfb, F.fin, F.init, static_cast<float *>(dk),
+                           static_cast<float *>(dv), L.part);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),
                        dim3(kReduceCh * kReduceSlices), 0,
                        stream, B * L.nseg, C, L.part, dw, du);
@@ -747,7 +816,8 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     if (e != hipSuccess || ga == nullptr) return e;
     const int64_t n = B * C;
     hipLaunchKernelGGL(wkv_state_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       stream, n, C, L.nseg, F.init, L.rincl, ga, gb, gp);
+                       stream, n, T, C, L.nseg, F.init, L.rincl, w, dfa, dfb, F.fin, ga, gb,
+                       gp);
     return hipGetLastError();
 }
 

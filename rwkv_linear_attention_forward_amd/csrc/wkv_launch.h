@@ -99,11 +99,14 @@ hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *
 // dy, r, dk, dv, dr are in storage format `fmt`; dw, du are fp32.
 // With `ga`, `gb`, `gp` ([B][C], all three or none) it also gives the gradient with respect
 // to the state (a, b, p) the forward started from (F's record of the carry before token 0).
+// With `dfa`, `dfb` ([B][C], both or none; fp32 format only) L also has the terms
+// dfa * a_T + dfb * b_T of the final state F.fin the forward returned (p_T held fixed).
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                            const float *u, const void *k, const void *v, const void *dy,
                            const void *r, const FwdLayout &F, void *dk, void *dv, void *dr,
                            float *dw, float *du, float *ga, float *gb, float *gp,
-                           const BwdLayout &L, uint64_t epoch, hipStream_t stream);
+                           const float *dfa, const float *dfb, const BwdLayout &L,
+                           uint64_t epoch, hipStream_t stream);
 
 // dw = du = 0 over C channels (backward of an empty batch or sequence).
 hipError_t launch_zero2(float *dw, float *du, int64_t C, hipStream_t stream);

@@ -41,3 +41,38 @@ def backward_state_grad(w, u, k, v, dy, state):
     dk, dv, dw, du = oracle.backward_direct(w, u, kk, vv, g)
     dk0, dv0 = dk[:, 0], dv[:, 0]
     return (dk[:, 1:], dv[:, 1:], dw, du, dv0 / b, dk0 / b - dv0 * a / (b * b), dk0)
+
+
+def final_state_terms(w, u, k, v, state, dA, dB):
+    """The gradients of sum_{b,c} (dA A_T + dB B_T), (A_T, B_T) the state after the last
+    token, in the order (dk, dv, dw, du, da, db, dp). From the recursion unrolled: A_T =
+    sum_i e^{k_i - (T-1-i) w} v_i + e^{-T w} A_0 with A_0 = a e^p (B alike, without v).
+    dA, dB [B, C] may be tiny and k large: every product is formed as one exponential of a
+    sum of logs."""
+    w = np.asarray(w, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    a, b, p = (np.asarray(s, np.float64) for s in state)
+    dA = np.asarray(dA, np.float64)
+    dB = np.asarray(dB, np.float64)
+    T = k.shape[1]
+    age = (T - 1 - np.arange(T, dtype=np.float64))[None, :, None]
+    x = k - age * w[None, None, :]
+    lA = np.log(np.abs(dA))[:, None, :]
+    lB = np.log(np.abs(dB))[:, None, :]
+    cA = np.sign(dA)[:, None, :] * np.exp(x + lA)   # e^{k_i - age w} dA
+    cB = np.sign(dB)[:, None, :] * np.exp(x + lB)
+    dv = cA
+    dk = cA * v + cB
+    dw = -np.sum(age * dk, axis=(0, 1))
+    f = np.exp(-T * w[None, :] + p)                  # e^{-T w} e^p
+    xa, xb = dA * f, dB * f                          # into da, db
+    dw = dw - T * np.sum(xa * a + xb * b, axis=0)
+    return dk, dv, dw, np.zeros_like(w), xa, xb, a * xa + b * xb
+
+
+def backward_state_grad_cot(w, u, k, v, dy, state, dA, dB):
+    """backward_state_grad for L = sum(dy * y) + sum(dA A_T + dB B_T)."""
+    base = backward_state_grad(w, u, k, v, dy, state)
+    extra = final_state_terms(w, u, k, v, state, dA, dB)
+    return tuple(x + y for x, y in zip(base, extra))

@@ -246,9 +246,9 @@ def test_backward_state_rejects_bad_arguments(pkg):
     lib = pkg.load_library()
     g = [ctypes.c_void_p(0x4000000 + 0x100000 * i) for i in range(16)]
 
-    def call(B=2, T=3, C=4, fws=g[5], da=g[12], db=g[13], dp=g[14]):
-        return lib.wkv_backward_state(B, T, C, g[0], g[1], g[2], g[3], g[4], fws, g[6], g[7],
-                                      g[8], g[9], da, db, dp, g[11], 1 << 40, None)
+    def call(B=2, T=3, C=4, fws=g[5], da=g[12], db=g[13], dp=g[14], dfa=None, dfb=None):
+        return lib.wkv_backward_state(B, T, C, g[0], g[1], g[2], g[3], g[4], dfa, dfb, fws,
+                                      g[6], g[7], g[8], g[9], da, db, dp, g[11], 1 << 40, None)
 
     assert call(T=-1) == pkg.WKV_ERR_INVALID_ARG
     assert call(fws=None) == pkg.WKV_ERR_INVALID_ARG
@@ -264,7 +264,15 @@ def test_backward_state_rejects_bad_arguments(pkg):
     assert b"overlaps an input" in lib.wkv_last_error()
     assert call(dp=g[6]) == pkg.WKV_ERR_INVALID_ARG
     assert b"two outputs overlap" in lib.wkv_last_error()
-    assert lib.wkv_backward_state(2, 3, 0, *([None] * 14), 0, None) == pkg.WKV_OK
+    # the final state's cotangent: both or neither, not for T = 0, not on an output
+    assert call(dfa=g[10]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"both of dfa, dfb" in lib.wkv_last_error()
+    assert call(T=0, dfa=g[10], dfb=g[15]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"T = 0" in lib.wkv_last_error()
+    assert call(dfa=g[10], dfb=ctypes.c_void_p(g[15].value + 1)) == pkg.WKV_ERR_INVALID_ARG
+    assert call(dfa=g[10], dfb=g[13]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"overlaps an input" in lib.wkv_last_error()
+    assert lib.wkv_backward_state(2, 3, 0, *([None] * 16), 0, None) == pkg.WKV_OK
 
 
 def test_decode_rejects_bad_arguments(pkg):

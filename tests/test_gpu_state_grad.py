@@ -136,3 +136,88 @@ def test_full_layer_state_gradient(wkv, dev):
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "l3b " + n, floor=floor))
     assert torch.count_nonzero(got[0][:, Tp:]).item() == 0
     _log("l3b (loss on the first %d tokens)" % Tp, worst)
+
+
+def _cot_case(wkv, dev, x, st, seed):
+    """GPU forward_state, then backward_state with a cotangent of the final state. The
+    cotangent is drawn on (A_T, B_T) from the oracle's own final state (dA = r e^{-p_T}) and
+    handed to the GPU in its decode convention (dfa = dA e^{p_T} with the GPU's p_T)."""
+    import torch
+    from oracle import forward_rescaled
+    B, T, C = x["k"].shape
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v", "dy")}
+    ws = wkv.forward_workspace(B, T, C, dev)
+    sg = [_t(dev, s) for s in st]
+    wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *sg, workspace=ws)
+    _, (_, _, po) = forward_rescaled(x["w"], x["u"], x["k"], x["v"], st)
+    rng = np.random.default_rng(seed)
+    ra = rng.standard_normal((B, C)) * 0.5
+    rb = rng.standard_normal((B, C)) * 0.5
+    dA, dB = ra * np.exp(-po), rb * np.exp(-po)
+    pg = sg[2].cpu().numpy().astype(np.float64)
+    dfa = _t(dev, (ra * np.exp(pg - po)).astype(np.float32))
+    dfb = _t(dev, (rb * np.exp(pg - po)).astype(np.float32))
+    got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws, dstate=(dfa, dfb))
+    torch.cuda.synchronize()
+    return got, dA, dB
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 37, 70), (1, 64, 64), (3, 129, 130),
+                                   (2, 300, 65), (1, 1000, 256)])
+@pytest.mark.parametrize("prange", [(-3.0, 3.0), (20.0, 30.0)])
+def test_final_state_cotangent_parity(wkv, dev, B, T, C, prange):
+    """L = sum(dy * y) + sum(dA A_T + dB B_T): every gradient against the oracle's direct
+    backward plus the final state's terms (tests/state_ref.py, pinned by finite differences
+    of the oracle)."""
+    from state_ref import backward_state_grad_cot
+    x = wkv_inputs.generate("l3b", seed=100 + B * T + C, B=B, T=T, C=C)
+    st = wkv_inputs.random_state(B, C, seed=T + 2 * C, p_range=prange)
+    got, dA, dB = _cot_case(wkv, dev, x, st, seed=T + C)
+    ref = backward_state_grad_cot(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB)
+    worst = 0.0
+    for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
+        r = np.asarray(r, np.float64)
+        floor = 0.1 if n[1] in "kvwu" else 0.1 * max(float(np.max(np.abs(r))), 1e-300)
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s B=%d T=%d C=%d p in %s"
+                                            % (n, B, T, C, prange), floor=floor))
+    _log("final-state cotangent B=%d T=%d C=%d p in %s" % (B, T, C, prange), worst)
+
+
+@pytest.mark.parametrize("cuts", [(0, 97, 300), (0, 64, 128, 300), (0, 1, 2, 300)])
+def test_pieces_chain_to_the_whole_sequence(wkv, dev, cuts):
+    """A sequence run forward in pieces (each from the state the last one left) and then
+    backward from the last piece to the first, each piece's da, db handed to the one before
+    as its final state's cotangent: the gradients of the whole sequence, from its initial
+    state, against the oracle's direct backward of the whole."""
+    import torch
+    B, C = 2, 130
+    T = cuts[-1]
+    x = wkv_inputs.generate("l3b", seed=110 + len(cuts), B=B, T=T, C=C)
+    st = wkv_inputs.random_state(B, C, seed=111, p_range=(-3.0, 3.0))
+    t = {n: _t(dev, x[n]) for n in ("w", "u", "k", "v", "dy")}
+    sg = [_t(dev, s) for s in st]
+    pieces = []
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        sl = {n: t[n][:, t0:t1].contiguous() for n in ("k", "v", "dy")}
+        ws = wkv.forward_workspace(B, t1 - t0, C, dev)
+        wkv.forward_state(t["w"], t["u"], sl["k"], sl["v"], *sg, workspace=ws)
+        pieces.append((sl, ws))
+    grads = [None] * len(pieces)
+    dstate = None
+    for i in range(len(pieces) - 1, -1, -1):
+        sl, ws = pieces[i]
+        grads[i] = wkv.backward_state(t["w"], t["u"], sl["k"], sl["v"], sl["dy"], ws,
+                                      dstate=dstate)
+        dstate = (grads[i][4], grads[i][5])
+    torch.cuda.synchronize()
+    ref = backward_state_grad(x["w"], x["u"], x["k"], x["v"], x["dy"], st)
+    got = [torch.cat([g[0] for g in grads], dim=1), torch.cat([g[1] for g in grads], dim=1),
+           sum(g[2].double() for g in grads), sum(g[3].double() for g in grads),
+           grads[0][4], grads[0][5], grads[0][6]]
+    worst = 0.0
+    for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
+        r = np.asarray(r, np.float64)
+        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s cuts=%s" % (n, cuts),
+                                            floor=floor))
+    _log("pieces %s" % (cuts,), worst)

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from state_ref import backward_state_grad, backward_with_state, prepend_state_token as _prepend
+from state_ref import (backward_state_grad, backward_state_grad_cot, backward_with_state,
+                       prepend_state_token as _prepend)
 
 
 def _rand(B, T, C, seed, kscale=1.0):
@@ -140,3 +141,63 @@ def test_state_gradient_closed_form_single_token():
     np.testing.assert_allclose(got[4], g * ep, rtol=1e-12)
     np.testing.assert_allclose(got[5], -hh * ep, rtol=1e-12)
     np.testing.assert_allclose(got[6], (a * g - b * hh) * ep, rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_final_state_cotangent_finite_differences(T):
+    # L = sum(dy * y) + sum(dA A_T + dB B_T), (A_T, B_T) = (a_T e^{p_T}, b_T e^{p_T}) the
+    # oracle's final state: every gradient against central differences of the oracle
+    rng, w, u, k, v = _rand(2, T, 3, 60 + T, kscale=1.5)
+    st = _state(rng, 2, 3)
+    dy = rng.standard_normal(k.shape)
+    dA = rng.standard_normal((2, 3)) * 0.3
+    dB = rng.standard_normal((2, 3)) * 0.3
+    got = backward_state_grad_cot(w, u, k, v, dy, st, dA, dB)
+
+    def loss(w_, u_, k_, v_, s_):
+        y, (a, b, p) = oracle.forward_rescaled(w_, u_, k_, v_, s_)
+        return float(np.sum(dy * y) + np.sum(dA * a * np.exp(p) + dB * b * np.exp(p)))
+
+    args = [w, u, k, v, list(st)]
+    # (argument, state field, index in got): w, u, k, v, then a, b, p
+    flat = [(0, None, 2), (1, None, 3), (2, None, 0), (3, None, 1), (4, 0, 4), (4, 1, 5),
+            (4, 2, 6)]
+    for i, j, slot in flat:
+        x = args[i] if j is None else args[4][j]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-6 * max(1.0, abs(x[idx]))
+            vals = []
+            for sgn in (1.0, -1.0):
+                xx = x.copy()
+                xx[idx] += sgn * h
+                aa = [a_ if not isinstance(a_, list) else list(a_) for a_ in args]
+                if j is None:
+                    aa[i] = xx
+                else:
+                    aa[4][j] = xx
+                vals.append(loss(aa[0], aa[1], aa[2], aa[3], tuple(aa[4])))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        np.testing.assert_allclose(got[slot], fd, rtol=1e-6, atol=1e-8,
+                                   err_msg="slot %d" % slot)
+
+
+def test_final_state_cotangent_chains_two_pieces():
+    # the gradient of a sequence run in two pieces: the second piece's state gradient
+    # (da, db at its start) is the cotangent of the first piece's final state
+    rng, w, u, k, v = _rand(2, 11, 3, 70, kscale=1.5)
+    st = _state(rng, 2, 3)
+    dy = rng.standard_normal(k.shape)
+    whole = backward_state_grad(w, u, k, v, dy, st)
+    T1 = 4
+    _, mid = oracle.forward_rescaled(w, u, k[:, :T1], v[:, :T1], st)
+    g2 = backward_state_grad(w, u, k[:, T1:], v[:, T1:], dy[:, T1:], mid)
+    a1, b1, p1 = mid
+    dA, dB = g2[4] * np.exp(-p1), g2[5] * np.exp(-p1)
+    g1 = backward_state_grad_cot(w, u, k[:, :T1], v[:, :T1], dy[:, :T1], st, dA, dB)
+    np.testing.assert_allclose(np.concatenate([g1[0], g2[0]], axis=1), whole[0], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate([g1[1], g2[1]], axis=1), whole[1], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(g1[2] + g2[2], whole[2], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(g1[3] + g2[3], whole[3], rtol=1e-9, atol=1e-12)
+    for i in (4, 5, 6):
+        np.testing.assert_allclose(g1[i], whole[i], rtol=1e-9, atol=1e-12)
