@@ -356,6 +356,21 @@ def bench_forward_state(wkv, torch, dev, x, steps=100, warmup=100):
     us_inf = timed(lambda: wkv.forward_infer(t["w"], t["u"], t["k"], t["v"], state=st,
                                              workspace=ws, out=y))
     ok = bool(torch.isfinite(y).all()) and all(bool(torch.isfinite(a).all()) for a in st)
+    # its backward (a sequence trained in pieces): the state gradient alone, then with the
+    # next piece's cotangent of the final state (a second pass over k, v, dk, dv)
+    wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws, out=y)
+    dy = torch.from_numpy(x["dy"]).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    dstate = tuple(torch.randn(B, C, device=dev, generator=g) * 0.1 for _ in range(2))
+    bws = torch.empty(max(16, wkv.backward_workspace_size(B, T, C, True)), dtype=torch.uint8,
+                      device=dev)
+    grads = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], dy, ws, workspace=bws)
+    us_b = timed(lambda: wkv.backward_state(t["w"], t["u"], t["k"], t["v"], dy, ws,
+                                            workspace=bws, out=grads))
+    us_bc = timed(lambda: wkv.backward_state(t["w"], t["u"], t["k"], t["v"], dy, ws,
+                                             dstate=dstate, workspace=bws, out=grads))
+    ok = ok and all(bool(torch.isfinite(a).all()) for a in grads)
     alg = 12 * B * T * C + 24 * B * C
     gbps = alg / (us * 1e-6) / 1e9
     gbps_inf = alg / (us_inf * 1e-6) / 1e9
@@ -363,7 +378,8 @@ def bench_forward_state(wkv, torch, dev, x, steps=100, warmup=100):
             "us": us, "elem_per_s": B * T * C / (us * 1e-6), "algorithmic_gbps": gbps,
             "frac_of_peak": gbps / PEAK_GBPS, "infer_us": us_inf,
             "infer_elem_per_s": B * T * C / (us_inf * 1e-6),
-            "infer_frac_of_peak": gbps_inf / PEAK_GBPS, "steps": steps, "outputs_finite": ok}
+            "infer_frac_of_peak": gbps_inf / PEAK_GBPS, "backward_state_us": us_b,
+            "backward_state_cotangent_us": us_bc, "steps": steps, "outputs_finite": ok}
 
 
 def bench_gated(wkv, torch, dev, x, steps=100, warmup=100):

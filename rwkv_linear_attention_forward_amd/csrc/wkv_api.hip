@@ -521,7 +521,7 @@ int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const fl
             if (rc != WKV_OK) return rc;
             hipStream_t st = static_cast<hipStream_t>(stream);
             hipError_t e = wkvdev::launch_zero2(da, db, B * C, st);
-            if (e == hipSuccess) e = wkvdev::launch_zero2(dp, dp, B * C, st);
+            if (e == hipSuccess) e = wkvdev::launch_zero2(dp, da, B * C, st);  // da again
             if (e != hipSuccess) return fail_hip(e, fn);
         }
     }

@@ -705,44 +705,66 @@ static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int
 // respect to a_T, b_T, dL/dA_T = da_T e^{-p_T} (B alike). Since A_T = sum_i e^{k_i - (T-1-i) w}
 // v_i + e^{-T w} A_0 (B_T without the v_i), token i gains, with c_i = e^{k_i - (T-1-i) w - p_T},
 //   dv_i += c_i da_T,   dk_i += c_i (da_T v_i + db_T),   dw -= (T-1-i) c_i (da_T v_i + db_T),
-// and the state before token 0 adds -T e^{-T w} (dA_T A_0 + dB_T B_0) to dw. One wave per
-// 64 channels x one 64-token window; the window's dw term is added to the backward's partial
-// for the same window, which is then summed in the usual fixed order. (c_i <= b_T: b_T is the
-// sum of all of them, so no exponential overflows.)
+// and the state before token 0 adds -T e^{-T w} (dA_T A_0 + dB_T B_0) to dw. A workgroup
+// takes 64 channels x one 64-token window, a wave 16 of its tokens (all loads issued before
+// the arithmetic); the window's dw term, its waves' sums added in a fixed order, goes into
+// the backward's partial for the same window, which is then reduced as usual. (c_i <= b_T:
+// b_T is the sum of all of them, so no exponential overflows.)
 constexpr int kCotWindow = kBwdWindow;
-__global__ __launch_bounds__(256) void wkv_final_cot_kernel(
+constexpr int kCotWaves = 4;
+constexpr int kCotPart = kCotWindow / kCotWaves;
+__global__ __launch_bounds__(kCotWaves * 64) void wkv_final_cot_kernel(
     int64_t B, int64_t T, int64_t C, int64_t ngrp, int64_t nseg, const float *__restrict__ w,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dfa,
     const float *__restrict__ dfb, const float *__restrict__ fin, const double *__restrict__ init,
     float *__restrict__ dk, float *__restrict__ dv, double *__restrict__ part) {
-    const int lane = (int)threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
-    if (unit >= B * ngrp * nseg) return;
-    const int64_t s = unit % nseg, bg = unit / nseg;
+    __shared__ double red[kCotWaves][64];
+    const int lane = (int)threadIdx.x & 63, q = (int)threadIdx.x >> 6;
+    const int64_t s = (int64_t)blockIdx.x % nseg, bg = (int64_t)blockIdx.x / nseg;
     const int64_t b = bg / ngrp, c = (bg - b * ngrp) * 64 + lane;
-    if (c >= C) return;
-    const int64_t n = B * C, ic = b * C + c;
+    const bool cval = c < C;
+    const int64_t cc = cval ? c : C - 1;
+    const int64_t n = B * C, ic = b * C + cc;
     const double dA = (double)dfa[ic], dB = (double)dfb[ic], pT = (double)fin[2 * n + ic];
-    const double wd = (double)w[c];
-    const int64_t t0 = s * kCotWindow, t1 = t0 + kCotWindow < T ? t0 + kCotWindow : T;
+    const double wd = (double)w[cc];
+    const int64_t t0 = s * kCotWindow + q * kCotPart;
+    float kv[kCotPart], vv[kCotPart], gk[kCotPart], gv[kCotPart];
+#pragma unroll
+    for (int j = 0; j < kCotPart; ++j) {
+        const int64_t t = t0 + j < T ? t0 + j : T - 1;
+        const int64_t i = (b * T + t) * C + cc;
+        kv[j] = k[i];
+        vv[j] = v[i];
+        gk[j] = dk[i];
+        gv[j] = dv[i];
+    }
     double acc = 0.0;
-#pragma unroll 4
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t i = (b * T + t) * C + c;
-        const double age = (double)(T - 1 - t);
-        const double cf = exp2_64(((double)k[i] - fma(age, wd, pT)) * kLog2eD);
-        const double q = fma(dA, (double)v[i], dB) * cf;
-        dv[i] = (float)fma(cf, dA, (double)dv[i]);
-        dk[i] = (float)((double)dk[i] + q);
-        acc = fma(age, q, acc);
+#pragma unroll
+    for (int j = 0; j < kCotPart; ++j) {
+        const int64_t t = t0 + j;
+        if (cval && t < T) {
+            const int64_t i = (b * T + t) * C + c;
+            const double age = (double)(T - 1 - t);
+            const double cf = exp2_64(((double)kv[j] - fma(age, wd, pT)) * kLog2eD);
+            const double qq = fma(dA, (double)vv[j], dB) * cf;
+            dv[i] = (float)fma(cf, dA, (double)gv[j]);
+            dk[i] = (float)((double)gk[j] + qq);
+            acc = fma(age, qq, acc);
+        }
     }
-    double dwt = -acc;
-    if (s == 0) {
-        const Carry st = get_cin(init, n, ic);
-        const double f = exp2_64(-fma((double)T, wd, pT) * kLog2eD + st.P);
-        dwt -= (double)T * f * fma(dA, st.a, dB * st.b);
+    red[q][lane] = -acc;
+    __syncthreads();
+    if (q == 0 && cval) {
+        double dwt = red[0][lane];
+#pragma unroll
+        for (int r = 1; r < kCotWaves; ++r) dwt += red[r][lane];
+        if (s == 0) {
+            const Carry st = get_cin(init, n, ic);
+            const double f = exp2_64(-fma((double)T, wd, pT) * kLog2eD + st.P);
+            dwt -= (double)T * f * fma(dA, st.a, dB * st.b);
+        }
+        part[(b * nseg + s) * C + c] += dwt;
     }
-    part[(b * nseg + s) * C + c] += dwt;
 }
 
 // Gradient with respect to the state before token 0. That state holds A0 = a e^p and
@@ -800,8 +822,8 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dfa != nullptr) {  // fp32 only (the caller checks)
-        const int64_t cunits = nbg * L.nseg;
-        hipLaunchKernelGGL(wkv_final_cot_kernel, dim3((unsigned)((cunits + 3) / 4)), dim3(256), 0,
+        hipLaunchKernelGGL(wkv_final_cot_kernel, dim3((unsigned)(nbg * L.nseg)),
+                           dim3(kCotWaves * 64), 0,
                            stream, B, T, C, (int64_t)ngrp, L.nseg, w,
                            static_cast<const float *>(k), static_cast<const float *>(v), dfa,
                            dfb, F.fin, F.init, static_cast<float *>(dk),
