@@ -140,7 +140,8 @@ int wkv_forward_infer(int dtype, int64_t B, int64_t T, int64_t C, const float *w
                       float *a, float *b, float *p, void *workspace, size_t workspace_bytes,
                       void *stream);
 
-/* Bytes of device scratch that wkv_backward and wkv_backward_gated need. With have_fwd_workspace != 0 the caller
+/* Bytes of device scratch that wkv_backward, wkv_backward_gated, wkv_backward_typed and
+ * wkv_backward_state need. With have_fwd_workspace != 0 the caller
  * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
  * window states are recomputed into this workspace, which then also covers
  * wkv_forward_workspace_size(B, T, C). */
@@ -178,7 +179,8 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
  * dp = a da + b db always (L depends on a, p only through a e^p). A forward from the empty
  * state (wkv_forward, or a = b = 0) gives da = db = dp = 0. Without dfa, dfb: dk, dv, dw,
  * du are bitwise those of wkv_backward with the same arguments; with them the final
- * state's terms are added by a second pass over k, v, dk, dv. T == 0 writes zero da, db,
+ * state acts as one more token at T in the future sums of all earlier tokens (the reverse
+ * scan starts from it), at about 6% more time. T == 0 writes zero da, db,
  * dp, dw, du, but is refused with dfa, dfb (a zero-length piece records no state: its
  * final state's cotangent is its initial state's, which the caller passes on). Outputs
  * must not overlap each other or any input. fp32 only. */

@@ -154,7 +154,8 @@ size_t bwd_own_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t n = (size_t)B * nseg * (size_t)C;
     return round_up((size_t)B * ngrp * nseg * 8u, 256) +
            2 * round_up(n * (wkvdev::kRevFields * sizeof(double)), 256) +
-           round_up(n * 2 * sizeof(double), 256);
+           round_up(n * 2 * sizeof(double), 256) +
+           round_up((size_t)B * (size_t)C * (wkvdev::kRevFields * sizeof(double)), 256);
 }
 
 wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
@@ -170,6 +171,8 @@ wkvdev::BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     L.rincl = reinterpret_cast<double *>(p);
     p += round_up(n * (wkvdev::kRevFields * sizeof(double)), 256);
     L.part = reinterpret_cast<double *>(p);
+    p += round_up(n * 2 * sizeof(double), 256);
+    L.tail = reinterpret_cast<double *>(p);
     return L;
 }
 

@@ -511,7 +511,13 @@ __global__ __launch_bounds__(NW * 64, 3) void wkv_backward_kernel(
     // published (or past the sequence end), making sure every window in between has its
     // reverse aggregate in memory, then fold those back in order: bitwise the sequential
     // chain rincl[s] = rfold(rincl[s+1], ragg[s]) whatever the timing.
+    // beyond the last window the future is zero, or what a cotangent of the final state puts
+    // there (as sums at the window end, F.tail)
+    auto beyond = [&]() {
+        return F.tail != nullptr ? get_rrec(F.tail, F.nrec / F.nseg, bidx * C + cl) : rev_zero();
+    };
     RevCarry fut = rev_zero();
+    if (s == nseg - 1) fut = beyond();
     if (s < nseg - 1) {
         int64_t j = s + 1;
         int it = 0;
@@ -560,7 +566,7 @@ __global__ __launch_bounds__(NW * 64, 3) void wkv_backward_kernel(
                                                           dw_x);
             window_rev_stage<NW, CH>(sh, rs2, q, lane);
         }
-        if (j < nseg) fut = get_rrec(rincl, nrec, (bidx * nseg + j) * C + cl);
+        fut = j < nseg ? get_rrec(rincl, nrec, (bidx * nseg + j) * C + cl) : beyond();
         for (int64_t m = j - 1; m > s; --m)
             fut = rfollow(fut, get_rrec(ragg, nrec, (bidx * nseg + m) * C + cl),
                           (double)WIN * K.w2());
@@ -702,102 +708,82 @@ static void launch_backward_io(int64_t units, hipStream_t stream, int64_t B, int
 
 // Cotangent of the final state. With (a_T, b_T, p_T) the state the forward returned after
 // token T-1 (A_T = a_T e^{p_T}, B_T = b_T e^{p_T}) and da_T, db_T the gradient of L with
-// respect to a_T, b_T, dL/dA_T = da_T e^{-p_T} (B alike). Since A_T = sum_i e^{k_i - (T-1-i) w}
-// v_i + e^{-T w} A_0 (B_T without the v_i), token i gains, with c_i = e^{k_i - (T-1-i) w - p_T},
-//   dv_i += c_i da_T,   dk_i += c_i (da_T v_i + db_T),   dw -= (T-1-i) c_i (da_T v_i + db_T),
-// and the state before token 0 adds -T e^{-T w} (dA_T A_0 + dB_T B_0) to dw. A workgroup
-// takes 64 channels x one 64-token window, a wave 16 of its tokens (all loads issued before
-// the arithmetic); the window's dw term, its waves' sums added in a fixed order, goes into
-// the backward's partial for the same window, which is then reduced as usual. (c_i <= b_T:
-// b_T is the sum of all of them, so no exponential overflows.)
-constexpr int kCotWindow = kBwdWindow;
-constexpr int kCotWaves = 4;
-constexpr int kCotPart = kCotWindow / kCotWaves;
-__global__ __launch_bounds__(kCotWaves * 64) void wkv_final_cot_kernel(
-    int64_t B, int64_t T, int64_t C, int64_t ngrp, int64_t nseg, const float *__restrict__ w,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ dfa,
-    const float *__restrict__ dfb, const float *__restrict__ fin, const double *__restrict__ init,
-    float *__restrict__ dk, float *__restrict__ dv, double *__restrict__ part) {
-    __shared__ double red[kCotWaves][64];
-    const int lane = (int)threadIdx.x & 63, q = (int)threadIdx.x >> 6;
-    const int64_t s = (int64_t)blockIdx.x % nseg, bg = (int64_t)blockIdx.x / nseg;
-    const int64_t b = bg / ngrp, c = (bg - b * ngrp) * 64 + lane;
-    const bool cval = c < C;
-    const int64_t cc = cval ? c : C - 1;
-    const int64_t n = B * C, ic = b * C + cc;
-    const double dA = (double)dfa[ic], dB = (double)dfb[ic], pT = (double)fin[2 * n + ic];
-    const double wd = (double)w[cc];
-    const int64_t t0 = s * kCotWindow + q * kCotPart;
-    float kv[kCotPart], vv[kCotPart], gk[kCotPart], gv[kCotPart];
-#pragma unroll
-    for (int j = 0; j < kCotPart; ++j) {
-        const int64_t t = t0 + j < T ? t0 + j : T - 1;
-        const int64_t i = (b * T + t) * C + cc;
-        kv[j] = k[i];
-        vv[j] = v[i];
-        gk[j] = dk[i];
-        gv[j] = dv[i];
+// respect to a_T, b_T: dL/dA_T = da_T e^{-p_T} (B alike). A_T = sum_i e^{-(T-1-i) w} e^{k_i}
+// v_i + e^{-T w} A_0 is what a token at T would see, so the cotangent acts as one more
+// token at T with s_T = dA_T and s_T y_T = -dB_T in the future sums G, H of every earlier
+// token (and of the state before token 0): dk, dv and da, db, dp take it in through the
+// backward's reverse scan, which starts the last window from it. As sums at that window's
+// end (nseg * 64 tokens, d = nseg * 64 - T tokens past T): (G, H) = (dA_T, -dB_T) e^{d w}.
+__global__ __launch_bounds__(256) void wkv_tail_kernel(int64_t n, int64_t T, int64_t C,
+                                                       int64_t nseg,
+                                                       const float *__restrict__ w,
+                                                       const float *__restrict__ dfa,
+                                                       const float *__restrict__ dfb,
+                                                       const float *__restrict__ fin,
+                                                       double *__restrict__ tail) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t c = i % C;
+    const double d = (double)(nseg * kBwdWindow - T);
+    RevCarry t{(double)dfa[i], -(double)dfb[i],
+               (d * (double)w[c] - (double)fin[2 * n + i]) * kLog2eD};
+    if (t.g == 0.0 && t.h == 0.0) t = rev_zero();
+    rnormalize(t);
+    put_rrec(tail, n, i, t);
+}
+
+// ... and dw: the extra token's term -s_T (A'_T - y_T B'_T) = -(dA_T A'_T + dB_T B'_T), with
+// the age-weighted sums A'_T, B'_T after token T-1: from the forward's carry entering the
+// last 32-token chunk, the chunk's tokens are folded in one at a time (fp64, rescaled at
+// every token) and the term is added to the last window's dw partial. One lane per (b, c).
+__global__ __launch_bounds__(256) void wkv_tail_dw_kernel(
+    int64_t B, int64_t T, int64_t C, int64_t nseg, const FwdCarries F,
+    const float *__restrict__ w, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ dfa, const float *__restrict__ dfb,
+    const float *__restrict__ fin, double *__restrict__ part) {
+    const int64_t n = B * C;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t b = i / C, c = i - b * C;
+    const int64_t ci = (T - 1) / kCinChunk;
+    Carry st = chunk_carry(F, b, ci, C, (int)c);
+    const double w2 = (double)w[c] * kLog2eD;
+    for (int64_t t = ci * kCinChunk; t < T; ++t) {
+        const int64_t x = (b * T + t) * C + c;
+        const double kx = (double)k[x] * kLog2eD, vx = (double)v[x];
+        const double pd = st.P - w2;
+        const double m = fmax(pd, kx);
+        const double fa = exp2_64(pd - m), fx = exp2_64(kx - m);
+        st.ap = (st.ap + st.a) * fa;
+        st.bp = (st.bp + st.b) * fa;
+        st.a = fma(st.a, fa, fx * vx);
+        st.b = fma(st.b, fa, fx);
+        st.P = m;
     }
-    double acc = 0.0;
-#pragma unroll
-    for (int j = 0; j < kCotPart; ++j) {
-        const int64_t t = t0 + j;
-        if (cval && t < T) {
-            const int64_t i = (b * T + t) * C + c;
-            const double age = (double)(T - 1 - t);
-            const double cf = exp2_64(((double)kv[j] - fma(age, wd, pT)) * kLog2eD);
-            const double qq = fma(dA, (double)vv[j], dB) * cf;
-            dv[i] = (float)fma(cf, dA, (double)gv[j]);
-            dk[i] = (float)((double)gk[j] + qq);
-            acc = fma(age, qq, acc);
-        }
-    }
-    red[q][lane] = -acc;
-    __syncthreads();
-    if (q == 0 && cval) {
-        double dwt = red[0][lane];
-#pragma unroll
-        for (int r = 1; r < kCotWaves; ++r) dwt += red[r][lane];
-        if (s == 0) {
-            const Carry st = get_cin(init, n, ic);
-            const double f = exp2_64(-fma((double)T, wd, pT) * kLog2eD + st.P);
-            dwt -= (double)T * f * fma(dA, st.a, dB * st.b);
-        }
-        part[(b * nseg + s) * C + c] += dwt;
-    }
+    const double sc = exp2_64(st.P - (double)fin[2 * n + i] * kLog2eD);
+    const double term = -fma((double)dfa[i], st.ap, (double)dfb[i] * st.bp) * sc;
+    part[(b * nseg + nseg - 1) * C + c] += term;
 }
 
 // Gradient with respect to the state before token 0. That state holds A0 = a e^p and
 // B0 = b e^p, which reach token t as e^{-t w} A0 and e^{-t w} B0, so dL/dA0 = G_{-1} and
-// dL/dB0 = -H_{-1}: the future sums over the whole sequence, which the backward leaves as
-// window 0's reverse inclusive record. With the state (a, b, 2^P = e^p) as the forward
-// recorded it: da = G e^p, db = -H e^p, dp = (a G - b H) e^p. A cotangent (da_T, db_T) of
-// the final state reaches A0 as e^{-T w} dA_T: da gains da_T e^{-T w + p - p_T} (db alike),
-// dp gains a times that plus b times db's. One lane per (b, c).
+// dL/dB0 = -H_{-1}: the future sums over the whole sequence (a cotangent of the final state
+// included), which the backward leaves as window 0's reverse inclusive record. With the
+// state (a, b, 2^P = e^p) as the forward recorded it: da = G e^p, db = -H e^p,
+// dp = (a G - b H) e^p. One lane per (b, c).
 __global__ __launch_bounds__(256) void wkv_state_grad_kernel(
-    int64_t n, int64_t T, int64_t C, int64_t nseg, const double *__restrict__ init,
-    const double *__restrict__ rincl, const float *__restrict__ w,
-    const float *__restrict__ dfa, const float *__restrict__ dfb, const float *__restrict__ fin,
-    float *__restrict__ ga, float *__restrict__ gb, float *__restrict__ gp) {
+    int64_t n, int64_t C, int64_t nseg, const double *__restrict__ init,
+    const double *__restrict__ rincl, float *__restrict__ ga, float *__restrict__ gb,
+    float *__restrict__ gp) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int64_t b = i / C, c = i - b * C;
     const RevCarry fut = get_rrec(rincl, n * nseg, b * nseg * C + c);
     const Carry st = get_cin(init, n, i);
     const double sc = exp2_64(fut.r + st.P);
-    double da = fut.g * sc, db = -fut.h * sc;
-    double dp = fma(st.a, fut.g, -st.b * fut.h) * sc;
-    if (dfa != nullptr) {
-        const double f =
-            exp2_64(-fma((double)T, (double)w[c], (double)fin[2 * n + i]) * kLog2eD + st.P);
-        const double xa = (double)dfa[i] * f, xb = (double)dfb[i] * f;
-        da += xa;
-        db += xb;
-        dp += fma(st.a, xa, st.b * xb);
-    }
-    ga[i] = (float)da;
-    gb[i] = (float)db;
-    gp[i] = (float)dp;
+    ga[i] = (float)(fut.g * sc);
+    gb[i] = (float)(-fut.h * sc);
+    gp[i] = (float)(fma(st.a, fut.g, -st.b * fut.h) * sc);
 }
 
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
@@ -809,7 +795,16 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nbg = B * ngrp;
     const int64_t units = nbg * L.nseg;
-    const FwdCarries fc{F.incl, F.cin, F.init, B * F.nseg * C, F.nseg};
+    const FwdCarries fc{F.incl, F.cin, F.init, dfa != nullptr ? L.tail : nullptr,
+                        B * F.nseg * C, F.nseg};
+    const int64_t n = B * C;
+    const dim3 nb((unsigned)((n + 255) / 256));
+    if (dfa != nullptr) {  // fp32 only (the caller checks)
+        hipLaunchKernelGGL(wkv_tail_kernel, nb, dim3(256), 0, stream, n, T, C, L.nseg, w, dfa,
+                           dfb, F.fin, L.tail);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (fmt == Io::BF16)
         launch_backward_io<Io::BF16>(units, stream, B, T, C, ngrp, nbg, L, epoch, w, u, k, v, dy,
                                      r, fc, dk, dv, dr, dw, du);
@@ -821,13 +816,10 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
                                     r, fc, dk, dv, dr, dw, du);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dfa != nullptr) {  // fp32 only (the caller checks)
-        hipLaunchKernelGGL(wkv_final_cot_kernel, dim3((unsigned)(nbg * L.nseg)),
-                           dim3(kCotWaves * 64), 0,
-                           stream, B, T, C, (int64_t)ngrp, L.nseg, w,
+    if (dfa != nullptr) {
+        hipLaunchKernelGGL(wkv_tail_dw_kernel, nb, dim3(256), 0, stream, B, T, C, L.nseg, fc, w,
                            static_cast<const float *>(k), static_cast<const float *>(v), dfa,
-                           dfb, F.fin, F.init, static_cast<float *>(dk),
-                           static_cast<float *>(dv), L.part);
+                           dfb, F.fin, L.part);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -836,10 +828,8 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
                        stream, B * L.nseg, C, L.part, dw, du);
     e = hipGetLastError();
     if (e != hipSuccess || ga == nullptr) return e;
-    const int64_t n = B * C;
-    hipLaunchKernelGGL(wkv_state_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       stream, n, T, C, L.nseg, F.init, L.rincl, w, dfa, dfb, F.fin, ga, gb,
-                       gp);
+    hipLaunchKernelGGL(wkv_state_grad_kernel, nb, dim3(256), 0, stream, n, C, L.nseg, F.init,
+                       L.rincl, ga, gb, gp);
     return hipGetLastError();
 }
 

@@ -323,6 +323,7 @@ struct FwdCarries {
     const double *incl;
     const double *cin;
     const double *init;  // [5][B][C]: the carry before token 0
+    const double *tail;  // [3][B][C] or null: the future sums beyond the last window
     int64_t nrec;
     int64_t nseg;
 };

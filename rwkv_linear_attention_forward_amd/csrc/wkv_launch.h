@@ -74,12 +74,15 @@ constexpr int kBwdWindow = kBwdWaves * kCinChunk;
 //   ragg[3][B][nseg][C]      reverse window aggregates (from a zero future)
 //   rincl[3][B][nseg][C]     reverse inclusive carries: the future sums entering window s
 //   part[2][B][nseg][C]      per-window dw, du partials (fp64), summed by a second kernel
+//   tail[3][B][C]            the future sums beyond the last window, when the final state
+//                            has a cotangent (otherwise unused: that future is zero)
 struct BwdLayout {
     int64_t nseg;
     uint64_t *flags;
     double *ragg;
     double *rincl;
     double *part;
+    double *tail;
 };
 
 // `sa`, `sb`, `sp` ([B][C], all three or none) hold the state before token 0 in the decode

@@ -70,9 +70,10 @@ def _fwd_bytes(B, T, C, window=64, chunk=32):
 
 def _bwd_bytes(B, T, C, window=64):
     """Backward workspace: flags, reverse aggregates and inclusive carries (24 B records),
-    dw/du partials (2 fp64)."""
+    dw/du partials (2 fp64), and one 24 B record per (b, c) for a final state's cotangent."""
     nseg, ngrp = -(-T // window), -(-C // 64)
-    return _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 24) + _r256(B * nseg * C * 16)
+    return (_r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 24) + _r256(B * nseg * C * 16)
+            + _r256(B * C * 24))
 
 
 def test_sizes(pkg):

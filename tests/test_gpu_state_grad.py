@@ -221,3 +221,28 @@ def test_pieces_chain_to_the_whole_sequence(wkv, dev, cuts):
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s cuts=%s" % (n, cuts),
                                             floor=floor))
     _log("pieces %s" % (cuts,), worst)
+
+
+def test_final_state_cotangent_extreme_decay(wkv, dev):
+    """w up to 200 with 28 padded tokens after T: the cotangent, placed at the last window's
+    end, carries a growth of up to e^{28 * 200} there, which only the per-token path can
+    hold (and a few channels with w ~ 1e-7, where it does not decay at all)."""
+    from state_ref import backward_state_grad_cot
+    B, T, C = 2, 100, 70
+    rng = np.random.default_rng(120)
+    w = np.exp(rng.uniform(-8.0, np.log(200.0), C)).astype(np.float32)
+    w[:3] = 1e-7
+    x = {"w": w, "u": rng.uniform(-1, 1, C).astype(np.float32),
+         "k": rng.standard_normal((B, T, C)).astype(np.float32),
+         "v": rng.standard_normal((B, T, C)).astype(np.float32),
+         "dy": rng.standard_normal((B, T, C)).astype(np.float32)}
+    st = wkv_inputs.random_state(B, C, seed=121, p_range=(-3.0, 3.0))
+    got, dA, dB = _cot_case(wkv, dev, x, st, seed=122)
+    ref = backward_state_grad_cot(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB)
+    worst = 0.0
+    for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
+        r = np.asarray(r, np.float64)
+        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s extreme w" % n,
+                                            floor=floor))
+    _log("final-state cotangent, w up to 200", worst)
