@@ -272,8 +272,9 @@ def bench_copy(torch, dev, reps=3):
             "gbps": 2 * COPY_BYTES / (statistics.median(ms) * 1e-3) / 1e9}
 
 
-def bench_decode(wkv, torch, dev, steps=20, warmup=3):
+def bench_decode(wkv, torch, dev, steps=20, warmup=3, dtype=None):
     import wkv_inputs
+    dtype = torch.float32 if dtype is None else dtype
     cfg = wkv_inputs.DECODE
     B, C, L = cfg["B"], cfg["C"], cfg["layers"]
     params = [wkv_inputs.decode_layer_params(l) for l in range(L)]
@@ -281,10 +282,10 @@ def bench_decode(wkv, torch, dev, steps=20, warmup=3):
     u = [torch.from_numpy(pu).to(dev) for _, pu in params]
     st = [tuple(torch.from_numpy(a).to(dev) for a in wkv_inputs.empty_decode_state(B, C))
           for _ in range(L)]
-    y = torch.empty(B, C, dtype=torch.float32, device=dev)
+    y = torch.empty(B, C, dtype=dtype, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(1005)
-    kv = torch.empty(L, 2, B, C, dtype=torch.float32, device=dev)
+    kv = torch.empty(L, 2, B, C, dtype=dtype, device=dev)
 
     def calls():
         for l in range(L):
@@ -317,6 +318,10 @@ def bench_decode(wkv, torch, dev, steps=20, warmup=3):
     with torch.cuda.graph(graph):
         calls()
     per_call_us = timed(graph.replay)
+    if dtype != torch.float32:  # the 16-bit form: only its graph-replayed rate
+        gbps = 30 * B * C / (per_call_us * 1e-6) / 1e9
+        return {"us_per_call": per_call_us, "algorithmic_gbps": gbps,
+                "frac_of_peak": gbps / PEAK_GBPS, "bytes_per_elem": 30}
     gbps = 36 * B * C / (per_call_us * 1e-6) / 1e9
     return {"workload": "batched decode B=%d C=%d, %d layer states, k, v ~ N(0,1)" % (B, C, L),
             "us_per_call": per_call_us, "elem_per_s": B * C / (per_call_us * 1e-6),
@@ -584,6 +589,7 @@ def main(argv=None):
         out["copy_1gib"] = bench_copy(torch, dev)
     if not args.no_decode:
         out["decode"] = bench_decode(wkv, torch, dev)
+        out["decode"]["bf16"] = bench_decode(wkv, torch, dev, dtype=torch.bfloat16)
     if not args.no_state:
         out["forward_state"] = bench_forward_state(wkv, torch, dev, x)
     if not args.no_gated:

@@ -218,6 +218,16 @@ int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *
 int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
                     const float *v, float *a, float *b, float *p, float *y, void *stream);
 
+/* wkv_decode_step with k, v and y [B][C] in the storage format `dtype` (WKV_F32, WKV_BF16 or
+ * WKV_F16; 16-bit tensors 2-byte aligned): k, v are widened to fp32 on load and y is rounded
+ * to the format (to nearest even) on store; w, u and the state a, b, p stay fp32, so the
+ * state carries the same precision as in wkv_decode_step (a serving loop whose activations
+ * are 16-bit decodes with 30 instead of 36 bytes per element). Same recursive form ("RWKV
+ * についての調査記録", section "RWKVとは？"), validation and errors. */
+int wkv_decode_step_typed(int dtype, int64_t B, int64_t C, const float *w, const float *u,
+                          const void *k, const void *v, float *a, float *b, float *p, void *y,
+                          void *stream);
+
 /* Token-shift mix, the step that produces the inputs of the R, K, V projections
  * ("RWKV解读：在Transformer的时代的新RNN", section 二.3, formula (7): they are computed from a
  * weighted sum of the current and the previous token's input, one trained per-channel weight

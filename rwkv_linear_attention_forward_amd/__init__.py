@@ -42,7 +42,8 @@ EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_st
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
            "wkv_forward_infer",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
-           "wkv_backward_typed", "wkv_backward_state", "wkv_decode_step", "wkv_token_shift",
+           "wkv_backward_typed", "wkv_backward_state", "wkv_decode_step",
+           "wkv_decode_step_typed", "wkv_token_shift",
            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
 
 # Storage formats of the [B, T, C] tensors (dtype codes of the *_typed entry points).
@@ -110,6 +111,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_state.restype = ctypes.c_int
     lib.wkv_backward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_decode_step_typed.restype = ctypes.c_int
+    lib.wkv_decode_step_typed.argtypes = [ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _P]
     lib.wkv_decode_step.restype = ctypes.c_int
     lib.wkv_decode_step.argtypes = [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = lib
@@ -411,11 +415,18 @@ def backward_gated(w, u, k, v, r, dout, fwd_workspace=None, workspace=None, out=
 
 
 def decode_step(w, u, k, v, a, b, p, out=None):
-    """One token for B sequences: y [B,C]; the state (a, b, p) [B,C] is updated in place."""
-    _need(k, "k", 2)
+    """One token for B sequences: y [B,C]; the state (a, b, p) [B,C] float32 is updated in
+    place. k, v (and y / out) share one of float32, bfloat16, float16."""
+    if not isinstance(k, torch.Tensor):
+        raise TypeError("k must be a torch.Tensor")
+    if k.dtype not in _DTYPE_CODE:
+        raise TypeError("k must be float32, bfloat16 or float16, got %s" % k.dtype)
+    _need(k, "k", 2, dtype=k.dtype)
     dev = k.device
+    _need(v, "v", 2, dev, dtype=k.dtype)
     for t, n in ((v, "v"), (a, "a"), (b, "b"), (p, "p")):
-        _need(t, n, 2, dev)
+        if n != "v":
+            _need(t, n, 2, dev)
         if t.shape != k.shape:
             raise ValueError("%s shape %s != k shape %s" % (n, tuple(t.shape), tuple(k.shape)))
     _need(w, "w", 1, dev)
@@ -424,11 +435,18 @@ def decode_step(w, u, k, v, a, b, p, out=None):
     if w.shape[0] != C or u.shape[0] != C:
         raise ValueError("w and u must have C=%d elements" % C)
     y = torch.empty_like(k) if out is None else out
-    _need(y, "out", 2, dev)
+    _need(y, "out", 2, dev, dtype=k.dtype)
     if y.shape != k.shape:
         raise ValueError("out has the wrong shape")
-    _check(load_library().wkv_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(a),
-                                          _ptr(b), _ptr(p), _ptr(y), _stream(dev)))
+    lib = load_library()
+    if k.dtype == torch.float32:
+        rc = lib.wkv_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                 _ptr(p), _ptr(y), _stream(dev))
+    else:
+        rc = lib.wkv_decode_step_typed(_DTYPE_CODE[k.dtype], B, C, _ptr(w), _ptr(u), _ptr(k),
+                                       _ptr(v), _ptr(a), _ptr(b), _ptr(p), _ptr(y),
+                                       _stream(dev))
+    _check(rc)
     return y
 
 

@@ -560,9 +560,11 @@ int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *
                          workspace, workspace_bytes, stream);
 }
 
-int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
-                    const float *v, float *a, float *b, float *p, float *y, void *stream) {
-    static const char *fn = "wkv_decode_step";
+namespace {
+
+int decode_call(const char *fn, wkvdev::Io fmt, int64_t B, int64_t C, const float *w,
+                const float *u, const void *k, const void *v, float *a, float *b, float *p,
+                void *y, void *stream) {
     g_err[0] = '\0';
     if (B < 0 || C < 0) return fail(WKV_ERR_INVALID_ARG, "%s: negative dimension", fn);
     if (C > kMaxC) return fail(WKV_ERR_INVALID_ARG, "%s: C exceeds %lld", fn, (long long)kMaxC);
@@ -573,22 +575,42 @@ int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const 
         !nonnull(v, "v", fn) || !nonnull(a, "a", fn) || !nonnull(b, "b", fn) ||
         !nonnull(p, "p", fn) || !nonnull(y, "y", fn))
         return WKV_ERR_INVALID_ARG;
+    const size_t es = fmt == wkvdev::Io::F32 ? 4u : 2u;
     const void *ptrs[8] = {w, u, k, v, a, b, p, y};
     const char *names[8] = {"w", "u", "k", "v", "a", "b", "p", "y"};
+    const size_t align[8] = {4, 4, es, es, 4, 4, 4, es};
     for (int i = 0; i < 8; ++i)
-        if (!aligned(ptrs[i], 4, names[i], fn)) return WKV_ERR_INVALID_ARG;
-    const size_t nb = (size_t)(B * C) * 4u;
-    const size_t sizes[8] = {(size_t)C * 4u, (size_t)C * 4u, nb, nb, nb, nb, nb, nb};
+        if (!aligned(ptrs[i], align[i], names[i], fn)) return WKV_ERR_INVALID_ARG;
+    const size_t nb = (size_t)(B * C) * 4u, ne = (size_t)(B * C) * es;
+    const size_t sizes[8] = {(size_t)C * 4u, (size_t)C * 4u, ne, ne, nb, nb, nb, ne};
     for (int i = 4; i < 8; ++i)      // written: a, b, p, y
         for (int j = 0; j < 8; ++j)  // against everything else
             if (j != i && overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, names[i], names[j]);
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
-    hipError_t e = wkvdev::launch_decode(B, C, w, u, k, v, a, b, p, y,
+    hipError_t e = wkvdev::launch_decode(B, C, fmt, w, u, k, v, a, b, p, y,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
     return WKV_OK;
+}
+
+}  // namespace
+
+int wkv_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
+                    const float *v, float *a, float *b, float *p, float *y, void *stream) {
+    return decode_call("wkv_decode_step", wkvdev::Io::F32, B, C, w, u, k, v, a, b, p, y,
+                       stream);
+}
+
+int wkv_decode_step_typed(int dtype, int64_t B, int64_t C, const float *w, const float *u,
+                          const void *k, const void *v, float *a, float *b, float *p, void *y,
+                          void *stream) {
+    static const char *fn = "wkv_decode_step_typed";
+    g_err[0] = '\0';
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    return decode_call(fn, fmt, B, C, w, u, k, v, a, b, p, y, stream);
 }
 
 namespace {

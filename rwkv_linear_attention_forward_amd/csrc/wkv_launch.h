@@ -125,8 +125,9 @@ hipError_t launch_shift_backward(int64_t B, int64_t T, int64_t C, const float *x
                                  const float *d_k, const float *d_v, float *dx, float *dx_prev,
                                  float *dmu, double *part, hipStream_t stream);
 
-hipError_t launch_decode(int64_t B, int64_t C, const float *w, const float *u, const float *k,
-                         const float *v, float *a, float *b, float *p, float *y,
+// k, v, y ([B][C]) in storage format `fmt`; the state a, b, p stays fp32.
+hipError_t launch_decode(int64_t B, int64_t C, Io fmt, const float *w, const float *u,
+                         const void *k, const void *v, float *a, float *b, float *p, void *y,
                          hipStream_t stream);
 
 }  // namespace wkvdev

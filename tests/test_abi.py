@@ -288,6 +288,19 @@ def test_decode_rejects_bad_arguments(pkg):
                                None) == pkg.WKV_ERR_INVALID_ARG
     assert b"overlaps" in lib.wkv_last_error()
     assert lib.wkv_decode_step(0, 3, *([None] * 8), None) == pkg.WKV_OK
+    # the 16-bit form: unknown dtype, 2-byte alignment of k, v, y, 4-byte of the state
+    assert lib.wkv_decode_step_typed(9, 2, 3, *f[:8], None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"unknown dtype" in lib.wkv_last_error()
+    odd = ctypes.c_void_p(f[2].value + 1)
+    assert lib.wkv_decode_step_typed(1, 2, 3, f[0], f[1], odd, f[3], f[4], f[5], f[6], f[7],
+                                     None) == pkg.WKV_ERR_INVALID_ARG
+    half = ctypes.c_void_p(f[4].value + 2)
+    assert lib.wkv_decode_step_typed(1, 2, 3, f[0], f[1], f[2], f[3], half, f[5], f[6], f[7],
+                                     None) == pkg.WKV_ERR_INVALID_ARG
+    assert lib.wkv_decode_step_typed(1, 2, 3, f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[4],
+                                     None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"overlaps" in lib.wkv_last_error()
+    assert lib.wkv_decode_step_typed(2, 0, 3, *([None] * 8), None) == pkg.WKV_OK
 
 
 def test_python_layer_rejects_bad_tensors(pkg):

@@ -192,3 +192,37 @@ def test_decode_graph_replays_match_eager(wkv, dev):
         for l in range(L):
             for x, z in zip(gst[l], est[l]):
                 assert torch.equal(x, z), "replay %d layer %d" % (r, l)
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+def test_decode_16bit_storage(wkv, dev, dtype):
+    """k, v, y stored in 16 bits, the state in fp32: y and the state are bitwise those of the
+    fp32 decode on the same (exactly widened) k, v, with y rounded to the format to nearest
+    even; and the chain follows the oracle on those inputs to the fp32 tolerance plus one
+    unit in the format's last place."""
+    import torch
+    from helpers import assert_io_close
+    tdt = getattr(torch, dtype)
+    B, C, steps = 33, 200, 40
+    layer = 5
+    wn, un = wkv_inputs.decode_layer_params(layer, C=C)
+    w, u = _t(dev, wn), _t(dev, un)
+    s16 = [_t(dev, s) for s in wkv_inputs.empty_decode_state(B, C)]
+    s32 = [t.clone() for t in s16]
+    ost = wkv_inputs.empty_decode_state(B, C)
+    worst = 0.0
+    for s in range(steps):
+        kn, vn = wkv_inputs.decode_step_inputs(s, layer, B=B, C=C)
+        k16, v16 = _t(dev, kn).to(tdt), _t(dev, vn).to(tdt)
+        y16 = wkv.decode_step(w, u, k16, v16, *s16)
+        y32 = wkv.decode_step(w, u, k16.float(), v16.float(), *s32)
+        torch.cuda.synchronize()
+        assert y16.dtype == tdt
+        assert torch.equal(y16, y32.to(tdt)), "step %d" % s
+        for x, z in zip(s16, s32):
+            assert torch.equal(x, z), "state, step %d" % s
+        kw, vw = (t.float().cpu().numpy() for t in (k16, v16))
+        yr, ost = oracle.decode_step(wn, un, kw, vw, ost)
+        worst = max(worst, assert_io_close(y16.float().cpu().numpy(), yr, dtype,
+                                           "%s step %d" % (dtype, s)))
+    print("[decode %s] max allowance used %.3g" % (dtype, worst), flush=True)
