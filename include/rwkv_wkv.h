@@ -183,12 +183,31 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
  * scan starts from it), at about 6% more time. T == 0 writes zero da, db,
  * dp, dw, du, but is refused with dfa, dfb (a zero-length piece records no state: its
  * final state's cotangent is its initial state's, which the caller passes on). Outputs
- * must not overlap each other or any input. fp32 only. */
+ * must not overlap each other or any input. */
 int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                        const float *k, const float *v, const float *dy, const float *dfa,
                        const float *dfb, const void *fwd_workspace, float *dk, float *dv,
                        float *dw, float *du, float *da, float *db, float *dp,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* wkv_forward_state and wkv_backward_state for the other storage formats and the gate, as
+ * wkv_forward_typed / wkv_backward_typed are for wkv_forward / wkv_backward: k, v, dy, r,
+ * y, dk, dv, dr in the format `dtype` (WKV_F32, WKV_BF16 or WKV_F16), with r == NULL (and
+ * dr == NULL) for the plain operator or the receptance gate out = sigma(r) * y (dy then the
+ * cotangent of out). w, u, the state a, b, p, its cotangent dfa, dfb, and dw, du, da, db,
+ * dp stay fp32. wkv_forward_state_typed keeps the states its backward reads (unlike
+ * wkv_forward_infer, whose outputs it shares bitwise); a, b, p all or none. Arithmetic,
+ * workspaces and errors as in the fp32 entry points. */
+int wkv_forward_state_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                            const float *u, const void *k, const void *v, const void *r,
+                            void *y, float *a, float *b, float *p, void *workspace,
+                            size_t workspace_bytes, void *stream);
+int wkv_backward_state_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                             const float *u, const void *k, const void *v, const void *dy,
+                             const void *r, const float *dfa, const float *dfb,
+                             const void *fwd_workspace, void *dk, void *dv, void *dr,
+                             float *dw, float *du, float *da, float *db, float *dp,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward of the gated forward, L = sum dout * sigma(r) * y: as wkv_backward with the
  * cotangent dy = dout * sigma(r) formed on the fly, plus dr [B][T][C] =

@@ -42,7 +42,8 @@ EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_st
            "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
            "wkv_forward_infer",
            "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
-           "wkv_backward_typed", "wkv_backward_state", "wkv_decode_step",
+           "wkv_backward_typed", "wkv_backward_state", "wkv_forward_state_typed",
+           "wkv_backward_state_typed", "wkv_decode_step",
            "wkv_decode_step_typed", "wkv_token_shift",
            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
 
@@ -111,6 +112,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_state.restype = ctypes.c_int
     lib.wkv_backward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_forward_state_typed.restype = ctypes.c_int
+    lib.wkv_forward_state_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_backward_state_typed.restype = ctypes.c_int
+    lib.wkv_backward_state_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]
     lib.wkv_decode_step_typed.restype = ctypes.c_int
     lib.wkv_decode_step_typed.argtypes = [ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P]
@@ -242,24 +250,38 @@ def forward(w, u, k, v, workspace=None, out=None):
     return _forward_common(w, u, k, v, None, workspace, out)
 
 
-def forward_state(w, u, k, v, a, b, p, workspace=None, out=None):
-    """y [B,T,C] = WKV(w, u, k, v) started from the state (a, b, p) [B,C] (the decode
-    convention), which is overwritten with the state after the last token."""
-    B, T, C, dev = _check_btc(w, u, k, v)
+def forward_state(w, u, k, v, a, b, p, workspace=None, out=None, r=None):
+    """y [B,T,C] = WKV(w, u, k, v) started from the state (a, b, p) [B,C] float32 (the decode
+    convention), which is overwritten with the state after the last token; with r, the
+    gated output sigma(r) * y. k, v, r, out share one of float32, bfloat16, float16. The
+    workspace keeps what backward_state() reads."""
+    B, T, C, dev = _check_btc(w, u, k, v, typed=True)
     for t, n in ((a, "a"), (b, "b"), (p, "p")):
         _need(t, n, 2, dev)
         if tuple(t.shape) != (B, C):
             raise ValueError("%s must have shape %s, got %s" % (n, (B, C), tuple(t.shape)))
+    if r is not None:
+        _need(r, "r", 3, dev, dtype=k.dtype)
+        if r.shape != k.shape:
+            raise ValueError("r has the wrong shape")
     y = torch.empty_like(k) if out is None else out
-    _need(y, "out", 3, dev)
+    _need(y, "out", 3, dev, dtype=k.dtype)
     if y.shape != k.shape:
         raise ValueError("out has the wrong shape")
     if workspace is None:
         workspace = forward_workspace(B, T, C, dev)
     _check_ws(workspace, dev, "workspace")
-    _check(load_library().wkv_forward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
-                                            _ptr(y), _ptr(a), _ptr(b), _ptr(p),
-                                            _ptr(workspace), workspace.numel(), _stream(dev)))
+    lib = load_library()
+    if k.dtype == torch.float32 and r is None:
+        rc = lib.wkv_forward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(a),
+                                   _ptr(b), _ptr(p), _ptr(workspace), workspace.numel(),
+                                   _stream(dev))
+    else:
+        rc = lib.wkv_forward_state_typed(_DTYPE_CODE[k.dtype], B, T, C, _ptr(w), _ptr(u),
+                                         _ptr(k), _ptr(v), _ptr(r), _ptr(y), _ptr(a), _ptr(b),
+                                         _ptr(p), _ptr(workspace), workspace.numel(),
+                                         _stream(dev))
+    _check(rc)
     return y
 
 
@@ -322,18 +344,26 @@ def backward(w, u, k, v, dy, fwd_workspace=None, workspace=None, out=None):
     return _backward_common(w, u, k, v, dy, None, fwd_workspace, workspace, out)
 
 
-def backward_state(w, u, k, v, dy, fwd_workspace, dstate=None, workspace=None, out=None):
+def backward_state(w, u, k, v, dy, fwd_workspace, dstate=None, workspace=None, out=None,
+                   r=None):
     """(dk, dv, dw, du, da, db, dp) for a forward_state() call, whose workspace
     `fwd_workspace` is required: the gradients of sum(dy * y) plus, with `dstate` = (da_T,
     db_T) [B, C], of sum(da_T * a_T + db_T * b_T) for the final state (a_T, b_T, p_T) that
     call returned (the next piece's da, db). da, db, dp [B, C] are the gradient with
     respect to the state (a, b, p) the forward started from (it records both states, so the
-    caller need not keep them). float32 only; `out` may hold preallocated (dk, dv, dw, du,
-    da, db, dp)."""
-    B, T, C, dev = _check_btc(w, u, k, v)
-    _need(dy, "dy", 3, dev)
-    if dy.shape != k.shape:
-        raise ValueError("dy has the wrong shape")
+    caller need not keep them). With r (a gated forward_state), dy is the cotangent of
+    sigma(r) * y and dr follows dv: (dk, dv, dr, dw, du, da, db, dp). k, v, dy, r and dk,
+    dv, dr share one of float32, bfloat16, float16; the rest is float32. `out` may hold the
+    outputs preallocated."""
+    B, T, C, dev = _check_btc(w, u, k, v, typed=True)
+    gated = r is not None
+    for t, n in ((dy, "dy"),) + (((r, "r"),) if gated else ()):
+        _need(t, n, 3, dev, dtype=k.dtype)
+        if t.shape != k.shape:
+            raise ValueError("%s has the wrong shape" % n)
+    if fwd_workspace is None:
+        raise ValueError("backward_state needs the workspace of the forward_state call")
+    _check_ws(fwd_workspace, dev, "fwd_workspace")
     dfa = dfb = None
     if dstate is not None:
         dfa, dfb = tuple(dstate)
@@ -341,30 +371,41 @@ def backward_state(w, u, k, v, dy, fwd_workspace, dstate=None, workspace=None, o
             _need(t, n, 2, dev)
             if tuple(t.shape) != (B, C):
                 raise ValueError("%s must have shape %s, got %s" % (n, (B, C), tuple(t.shape)))
-    if fwd_workspace is None:
-        raise ValueError("backward_state needs the workspace of the forward_state call")
-    _check_ws(fwd_workspace, dev, "fwd_workspace")
     wsz = backward_workspace_size(B, T, C, True)
     if workspace is None or workspace.numel() < wsz:
         workspace = torch.empty(max(16, wsz), dtype=torch.uint8, device=dev)
     _check_ws(workspace, dev, "workspace")
-    shapes = ((B, T, C), (B, T, C), (C,), (C,), (B, C), (B, C), (B, C))
-    names = ("dk", "dv", "dw", "du", "da", "db", "dp")
+    big = (B, T, C)
+    names = ("dk", "dv") + (("dr",) if gated else ()) + ("dw", "du", "da", "db", "dp")
+    shapes = (big, big) + ((big,) if gated else ()) + ((C,), (C,), (B, C), (B, C), (B, C))
+    dts = (k.dtype, k.dtype) + ((k.dtype,) if gated else ()) + (torch.float32,) * 5
     if out is None:
-        grads = tuple(torch.empty(sh, dtype=torch.float32, device=dev) for sh in shapes)
+        grads = tuple(torch.empty(sh, dtype=dt, device=dev) for sh, dt in zip(shapes, dts))
     else:
         grads = tuple(out)
         if len(grads) != len(names):
             raise ValueError("out must hold %d tensors" % len(names))
-        for t, n, sh in zip(grads, names, shapes):
-            _need(t, n, len(sh), dev)
+        for t, n, sh, dt in zip(grads, names, shapes, dts):
+            _need(t, n, len(sh), dev, dtype=dt)
             if tuple(t.shape) != sh:
                 raise ValueError("%s has the wrong shape" % n)
-    _check(load_library().wkv_backward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
-                                             _ptr(dy), _ptr(dfa), _ptr(dfb),
-                                             _ptr(fwd_workspace), *(_ptr(g) for g in grads),
-                                             _ptr(workspace),
-                                             workspace.numel(), _stream(dev)))
+    dk, dv = grads[0], grads[1]
+    dr = grads[2] if gated else None
+    dw, du, da, db, dp = grads[-5:]
+    lib = load_library()
+    if k.dtype == torch.float32 and not gated:
+        rc = lib.wkv_backward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                    _ptr(dfa), _ptr(dfb), _ptr(fwd_workspace), _ptr(dk),
+                                    _ptr(dv), _ptr(dw), _ptr(du), _ptr(da), _ptr(db), _ptr(dp),
+                                    _ptr(workspace), workspace.numel(), _stream(dev))
+    else:
+        rc = lib.wkv_backward_state_typed(_DTYPE_CODE[k.dtype], B, T, C, _ptr(w), _ptr(u),
+                                          _ptr(k), _ptr(v), _ptr(dy), _ptr(r), _ptr(dfa),
+                                          _ptr(dfb), _ptr(fwd_workspace), _ptr(dk), _ptr(dv),
+                                          _ptr(dr), _ptr(dw), _ptr(du), _ptr(da), _ptr(db),
+                                          _ptr(dp), _ptr(workspace), workspace.numel(),
+                                          _stream(dev))
+    _check(rc)
     return grads
 
 

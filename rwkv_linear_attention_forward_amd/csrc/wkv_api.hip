@@ -367,6 +367,21 @@ int wkv_forward_infer(int dtype, int64_t B, int64_t T, int64_t C, const float *w
                         workspace_bytes, stream, false);
 }
 
+int wkv_forward_state_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                            const float *u, const void *k, const void *v, const void *r,
+                            void *y, float *a, float *b, float *p, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_forward_state_typed";
+    g_err[0] = '\0';
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    const int given = (a != nullptr) + (b != nullptr) + (p != nullptr);
+    if (given != 0 && given != 3)
+        return fail(WKV_ERR_INVALID_ARG, "%s: give all of a, b, p or none", fn);
+    return forward_call(fn, B, T, C, fmt, w, u, k, v, r, y, a, b, p, workspace,
+                        workspace_bytes, stream, true);
+}
+
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                       const float *k, const float *v, const float *r, float *out,
                       void *workspace, size_t workspace_bytes, void *stream) {
@@ -495,12 +510,14 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
                          stream);
 }
 
-int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                       const float *k, const float *v, const float *dy, const float *dfa,
-                       const float *dfb, const void *fwd_workspace, float *dk, float *dv,
-                       float *dw, float *du, float *da, float *db, float *dp,
-                       void *workspace, size_t workspace_bytes, void *stream) {
-    static const char *fn = "wkv_backward_state";
+namespace {
+
+int backward_state_call(const char *fn, wkvdev::Io fmt, int64_t B, int64_t T, int64_t C,
+                        const float *w, const float *u, const void *k, const void *v,
+                        const void *dy, const void *r, const float *dfa, const float *dfb,
+                        const void *fwd_workspace, void *dk, void *dv, void *dr, float *dw,
+                        float *du, float *da, float *db, float *dp, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B > 0 && C > 0) {
@@ -528,9 +545,36 @@ int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const fl
             if (e != hipSuccess) return fail_hip(e, fn);
         }
     }
-    return backward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr, fwd_workspace,
-                         dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream, da, db, dp,
-                         dfa, dfb);
+    return backward_call(fn, B, T, C, fmt, w, u, k, v, dy, r, fwd_workspace, dk, dv, dr, dw, du,
+                         workspace, workspace_bytes, stream, da, db, dp, dfa, dfb);
+}
+
+}  // namespace
+
+int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *dy, const float *dfa,
+                       const float *dfb, const void *fwd_workspace, float *dk, float *dv,
+                       float *dw, float *du, float *da, float *db, float *dp,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_state_call("wkv_backward_state", wkvdev::Io::F32, B, T, C, w, u, k, v, dy,
+                               nullptr, dfa, dfb, fwd_workspace, dk, dv, nullptr, dw, du, da, db,
+                               dp, workspace, workspace_bytes, stream);
+}
+
+int wkv_backward_state_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
+                             const float *u, const void *k, const void *v, const void *dy,
+                             const void *r, const float *dfa, const float *dfb,
+                             const void *fwd_workspace, void *dk, void *dv, void *dr,
+                             float *dw, float *du, float *da, float *db, float *dp,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_backward_state_typed";
+    g_err[0] = '\0';
+    wkvdev::Io fmt;
+    if (!io_of(dtype, fn, &fmt)) return WKV_ERR_INVALID_ARG;
+    if ((r == nullptr) != (dr == nullptr) && B > 0 && T > 0 && C > 0)
+        return fail(WKV_ERR_INVALID_ARG, "%s: r and dr must be given together", fn);
+    return backward_state_call(fn, fmt, B, T, C, w, u, k, v, dy, r, dfa, dfb, fwd_workspace, dk,
+                               dv, dr, dw, du, da, db, dp, workspace, workspace_bytes, stream);
 }
 
 int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -736,9 +736,10 @@ __global__ __launch_bounds__(256) void wkv_tail_kernel(int64_t n, int64_t T, int
 // the age-weighted sums A'_T, B'_T after token T-1: from the forward's carry entering the
 // last 32-token chunk, the chunk's tokens are folded in one at a time (fp64, rescaled at
 // every token) and the term is added to the last window's dw partial. One lane per (b, c).
+template <Io IO>
 __global__ __launch_bounds__(256) void wkv_tail_dw_kernel(
     int64_t B, int64_t T, int64_t C, int64_t nseg, const FwdCarries F,
-    const float *__restrict__ w, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ w, const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v,
     const float *__restrict__ dfa, const float *__restrict__ dfb,
     const float *__restrict__ fin, double *__restrict__ part) {
     const int64_t n = B * C;
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(256) void wkv_tail_dw_kernel(
     const double w2 = (double)w[c] * kLog2eD;
     for (int64_t t = ci * kCinChunk; t < T; ++t) {
         const int64_t x = (b * T + t) * C + c;
-        const double kx = (double)k[x] * kLog2eD, vx = (double)v[x];
+        const double kx = (double)io_ld<IO>(k, x) * kLog2eD, vx = (double)io_ld<IO>(v, x);
         const double pd = st.P - w2;
         const double m = fmax(pd, kx);
         const double fa = exp2_64(pd - m), fx = exp2_64(kx - m);
@@ -799,7 +800,7 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
                         B * F.nseg * C, F.nseg};
     const int64_t n = B * C;
     const dim3 nb((unsigned)((n + 255) / 256));
-    if (dfa != nullptr) {  // fp32 only (the caller checks)
+    if (dfa != nullptr) {
         hipLaunchKernelGGL(wkv_tail_kernel, nb, dim3(256), 0, stream, n, T, C, L.nseg, w, dfa,
                            dfb, F.fin, L.tail);
         hipError_t e = hipGetLastError();
@@ -817,9 +818,18 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dfa != nullptr) {
-        hipLaunchKernelGGL(wkv_tail_dw_kernel, nb, dim3(256), 0, stream, B, T, C, L.nseg, fc, w,
-                           static_cast<const float *>(k), static_cast<const float *>(v), dfa,
-                           dfb, F.fin, L.part);
+        if (fmt == Io::BF16)
+            hipLaunchKernelGGL(wkv_tail_dw_kernel<Io::BF16>, nb, dim3(256), 0, stream, B, T, C,
+                               L.nseg, fc, w, static_cast<const io_t<Io::BF16> *>(k),
+                               static_cast<const io_t<Io::BF16> *>(v), dfa, dfb, F.fin, L.part);
+        else if (fmt == Io::F16)
+            hipLaunchKernelGGL(wkv_tail_dw_kernel<Io::F16>, nb, dim3(256), 0, stream, B, T, C,
+                               L.nseg, fc, w, static_cast<const io_t<Io::F16> *>(k),
+                               static_cast<const io_t<Io::F16> *>(v), dfa, dfb, F.fin, L.part);
+        else
+            hipLaunchKernelGGL(wkv_tail_dw_kernel<Io::F32>, nb, dim3(256), 0, stream, B, T, C,
+                               L.nseg, fc, w, static_cast<const float *>(k),
+                               static_cast<const float *>(v), dfa, dfb, F.fin, L.part);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

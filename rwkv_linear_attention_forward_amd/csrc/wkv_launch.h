@@ -102,7 +102,7 @@ hipError_t launch_forward(int64_t B, int64_t T, int64_t C, Io fmt, const float *
 // dy, r, dk, dv, dr are in storage format `fmt`; dw, du are fp32.
 // With `ga`, `gb`, `gp` ([B][C], all three or none) it also gives the gradient with respect
 // to the state (a, b, p) the forward started from (F's record of the carry before token 0).
-// With `dfa`, `dfb` ([B][C], both or none; fp32 format only) L also has the terms
+// With `dfa`, `dfb` ([B][C] fp32, both or none) L also has the terms
 // dfa * a_T + dfb * b_T of the final state F.fin the forward returned (p_T held fixed).
 hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float *w,
                            const float *u, const void *k, const void *v, const void *dy,

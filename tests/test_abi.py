@@ -274,6 +274,24 @@ def test_backward_state_rejects_bad_arguments(pkg):
     assert call(dfa=g[10], dfb=g[13]) == pkg.WKV_ERR_INVALID_ARG
     assert b"overlaps an input" in lib.wkv_last_error()
     assert lib.wkv_backward_state(2, 3, 0, *([None] * 16), 0, None) == pkg.WKV_OK
+    # the typed form: unknown dtype, r without dr, and the same checks as above
+    assert lib.wkv_backward_state_typed(7, 2, 3, 4, *g[:5], None, None, None, g[5], g[6],
+                                        g[7], None, g[8], g[9], g[12], g[13], g[14], g[11],
+                                        1 << 40, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"unknown dtype" in lib.wkv_last_error()
+    assert lib.wkv_backward_state_typed(1, 2, 3, 4, *g[:5], g[15], None, None, g[5], g[6],
+                                        g[7], None, g[8], g[9], g[12], g[13], g[14], g[11],
+                                        1 << 40, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"r and dr" in lib.wkv_last_error()
+    assert lib.wkv_backward_state_typed(1, 2, 3, 4, *g[:5], None, None, None, None, g[6],
+                                        g[7], None, g[8], g[9], g[12], g[13], g[14], g[11],
+                                        1 << 40, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"fwd_workspace is NULL" in lib.wkv_last_error()
+    assert lib.wkv_forward_state_typed(5, 2, 3, 4, *g[:4], None, g[4], g[12], g[13], g[14],
+                                       g[11], 1 << 40, None) == pkg.WKV_ERR_INVALID_ARG
+    assert lib.wkv_forward_state_typed(1, 2, 3, 4, *g[:4], None, g[4], g[12], None, g[14],
+                                       g[11], 1 << 40, None) == pkg.WKV_ERR_INVALID_ARG
+    assert b"all of a, b, p or none" in lib.wkv_last_error()
 
 
 def test_decode_rejects_bad_arguments(pkg):

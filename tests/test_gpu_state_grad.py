@@ -246,3 +246,66 @@ def test_final_state_cotangent_extreme_decay(wkv, dev):
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s extreme w" % n,
                                             floor=floor))
     _log("final-state cotangent, w up to 200", worst)
+
+
+def _sig(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))
+
+
+@pytest.mark.parametrize("dtype,gated", [("bfloat16", False), ("float16", False),
+                                         ("float32", True), ("bfloat16", True)])
+def test_typed_and_gated_state_pair(wkv, dev, dtype, gated):
+    """forward_state / backward_state with 16-bit k, v, dy, r, y, dk, dv, dr and/or the
+    receptance gate, a cotangent of the final state included. The oracle runs on the same
+    values widened exactly; the gated reference is the plain one with the cotangent
+    dy = dout sigma(r), plus dr = dout sigma(r) (1 - sigma(r)) y. 16-bit outputs get one unit
+    in the format's last place on top of the fp32 tolerance."""
+    import torch
+    from oracle import forward_rescaled
+    from helpers import assert_io_close
+    from state_ref import backward_state_grad_cot
+    tdt = getattr(torch, dtype)
+    B, T, C = 2, 150, 70
+    x = wkv_inputs.generate("l3b", seed=130, B=B, T=T, C=C)
+    rng = np.random.default_rng(131)
+    rr = rng.standard_normal((B, T, C)).astype(np.float32) * 2
+    t = {n: _t(dev, x[n]).to(tdt) for n in ("k", "v", "dy")}
+    t["r"] = _t(dev, rr).to(tdt) if gated else None
+    for n in ("w", "u"):
+        t[n] = _t(dev, x[n])
+    wide = {n: t[n].float().cpu().numpy().astype(np.float64) for n in ("k", "v", "dy")}
+    rw = t["r"].float().cpu().numpy().astype(np.float64) if gated else None
+    st = wkv_inputs.random_state(B, C, seed=132, p_range=(-3.0, 3.0))
+    sg = [_t(dev, s) for s in st]
+    ws = wkv.forward_workspace(B, T, C, dev)
+    out = wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *sg, workspace=ws, r=t["r"])
+    yo, (_, _, po) = forward_rescaled(x["w"], x["u"], wide["k"], wide["v"], st)
+    ra = rng.standard_normal((B, C)) * 0.5
+    rb = rng.standard_normal((B, C)) * 0.5
+    dA, dB = ra * np.exp(-po), rb * np.exp(-po)
+    pg = sg[2].cpu().numpy().astype(np.float64)
+    dfa = _t(dev, (ra * np.exp(pg - po)).astype(np.float32))
+    dfb = _t(dev, (rb * np.exp(pg - po)).astype(np.float32))
+    got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws, dstate=(dfa, dfb),
+                             r=t["r"])
+    torch.cuda.synchronize()
+    dyeff = wide["dy"] * _sig(rw) if gated else wide["dy"]
+    ref = list(backward_state_grad_cot(x["w"], x["u"], wide["k"], wide["v"], dyeff, st, dA, dB))
+    names = ["dk", "dv", "dw", "du", "da", "db", "dp"]
+    yref = yo * _sig(rw) if gated else yo
+    if gated:
+        ref.insert(2, wide["dy"] * _sig(rw) * (1 - _sig(rw)) * yo)
+        names.insert(2, "dr")
+    ofl = out.float().cpu().numpy()
+    worst = (assert_io_close(ofl, yref, dtype, "out") if dtype != "float32"
+             else assert_wkv_close(ofl, yref, "out"))
+    for g, r, n in zip(got, ref, names):
+        g = g.float().cpu().numpy()
+        r = np.asarray(r, np.float64)
+        what = "%s %s gated=%s" % (n, dtype, gated)
+        if n in ("dk", "dv", "dr") and dtype != "float32":
+            worst = max(worst, assert_io_close(g, r, dtype, what))
+        else:
+            floor = 0.1 if n[1] in "kvwur" else 0.1 * float(np.max(np.abs(r)))
+            worst = max(worst, assert_wkv_close(g, r, what, floor=floor))
+    _log("%s gated=%s with cotangent" % (dtype, gated), worst)
