@@ -97,7 +97,8 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
  * "コードを見ながらRWKVの構造を把握": the prompt's tokens go through the layer one after
  * another, each updating the state, before the next token is predicted), with the prompt
  * run in parallel. y and the workspace are as for wkv_forward (same size); a wkv_backward
- * given this workspace treats the initial state as a constant (no gradient flows to it).
+ * given this workspace treats the initial state as a constant, wkv_backward_state also
+ * gives the gradient with respect to it (and takes one for the final state).
  * The final state is accurate to fp32 (p is rounded first, a and b rescaled to match).
  * a, b, p must not overlap each other, k, v, y, w, u or the workspace. A zero-sized
  * dimension is a no-op that leaves the state unchanged. */
