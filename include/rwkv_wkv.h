@@ -181,7 +181,7 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
  * state (wkv_forward, or a = b = 0) gives da = db = dp = 0. Without dfa, dfb: dk, dv, dw,
  * du are bitwise those of wkv_backward with the same arguments; with them the final
  * state acts as one more token at T in the future sums of all earlier tokens (the reverse
- * scan starts from it), at about 6% more time. T == 0 writes zero da, db,
+ * scan starts from it), at about 3% more time. T == 0 writes zero da, db,
  * dp, dw, du, but is refused with dfa, dfb (a zero-length piece records no state: its
  * final state's cotangent is its initial state's, which the caller passes on). Outputs
  * must not overlap each other or any input. */

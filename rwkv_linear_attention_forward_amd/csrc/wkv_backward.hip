@@ -746,12 +746,21 @@ __global__ __launch_bounds__(256) void wkv_tail_dw_kernel(
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int64_t b = i / C, c = i - b * C;
-    const int64_t ci = (T - 1) / kCinChunk;
+    const int64_t ci = (T - 1) / kCinChunk, t0 = ci * kCinChunk;
+    const int Lv = (int)(T - t0);
+    float kc[kCinChunk], vc[kCinChunk];  // the chunk's tokens, all loads issued first
+#pragma unroll
+    for (int j = 0; j < kCinChunk; ++j) {
+        const int64_t x = (b * T + t0 + (j < Lv ? j : Lv - 1)) * C + c;
+        kc[j] = io_ld<IO>(k, x);
+        vc[j] = io_ld<IO>(v, x);
+    }
     Carry st = chunk_carry(F, b, ci, C, (int)c);
     const double w2 = (double)w[c] * kLog2eD;
-    for (int64_t t = ci * kCinChunk; t < T; ++t) {
-        const int64_t x = (b * T + t) * C + c;
-        const double kx = (double)io_ld<IO>(k, x) * kLog2eD, vx = (double)io_ld<IO>(v, x);
+#pragma unroll
+    for (int j = 0; j < kCinChunk; ++j) {
+        if (j >= Lv) break;
+        const double kx = (double)kc[j] * kLog2eD, vx = (double)vc[j];
         const double pd = st.P - w2;
         const double m = fmax(pd, kx);
         const double fa = exp2_64(pd - m), fx = exp2_64(kx - m);
