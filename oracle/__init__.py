@@ -33,8 +33,23 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wkv_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle_wkv.so")
+# WKV_ORACLE_SANITIZE=1 builds and loads an AddressSanitizer + UndefinedBehaviorSanitizer
+# build instead (its own file; the process must preload gcc's libasan), for the sanitizer
+# pass of the oracle's pins.
+SANITIZE = os.environ.get("WKV_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_wkv_san.so" if SANITIZE else "liboracle_wkv.so")
 _lib = None
+
+_CFLAGS = ["-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99", "-Wall"]
+_SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"]
+
+
+def compile_command(src: str, out: str) -> list:
+    """The gcc command that builds a copy of the oracle source `src` into `out` (with the
+    sanitizers when WKV_ORACLE_SANITIZE=1)."""
+    opt = _SAN_FLAGS if SANITIZE else ["-O2"]
+    return ["gcc"] + opt + _CFLAGS + [src, "-o", out, "-lm"]
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.c_int64
@@ -46,9 +61,7 @@ def build(force: bool = False) -> str:
             and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC)):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-           "-std=c99", "-Wall", _SRC, "-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
+    subprocess.run(compile_command(_SRC, tmp), check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 

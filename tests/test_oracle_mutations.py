@@ -108,8 +108,7 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new, kind):
     path = tmp_path / "mut.c"
     path.write_text(src.replace(old, new))
     so = tmp_path / "libmut.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99",
-                    str(path), "-o", str(so), "-lm"], check=True)
+    subprocess.run(oracle.compile_command(str(path), str(so)), check=True)
     oracle.use_library(str(so))
     try:
         if kind in ("direct", "recurrent", "rescaled"):
