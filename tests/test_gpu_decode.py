@@ -33,10 +33,13 @@ def test_decode_chain_equals_parallel_form(wkv, dev):
         assert_wkv_close(y.cpu().numpy(), ref[:, t], "t=%d" % t)
 
 
-@pytest.mark.parametrize("layer,B,steps", [(0, 256, 100), (39, 256, 100), (7, 8, 1000)])
+@pytest.mark.parametrize("layer,B,steps", [(0, 256, 1000), (39, 256, 1000), (7, 8, 1000)])
 def test_batched_decode_workload(wkv, dev, layer, B, steps):
-    """Full-width layer states; the 1000-step case covers the whole decode horizon."""
+    """The batched decode workload's full width (256 sequences x 5120 channels) over its whole
+    horizon of 1000 steps, for the first and the last of its 40 layer states (and a narrow
+    batch of a middle layer): every step's y against the oracle's chain, then the state."""
     import torch
+    from concurrent.futures import ThreadPoolExecutor
     C = wkv_inputs.DECODE["C"]
     wn, un = wkv_inputs.decode_layer_params(layer)
     w, u = _t(dev, wn), _t(dev, un)
@@ -44,12 +47,19 @@ def test_batched_decode_workload(wkv, dev, layer, B, steps):
     a, b, p = (_t(dev, s) for s in st)
     ost = st
     worst = 0.0
-    for s in range(steps):
-        kn, vn = wkv_inputs.decode_step_inputs(s, layer, B=B)
-        y = wkv.decode_step(w, u, _t(dev, kn), _t(dev, vn), a, b, p)
-        yr, ost = oracle.decode_step(wn, un, kn, vn, ost)
-        torch.cuda.synchronize()
-        worst = max(worst, assert_wkv_close(y.cpu().numpy(), yr, "layer %d step %d" % (layer, s)))
+    # the next step's inputs are drawn while this step runs (the draws are what they are,
+    # whichever thread makes them)
+    with ThreadPoolExecutor(max_workers=1) as pool:
+        nxt = pool.submit(wkv_inputs.decode_step_inputs, 0, layer, None, B)
+        for s in range(steps):
+            kn, vn = nxt.result()
+            if s + 1 < steps:
+                nxt = pool.submit(wkv_inputs.decode_step_inputs, s + 1, layer, None, B)
+            y = wkv.decode_step(w, u, _t(dev, kn), _t(dev, vn), a, b, p)
+            yr, ost = oracle.decode_step(wn, un, kn, vn, ost)
+            torch.cuda.synchronize()
+            worst = max(worst, assert_wkv_close(y.cpu().numpy(), yr,
+                                                "layer %d step %d" % (layer, s)))
     ga, gb, gp = (t.cpu().numpy().astype(np.float64) for t in (a, b, p))
     oa, ob, op = ost
     assert_wkv_close(ga / gb, oa / ob, "state ratio")
@@ -82,7 +92,11 @@ def test_resume_through_host_is_bitwise(wkv, dev):
         assert np.array_equal(s.cpu().numpy(), r.cpu().numpy())
 
 
-def test_sentinels_and_large_keys(wkv, dev):
+@pytest.mark.parametrize("kbig", [30.0, 1000.0])
+def test_sentinels_and_large_keys(wkv, dev, kbig):
+    """Both empty-state sentinels (p = -1e38 and -inf), with every seventh step's keys drawn
+    with standard deviation kbig (30: the long-context workload's spikes; 1000: far beyond
+    any workload), at the stated tolerance."""
     import torch
     B, C = 2, 64
     rng = np.random.default_rng(23)
@@ -95,14 +109,14 @@ def test_sentinels_and_large_keys(wkv, dev):
     ta, tb, tp = _t(dev, a), _t(dev, b), _t(dev, p)
     st = (a.astype(np.float64), b.astype(np.float64), np.full((B, C), -1e38))
     for s in range(40):
-        k = (rng.standard_normal((B, C)) * (1000.0 if s % 7 == 3 else 3.0)).astype(np.float32)
+        k = (rng.standard_normal((B, C)) * (kbig if s % 7 == 3 else 3.0)).astype(np.float32)
         v = rng.standard_normal((B, C)).astype(np.float32)
         y = wkv.decode_step(_t(dev, w), _t(dev, u), _t(dev, k), _t(dev, v), ta, tb, tp)
         yr, st = oracle.decode_step(w, u, k, v, st)
         torch.cuda.synchronize()
         yg = y.cpu().numpy()
         assert np.all(np.isfinite(yg))
-        assert_wkv_close(yg, yr, "step %d" % s, rtol=2e-3)
+        assert_wkv_close(yg, yr, "step %d" % s)
 
 
 def test_decode_rejects_bad_output_tensor(wkv, dev):

@@ -82,9 +82,8 @@ def test_large_keys_stay_finite(wkv, dev, kscale, spike):
     y, _ = _gpu_forward(wkv, dev, x)
     assert np.all(np.isfinite(y))
     ref = oracle.forward_direct(x["w"], x["u"], x["k"], x["v"])
-    # |k| near 1e3 has an input ulp of 6e-5, so only the looser bound is meaningful there
-    rtol = 1e-4 if max(kscale * 5, spike) < 200 else 2e-3
-    _log("large-k %g/%g" % (kscale, spike), x, assert_wkv_close(y, ref, "large k", rtol=rtol))
+    # the oracle runs on the same fp32 keys, widened exactly: the stated 1e-4 holds at any |k|
+    _log("large-k %g/%g" % (kscale, spike), x, assert_wkv_close(y, ref, "large k"))
     lo = np.minimum.accumulate(x["v"], axis=1)
     hi = np.maximum.accumulate(x["v"], axis=1)
     assert np.all(y >= lo - 1e-5) and np.all(y <= hi + 1e-5)

@@ -81,17 +81,15 @@ def test_exact_paths(wkv, dev, case):
     """Chunks that take the per-token paths: keys 1000 apart (forward and backward), and
     |u| > 60 (the backward's per-token path throughout)."""
     x = _inputs(2, 400, 96, seed=64)
-    rtol = 1e-4
     if case == "spike":
         rng = np.random.default_rng(65)
         m = rng.random(x["k"].shape) < 0.02
         x["k"] = np.where(m, np.float32(1000.0) * np.sign(rng.standard_normal(x["k"].shape)),
                           x["k"]).astype(np.float32)
-        rtol = 2e-3  # fp32 inputs alone move dk, dv by more than 1e-4 at |k| = 1000
     else:
         x["u"] = np.linspace(-80, 80, 96).astype(np.float32)
     out, grads = _run(wkv, dev, x)
-    _check(x, out, grads, case, rtol=rtol)
+    _check(x, out, grads, case)
 
 
 def test_full_layer(wkv, dev):
