@@ -29,7 +29,19 @@
  *     any HIP call and launch nothing; the message of the last failing call on the
  *     calling thread is available from wkv_last_error(). A zero-sized dimension is a
  *     successful no-op (dw and du are zero-filled when C > 0 and B*T == 0).
- *   - The library allocates no device memory: scratch space is passed in by the caller.
+ *   - The library allocates no device memory, with one exception: wkv_forward, whose
+ *     signature has no workspace, takes its scan's scratch from the current device's
+ *     stream-ordered memory pool (hipMallocAsync) and returns it (hipFreeAsync), both on
+ *     `stream`, within the call. Every other entry point uses only memory the caller passes.
+ *
+ * Entry points. wkv_forward, wkv_backward_workspace_size, wkv_backward and wkv_decode_step
+ * are the operator's three calls with the plainest boundary: a forward that writes y, a
+ * backward that needs nothing from the forward (it recomputes what it needs into its
+ * workspace), and a decode step. Training code that runs a backward after every forward
+ * should use the pair wkv_forward_train / wkv_backward_train instead, which hands the
+ * window states from the forward to the backward through a workspace and so saves the
+ * backward a pass over k and v. The other entry points add the gate, 16-bit storage, a
+ * state in and out, and the token-shift mix.
  */
 #ifndef RWKV_WKV_H
 #define RWKV_WKV_H
@@ -70,24 +82,32 @@ const char *wkv_status_string(int status);
 /* Message of the last failing call made by this thread ("" if none). Never NULL. */
 const char *wkv_last_error(void);
 
-/* Bytes of device scratch that wkv_forward and wkv_forward_state need for (B, T, C):
- * publication flags plus, for every (b, c) sequence and every 64-token window, the
- * window's aggregate and the recurrent state after it, the state entering the window's
- * second 32-token chunk (each: the two sums of the recursive form, their age-weighted
- * counterparts and their scale, 40 bytes), and per (b, c) the state before token 0 and the
- * final state. Returns 0 for invalid dims. */
+/* Forward: y [B][T][C] from k, v [B][T][C] and w, u [C], starting from the empty state
+ * (formula (8) of "RWKV解读：在Transformer的时代的新RNN", section 二.3). The scan's scratch
+ * (publication flags and per-window records, fwd_scan_bytes: 48 bytes per 64 tokens and
+ * channel plus 8 per window and 64 channels) comes from the stream-ordered pool for the
+ * duration of the call; an allocation failure returns WKV_ERR_HIP. Keeps nothing for a
+ * backward (see wkv_forward_train). Requires C <= 2^24 and B*ceil(C/64)*ceil(T/64) < 2^31. */
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                const float *k, const float *v, float *y, void *stream);
+
+/* Bytes of device scratch that wkv_forward_train and wkv_forward_state need for (B, T, C):
+ * a 256-byte stamp, publication flags plus, for every (b, c) sequence and every 64-token
+ * window, the window's aggregate and the recurrent state after it, the state entering the
+ * window's second 32-token chunk (each: the two sums of the recursive form, their
+ * age-weighted counterparts and their scale, 40 bytes), and per (b, c) the state before
+ * token 0 and the final state. Returns 0 for invalid dims. */
 size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 
-/* Forward: y [B][T][C] from k, v [B][T][C] and w, u [C], starting from the empty state
- * (formula (8) of "RWKV解读：在Transformer的时代的新RNN", section 二.3).
+/* The training forward: y as wkv_forward, plus the window states a backward reads, left in
  * `workspace` (16-byte aligned, at least wkv_forward_workspace_size(B, T, C) bytes given in
- * `workspace_bytes`) is required whenever B*T*C > 0; its previous content is ignored. After
- * the call it holds the states at window boundaries, which wkv_backward can reuse to skip
- * its own pass over k and v; it must not be used by two calls at the same time.
- * Requires C <= 2^24 and B*ceil(C/64)*ceil(T/64) < 2^31. */
-int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                const float *k, const float *v, float *y, void *workspace,
-                size_t workspace_bytes, void *stream);
+ * `workspace_bytes`; required whenever B*T*C > 0; its previous content is ignored). Pass
+ * the same workspace to wkv_backward_train (or wkv_backward_gated/typed) for the same
+ * inputs; it must not be used by two calls at the same time. The workspace is stamped with
+ * what the call left in it, which the backward checks. */
+int wkv_forward_train(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, float *y, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* Forward from a given state, leaving the state after the last token: the T tokens run as
  * in wkv_forward, but the scan starts from the decode state (a, b, p) [B][C] (same meaning
@@ -96,9 +116,10 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
  * prompt-then-generate use of the recursive form ("RWKV についての調査記録", section
  * "コードを見ながらRWKVの構造を把握": the prompt's tokens go through the layer one after
  * another, each updating the state, before the next token is predicted), with the prompt
- * run in parallel. y and the workspace are as for wkv_forward (same size); a wkv_backward
- * given this workspace treats the initial state as a constant, wkv_backward_state also
- * gives the gradient with respect to it (and takes one for the final state).
+ * run in parallel. y and the workspace are as for wkv_forward_train (same size); a
+ * wkv_backward_train given this workspace treats the initial state as a constant,
+ * wkv_backward_state also gives the gradient with respect to it (and takes one for the
+ * final state).
  * The final state is accurate to fp32 (p is rounded first, a and b rescaled to match).
  * a, b, p must not overlap each other, k, v, y, w, u or the workspace. A zero-sized
  * dimension is a no-op that leaves the state unchanged. */
@@ -111,17 +132,17 @@ int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const flo
  * through a sigmoid gate of r ("RWKV解读：在Transformer的时代的新RNN", section 二.3: R is
  * sigmoid-activated, a forgetting mechanism, formula (9); "RWKV についての調査記録", section
  * "コードを見ながらRWKVの構造を把握": wkv is computed, then gated by sigma). y itself is
- * not written. The workspace is as for wkv_forward and serves wkv_backward_gated (or
- * wkv_backward) the same way. out must not overlap any input. */
+ * not written. The workspace is as for wkv_forward_train and serves wkv_backward_gated (or
+ * wkv_backward_train) the same way. out must not overlap any input. */
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                       const float *k, const float *v, const float *r, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* wkv_forward (r == NULL) or wkv_forward_gated (r != NULL) with k, v, r and y/out in the
+/* wkv_forward_train (r == NULL) or wkv_forward_gated (r != NULL) with k, v, r and y/out in the
  * storage format `dtype` (WKV_F32, WKV_BF16 or WKV_F16); w and u stay fp32. Values are
  * widened to fp32 on load; every sum, carry and state is kept in fp32/fp64 as in the fp32
  * entry points, and only the outputs are rounded to the format (to nearest even). 16-bit
- * tensors must be 2-byte aligned. The workspace is the same as wkv_forward's. */
+ * tensors must be 2-byte aligned. The workspace is the same as wkv_forward_train's. */
 int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
                       const float *u, const void *k, const void *v, const void *r, void *y,
                       void *workspace, size_t workspace_bytes, void *stream);
@@ -133,33 +154,55 @@ int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w
  * points; the workspace (wkv_forward_workspace_size bytes) is left without the states a
  * backward reads (their age-weighted sums are never formed and the carries entering the
  * windows' second chunks and token 0 are not stored), so it must not be passed to
- * wkv_backward. This is the prompt prefill of "RWKV についての調査記録", section
- * "コードを見ながらRWKVの構造を把握" (the prompt's tokens update the state in order) run in
- * parallel, with 1.1 bytes per element less workspace traffic than wkv_forward_state. */
+ * a backward: a backward given it is refused (WKV_ERR_INVALID_ARG when this process filled
+ * it; otherwise its dw, du come out NaN, from the workspace's stamp). This is the prompt
+ * prefill of "RWKV についての調査記録", section "コードを見ながらRWKVの構造を把握" (the
+ * prompt's tokens update the state in order) run in parallel, with 1.1 bytes per element
+ * less workspace traffic than wkv_forward_state. */
 int wkv_forward_infer(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
                       const float *u, const void *k, const void *v, const void *r, void *y,
                       float *a, float *b, float *p, void *workspace, size_t workspace_bytes,
                       void *stream);
 
-/* Bytes of device scratch that wkv_backward, wkv_backward_gated, wkv_backward_typed and
- * wkv_backward_state need. With have_fwd_workspace != 0 the caller
- * will pass the workspace that wkv_forward filled for the same inputs; otherwise the
- * window states are recomputed into this workspace, which then also covers
- * wkv_forward_workspace_size(B, T, C). */
-size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace);
+/* Bytes of device scratch that wkv_backward needs for (B, T, C): its own records (flags,
+ * reverse window records, per-window dw/du partials) plus room for the forward window
+ * states it recomputes. Returns 0 for invalid dims. */
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
 
 /* Backward of L = sum_{b,t,c} dy[b,t,c] * y[b,t,c] ("RWKV についての調査記録", section
  * "Trainingについて": all parameters get gradients): dk, dv [B][T][C] and dw, du [C],
  * where dw and du are summed over b and t and overwritten (not accumulated). dw is the
- * gradient with respect to w itself (a caller that stores d = log w uses w * dw).
- * `fwd_workspace` is NULL or the workspace wkv_forward filled for the same B, T, C, w, u,
- * k, v (it is only read). `workspace` (16-byte aligned, wkv_backward_workspace_size(B, T,
- * C, fwd_workspace != NULL) bytes given in `workspace_bytes`) is clobbered. dw and du are
- * summed in a fixed order and are bitwise reproducible run to run. */
+ * gradient with respect to w itself (a caller that stores d = log w uses w * dw). Needs
+ * nothing from a forward: the window states are recomputed from k, v into `workspace`
+ * (16-byte aligned, wkv_backward_workspace_size(B, T, C) bytes given in `workspace_bytes`),
+ * which is clobbered. dw and du are summed in a fixed order and are bitwise reproducible
+ * run to run. */
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
-                 float *dk, float *dv, float *dw, float *du, void *workspace,
-                 size_t workspace_bytes, void *stream);
+                 const float *k, const float *v, const float *dy, float *dk, float *dv,
+                 float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device scratch that wkv_backward_train needs (its own records only: the forward
+ * window states come from the forward's workspace). Returns 0 for invalid dims. */
+size_t wkv_backward_train_workspace_size(int64_t B, int64_t T, int64_t C);
+
+/* wkv_backward after wkv_forward_train: `fwd_workspace` is the workspace that call filled
+ * for the same B, T, C, w, u, k, v (only read; required). Its window states replace the
+ * backward's own pass over k and v, and `workspace` needs only
+ * wkv_backward_train_workspace_size(B, T, C) bytes. Results are bitwise those of
+ * wkv_backward. A workspace that an inference forward (wkv_forward_infer) or a forward of
+ * other sizes last filled is refused with WKV_ERR_INVALID_ARG when this process filled it;
+ * a mismatch the library cannot see on the host (a workspace filled elsewhere) makes dw and
+ * du NaN through the workspace's stamp. */
+int wkv_backward_train(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *dy,
+                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes that wkv_backward_gated, wkv_backward_typed, wkv_backward_state and their typed
+ * forms need: with have_fwd_workspace != 0 the caller passes the workspace a state-keeping
+ * forward filled for the same inputs (= wkv_backward_train_workspace_size); with 0 the window
+ * states are recomputed into this workspace (= wkv_backward_workspace_size). */
+size_t wkv_backward_workspace_size_ex(int64_t B, int64_t T, int64_t C, int have_fwd_workspace);
 
 /* wkv_backward for a forward from a state (wkv_forward_state, whose workspace must be
  * given as `fwd_workspace`: it records the state the forward started from and the one it
@@ -178,8 +221,8 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u
  * dy_t y_t / D_t (D_t the denominator at token t): da = G e^p, db = -H e^p, dp = (a G -
  * b H) e^p, plus with dfa, dfb the path through the final state (A_T holds e^{-T w} A0).
  * dp = a da + b db always (L depends on a, p only through a e^p). A forward from the empty
- * state (wkv_forward, or a = b = 0) gives da = db = dp = 0. Without dfa, dfb: dk, dv, dw,
- * du are bitwise those of wkv_backward with the same arguments; with them the final
+ * state (wkv_forward_train, or a = b = 0) gives da = db = dp = 0. Without dfa, dfb: dk,
+ * dv, dw, du are bitwise those of wkv_backward_train with the same arguments; with them the final
  * state acts as one more token at T in the future sums of all earlier tokens (the reverse
  * scan starts from it), at about 3% more time. T == 0 writes zero da, db,
  * dp, dw, du, but is refused with dfa, dfb (a zero-length piece records no state: its
@@ -192,7 +235,7 @@ int wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w, const fl
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* wkv_forward_state and wkv_backward_state for the other storage formats and the gate, as
- * wkv_forward_typed / wkv_backward_typed are for wkv_forward / wkv_backward: k, v, dy, r,
+ * wkv_forward_typed / wkv_backward_typed are for the training pair: k, v, dy, r,
  * y, dk, dv, dr in the format `dtype` (WKV_F32, WKV_BF16 or WKV_F16), with r == NULL (and
  * dr == NULL) for the plain operator or the receptance gate out = sigma(r) * y (dy then the
  * cotangent of out). w, u, the state a, b, p, its cotangent dfa, dfb, and dw, du, da, db,
@@ -213,16 +256,18 @@ int wkv_backward_state_typed(int dtype, int64_t B, int64_t T, int64_t C, const f
 /* Backward of the gated forward, L = sum dout * sigma(r) * y: as wkv_backward with the
  * cotangent dy = dout * sigma(r) formed on the fly, plus dr [B][T][C] =
  * dout * sigma(r) * (1 - sigma(r)) * y (y recomputed, never read). `fwd_workspace` is NULL
- * or the workspace wkv_forward_gated (or wkv_forward) filled for the same inputs. */
+ * (states recomputed; workspace as for wkv_backward) or the workspace wkv_forward_gated (or
+ * wkv_forward_train) filled for the same inputs (workspace as for wkv_backward_train). */
 int wkv_backward_gated(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                        const float *k, const float *v, const float *r, const float *dout,
                        const void *fwd_workspace, float *dk, float *dv, float *dr, float *dw,
                        float *du, void *workspace, size_t workspace_bytes, void *stream);
 
-/* wkv_backward (r == dr == NULL; dy is the cotangent of y) or wkv_backward_gated (r, dr
- * given; dy is the cotangent of the gated output) with k, v, dy, r, dk, dv, dr in the
- * storage format `dtype`; w, u, dw, du stay fp32. Arithmetic as in the fp32 entry points;
- * dk, dv, dr are rounded to the format on store. */
+/* wkv_backward / wkv_backward_train (r == dr == NULL; dy is the cotangent of y;
+ * fwd_workspace NULL or not) or wkv_backward_gated (r, dr given; dy is the cotangent of the
+ * gated output) with k, v, dy, r, dk, dv, dr in the storage format `dtype`; w, u, dw, du
+ * stay fp32. Arithmetic as in the fp32 entry points; dk, dv, dr are rounded to the format on
+ * store. Workspace size: wkv_backward_workspace_size_ex(B, T, C, fwd_workspace != NULL). */
 int wkv_backward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w,
                        const float *u, const void *k, const void *v, const void *dy,
                        const void *r, const void *fwd_workspace, void *dk, void *dv, void *dr,

@@ -7,12 +7,13 @@ been built; there is no CPU fallback.
 
 Entry points mirror the C ABI in include/rwkv_wkv.h:
 
-    forward(w, u, k, v, workspace=None) -> y
+    forward(w, u, k, v, workspace=None) -> y      (with a workspace: the training forward)
     forward_state(w, u, k, v, a, b, p, workspace=None) -> y   (a, b, p: state in, state out)
     forward_gated(w, u, k, v, r, workspace=None) -> sigma(r) * y
     backward_gated(w, u, k, v, r, dout, fwd_workspace=None) -> (dk, dv, dr, dw, du)
     forward_workspace(B, T, C, device) -> uint8 tensor sized for the forward
     backward(w, u, k, v, dy, fwd_workspace=None) -> (dk, dv, dw, du)
+                                    (with fwd_workspace: the training backward)
     decode_step(w, u, k, v, a, b, p) -> y          (a, b, p updated in place)
     token_shift(x, mu, x_prev=None) -> (out_r, out_k, out_v, x_last)
     token_shift_backward(x, mu, dout, x_prev=None) -> (dx, dx_prev, dmu)
@@ -39,9 +40,11 @@ WKV_ERR_HIP = 3
 # Every symbol the header declares, for the export check.
 EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_string",
            "wkv_last_error", "wkv_forward_workspace_size",
-           "wkv_forward", "wkv_forward_state", "wkv_forward_gated", "wkv_forward_typed",
-           "wkv_forward_infer",
-           "wkv_backward_workspace_size", "wkv_backward", "wkv_backward_gated",
+           "wkv_forward", "wkv_forward_train", "wkv_forward_state", "wkv_forward_gated",
+           "wkv_forward_typed", "wkv_forward_infer",
+           "wkv_backward_workspace_size", "wkv_backward_train_workspace_size",
+           "wkv_backward_workspace_size_ex", "wkv_backward", "wkv_backward_train",
+           "wkv_backward_gated",
            "wkv_backward_typed", "wkv_backward_state", "wkv_forward_state_typed",
            "wkv_backward_state_typed", "wkv_decode_step",
            "wkv_decode_step_typed", "wkv_token_shift",
@@ -78,7 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_workspace_size.restype = ctypes.c_size_t
     lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
-    lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+    lib.wkv_forward_train.restype = ctypes.c_int
+    lib.wkv_forward_train.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                      _P]
     lib.wkv_forward_typed.restype = ctypes.c_int
     lib.wkv_forward_typed.argtypes = [ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
@@ -104,11 +110,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_state.restype = ctypes.c_int
     lib.wkv_forward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
-    lib.wkv_backward_workspace_size.restype = ctypes.c_size_t
-    lib.wkv_backward_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
+    for name in ("wkv_backward_workspace_size", "wkv_backward_train_workspace_size"):
+        getattr(lib, name).restype = ctypes.c_size_t
+        getattr(lib, name).argtypes = [_I64, _I64, _I64]
+    lib.wkv_backward_workspace_size_ex.restype = ctypes.c_size_t
+    lib.wkv_backward_workspace_size_ex.argtypes = [_I64, _I64, _I64, ctypes.c_int]
     lib.wkv_backward.restype = ctypes.c_int
     lib.wkv_backward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                 _P, ctypes.c_size_t, _P]
+                                 ctypes.c_size_t, _P]
+    lib.wkv_backward_train.restype = ctypes.c_int
+    lib.wkv_backward_train.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, ctypes.c_size_t, _P]
     lib.wkv_backward_state.restype = ctypes.c_int
     lib.wkv_backward_state.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -224,14 +236,19 @@ def _forward_common(w, u, k, v, r, workspace, out):
     _need(y, "out", 3, dev, dtype=k.dtype)
     if y.shape != k.shape:
         raise ValueError("out has the wrong shape")
+    lib = load_library()
+    if workspace is None and r is None and k.dtype == torch.float32:
+        # the plain forward: no workspace, nothing kept for a backward
+        _check(lib.wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                               _stream(dev)))
+        return y
     if workspace is None:
         workspace = forward_workspace(B, T, C, dev)
     _check_ws(workspace, dev, "workspace")
-    lib = load_library()
     if k.dtype == torch.float32:
         if r is None:
-            rc = lib.wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                 _ptr(workspace), workspace.numel(), _stream(dev))
+            rc = lib.wkv_forward_train(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                       _ptr(workspace), workspace.numel(), _stream(dev))
         else:
             rc = lib.wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                        _ptr(y), _ptr(workspace), workspace.numel(), _stream(dev))
@@ -245,8 +262,11 @@ def _forward_common(w, u, k, v, r, workspace, out):
 
 def forward(w, u, k, v, workspace=None, out=None):
     """y [B,T,C] = WKV(w, u, k, v). k, v (and y) are float32, bfloat16 or float16 (all the
-    same; w, u float32). `workspace` (uint8, forward_workspace_size bytes) is allocated if not
-    given; after the call it holds the states backward() can reuse."""
+    same; w, u float32). With `workspace` (uint8, forward_workspace_size bytes) this is the
+    training forward (wkv_forward_train, or wkv_forward_typed for 16-bit storage), which
+    leaves in it the states backward() can reuse; without it, float32 inputs go through
+    wkv_forward (no workspace, nothing kept) and 16-bit ones through wkv_forward_typed with a
+    workspace allocated here."""
     return _forward_common(w, u, k, v, None, workspace, out)
 
 
@@ -286,7 +306,9 @@ def forward_state(w, u, k, v, a, b, p, workspace=None, out=None, r=None):
 
 
 def backward_workspace_size(B: int, T: int, C: int, have_fwd_workspace: bool) -> int:
-    return int(load_library().wkv_backward_workspace_size(B, T, C, 1 if have_fwd_workspace else 0))
+    """Bytes of the backward's workspace, with or without a forward workspace to read."""
+    return int(load_library().wkv_backward_workspace_size_ex(B, T, C,
+                                                             1 if have_fwd_workspace else 0))
 
 
 def _backward_common(w, u, k, v, dy, r, fwd_workspace, workspace, out):
@@ -318,10 +340,14 @@ def _backward_common(w, u, k, v, dy, r, fwd_workspace, workspace, out):
     dr = grads[2] if gated else None
     dw, du = grads[-2], grads[-1]
     lib = load_library()
-    if k.dtype == torch.float32 and not gated:
-        rc = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
-                              _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
-                              _ptr(workspace), workspace.numel(), _stream(dev))
+    if k.dtype == torch.float32 and not gated and fwd_workspace is None:
+        rc = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy), _ptr(dk),
+                              _ptr(dv), _ptr(dw), _ptr(du), _ptr(workspace), workspace.numel(),
+                              _stream(dev))
+    elif k.dtype == torch.float32 and not gated:
+        rc = lib.wkv_backward_train(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                    _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
+                                    _ptr(workspace), workspace.numel(), _stream(dev))
     elif k.dtype == torch.float32:
         rc = lib.wkv_backward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                     _ptr(dy), _ptr(fwd_workspace), _ptr(dk), _ptr(dv), _ptr(dr),

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <mutex>
 #include <random>
+#include <unordered_map>
 
 #include "../../include/rwkv_wkv.h"
 #include "wkv_launch.h"
@@ -115,15 +116,23 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
 int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
-// Forward workspace: flags, aggregates, inclusive carries, chunk carries, the carry
-// entering token 0 and the final state (see wkv_launch.h).
-size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
+// Forward workspace: the stamp, flags, aggregates, inclusive carries (these four are all
+// the scan itself needs: fwd_scan_bytes), then chunk carries, the carry entering token 0
+// and the final state (see wkv_launch.h).
+size_t fwd_scan_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
+    return wkvdev::kWsHeaderBytes + round_up((size_t)B * ngrp * nseg * 8u, 256) +
+           2 * round_up(recs, 256);
+}
+
+size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
+    const size_t nseg = (size_t)nseg_of(T);
     const size_t nbc = (size_t)B * (size_t)C;
     const size_t recs = nbc * nseg * (wkvdev::kRecFields * sizeof(double));
     const size_t cin = recs * (size_t)wkvdev::kCinCarries;
-    return round_up((size_t)B * ngrp * nseg * 8u, 256) + 2 * round_up(recs, 256) +
-           round_up(cin, 256) + round_up(nbc * (wkvdev::kRecFields * sizeof(double)), 256) +
+    return fwd_scan_bytes(B, T, C) + round_up(cin, 256) +
+           round_up(nbc * (wkvdev::kRecFields * sizeof(double)), 256) +
            round_up(nbc * 3 * sizeof(float), 256);
 }
 
@@ -133,6 +142,8 @@ wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
     const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
     char *p = static_cast<char *>(ws);
     L.nseg = (int64_t)nseg;
+    L.hdr = reinterpret_cast<uint64_t *>(p);
+    p += wkvdev::kWsHeaderBytes;
     L.flags = reinterpret_cast<uint64_t *>(p);
     p += round_up((size_t)B * ngrp * nseg * 8u, 256);
     L.agg = reinterpret_cast<double *>(p);
@@ -191,6 +202,44 @@ uint64_t next_epoch() {
         g_epoch.store(seed & ((uint64_t(1) << 60) - 1));
     });
     return (g_epoch.fetch_add(1) + 1) & ((uint64_t(1) << 61) - 1);
+}
+
+// What this process last left in each forward workspace it filled (by address): whether the
+// states a backward reads were kept, and for which (B, T, C). A backward given a workspace
+// that an inference forward filled, or one filled for other sizes, is refused here; the
+// device-side stamp (checked when dw, du are summed) catches what this map cannot see.
+struct WsRecord {
+    int64_t B, T, C;
+    bool kept;
+};
+std::mutex g_ws_mu;
+std::unordered_map<uintptr_t, WsRecord> g_ws;
+
+void note_workspace(const void *ws, int64_t B, int64_t T, int64_t C, bool kept) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (g_ws.size() >= 4096) g_ws.clear();  // bounded; a forgotten entry only skips this check
+    g_ws[reinterpret_cast<uintptr_t>(ws)] = WsRecord{B, T, C, kept};
+}
+
+bool workspace_usable(const void *ws, int64_t B, int64_t T, int64_t C, const char *fn) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    const auto it = g_ws.find(reinterpret_cast<uintptr_t>(ws));
+    if (it == g_ws.end()) return true;
+    const WsRecord &r = it->second;
+    if (!r.kept) {
+        fail(WKV_ERR_INVALID_ARG,
+             "%s: fwd_workspace was last filled by wkv_forward_infer, which keeps no states "
+             "for a backward", fn);
+        return false;
+    }
+    if (r.B != B || r.T != T || r.C != C) {
+        fail(WKV_ERR_INVALID_ARG,
+             "%s: fwd_workspace was last filled for B=%lld T=%lld C=%lld, not B=%lld T=%lld "
+             "C=%lld", fn, (long long)r.B, (long long)r.T, (long long)r.C, (long long)B,
+             (long long)T, (long long)C);
+        return false;
+    }
+    return true;
 }
 
 // The storage format of a dtype code (WKV_F32, WKV_BF16, WKV_F16).
@@ -269,10 +318,12 @@ namespace {
 
 // wkv_forward, wkv_forward_state and wkv_forward_gated: sa, sb, sp are the state arrays of
 // the second (all three non-null) or null, r the gate of the third or null.
+// With validate_only the arguments are checked (workspace included) and nothing is launched.
 int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt,
                  const float *w, const float *u, const void *k, const void *v, const void *r,
                  void *y, float *sa, float *sb, float *sp, void *workspace,
-                 size_t workspace_bytes, void *stream, bool keep = true) {
+                 size_t workspace_bytes, void *stream, bool keep = true,
+                 bool validate_only = false) {
     g_err[0] = '\0';
     if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
     if (B == 0 || T == 0 || C == 0) return WKV_OK;
@@ -286,7 +337,7 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt
         !aligned(workspace, 16, "workspace", fn))
         return WKV_ERR_INVALID_ARG;
     const size_t nb = (size_t)(B * T * C) * es;
-    const size_t need = fwd_ws_bytes(B, T, C);
+    const size_t need = validate_only ? workspace_bytes : fwd_ws_bytes(B, T, C);
     if (workspace_bytes < need)
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
@@ -319,12 +370,14 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt
                                 sn[i], sn[j]);
         }
     }
+    if (validate_only) return WKV_OK;
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
     hipError_t e = wkvdev::launch_forward(B, T, C, fmt, w, u, k, v, r, y, sa, sb, sp,
                                           fwd_layout(B, T, C, workspace), next_epoch(), keep,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, fn);
+    note_workspace(workspace, B, T, C, keep);
     return WKV_OK;
 }
 
@@ -332,11 +385,40 @@ int forward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fmt
 
 extern "C" {
 
-int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                const float *k, const float *v, float *y, void *workspace,
-                size_t workspace_bytes, void *stream) {
-    return forward_call("wkv_forward", B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y,
+int wkv_forward_train(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                      const float *k, const float *v, float *y, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return forward_call("wkv_forward_train", B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y,
                         nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                const float *k, const float *v, float *y, void *stream) {
+    static const char *fn = "wkv_forward";
+    g_err[0] = '\0';
+    if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    // the look-back's records live in memory taken from the device's stream-ordered pool for
+    // the duration of the call (allocated and released on `stream`); validation happens
+    // before that, on a placeholder address that overlaps nothing
+    void *const probe = reinterpret_cast<void *>(uintptr_t(1) << 62);
+    const size_t need = fwd_scan_bytes(B, T, C);
+    int rc = forward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, nullptr,
+                          nullptr, nullptr, probe, need, nullptr, false, true);
+    if (rc != WKV_OK) return rc;
+    rc = check_device(fn);
+    if (rc != WKV_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) return fail_hip(e, "wkv_forward: scratch from the stream-ordered pool");
+    e = wkvdev::launch_forward(B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, nullptr,
+                               nullptr, nullptr, fwd_layout(B, T, C, ws), next_epoch(), false,
+                               st);
+    const hipError_t e2 = hipFreeAsync(ws, st);
+    if (e != hipSuccess) return fail_hip(e, fn);
+    if (e2 != hipSuccess) return fail_hip(e2, "wkv_forward: releasing its scratch");
+    return WKV_OK;
 }
 
 int wkv_forward_state(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -404,12 +486,21 @@ int wkv_forward_typed(int dtype, int64_t B, int64_t T, int64_t C, const float *w
                         workspace, workspace_bytes, stream);
 }
 
-size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C, int have_fwd_workspace) {
+size_t wkv_backward_workspace_size_ex(int64_t B, int64_t T, int64_t C,
+                                      int have_fwd_workspace) {
     if (B < 0 || T < 0 || C < 0 || C > kMaxC) return 0;
     if (B > 0 && T > 0 && C > 0 && (T > kMaxElems / B || B * T > kMaxElems / C)) return 0;
     size_t ws = bwd_own_bytes(B, T, C);
     if (!have_fwd_workspace) ws += fwd_ws_bytes(B, T, C);
     return ws;
+}
+
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
+    return wkv_backward_workspace_size_ex(B, T, C, 0);
+}
+
+size_t wkv_backward_train_workspace_size(int64_t B, int64_t T, int64_t C) {
+    return wkv_backward_workspace_size_ex(B, T, C, 1);
 }
 
 }  // extern "C"
@@ -451,7 +542,7 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
     if (!aligned(workspace, 16, "workspace", fn)) return WKV_ERR_INVALID_ARG;
     if (fwd_workspace != nullptr && !aligned(fwd_workspace, 16, "fwd_workspace", fn))
         return WKV_ERR_INVALID_ARG;
-    const size_t need = wkv_backward_workspace_size(B, T, C, fwd_workspace != nullptr);
+    const size_t need = wkv_backward_workspace_size_ex(B, T, C, fwd_workspace != nullptr);
     if (workspace_bytes < need)
         return fail(WKV_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
@@ -476,6 +567,8 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
             if (overlap(outs[i], osz[i], outs[j], osz[j]))
                 return fail(WKV_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
     }
+    if (fwd_workspace != nullptr && !workspace_usable(fwd_workspace, B, T, C, fn))
+        return WKV_ERR_INVALID_ARG;
     int rc = check_device(fn);
     if (rc != WKV_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -502,12 +595,23 @@ int backward_call(const char *fn, int64_t B, int64_t T, int64_t C, wkvdev::Io fm
 extern "C" {
 
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                 const float *k, const float *v, const float *dy, const void *fwd_workspace,
-                 float *dk, float *dv, float *dw, float *du, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+                 const float *k, const float *v, const float *dy, float *dk, float *dv,
+                 float *dw, float *du, void *workspace, size_t workspace_bytes, void *stream) {
     return backward_call("wkv_backward", B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr,
-                         fwd_workspace, dk, dv, nullptr, dw, du, workspace, workspace_bytes,
-                         stream);
+                         nullptr, dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream);
+}
+
+int wkv_backward_train(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                       const float *k, const float *v, const float *dy,
+                       const void *fwd_workspace, float *dk, float *dv, float *dw, float *du,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "wkv_backward_train";
+    if (B > 0 && T > 0 && C > 0) {
+        g_err[0] = '\0';
+        if (!nonnull(fwd_workspace, "fwd_workspace", fn)) return WKV_ERR_INVALID_ARG;
+    }
+    return backward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, dy, nullptr, fwd_workspace,
+                         dk, dv, nullptr, dw, du, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -632,9 +632,12 @@ __global__ __launch_bounds__(NW * 64, 3) void wkv_backward_kernel(
 constexpr int kReduceCh = 16;      // channels of a workgroup: one 128-byte row of fp64
 constexpr int kReduceSlices = 32;  // row slices of a workgroup
 
+// The forward workspace's stamp must show a launch that kept the backward's states for the
+// same (B, T, C); otherwise dw and du are set to NaN (the host refuses such a call when it
+// can tell; this catches what it cannot, e.g. a workspace filled by another process).
 __global__ __launch_bounds__(kReduceCh * kReduceSlices) void wkv_reduce_kernel(
     int64_t npart, int64_t C, const double *__restrict__ part, float *__restrict__ dw,
-    float *__restrict__ du) {
+    float *__restrict__ du, const uint64_t *__restrict__ hdr, int64_t B, int64_t T) {
     constexpr int RS = kReduceSlices, RB = 8;
     __shared__ double sw_[RS][kReduceCh], su_[RS][kReduceCh];
     const int ch = (int)threadIdx.x % kReduceCh;
@@ -669,8 +672,10 @@ __global__ __launch_bounds__(kReduceCh * kReduceSlices) void wkv_reduce_kernel(
             tw += sw_[r][ch];
             tu += su_[r][ch];
         }
-        dw[c] = (float)tw;
-        du[c] = (float)tu;
+        const bool stamped = hdr[0] == (kWsTag | kWsKept) && hdr[1] == (uint64_t)B &&
+                             hdr[2] == (uint64_t)T && hdr[3] == (uint64_t)C;
+        dw[c] = stamped ? (float)tw : __builtin_nanf("");
+        du[c] = stamped ? (float)tu : __builtin_nanf("");
     }
 }
 
@@ -844,7 +849,7 @@ hipError_t launch_backward(int64_t B, int64_t T, int64_t C, Io fmt, const float 
     }
     hipLaunchKernelGGL(wkv_reduce_kernel, dim3((unsigned)((C + kReduceCh - 1) / kReduceCh)),
                        dim3(kReduceCh * kReduceSlices), 0,
-                       stream, B * L.nseg, C, L.part, dw, du);
+                       stream, B * L.nseg, C, L.part, dw, du, F.hdr, B, T);
     e = hipGetLastError();
     if (e != hipSuccess || ga == nullptr) return e;
     hipLaunchKernelGGL(wkv_state_grad_kernel, nb, dim3(256), 0, stream, n, C, L.nseg, F.init,

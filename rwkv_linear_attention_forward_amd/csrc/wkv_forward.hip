@@ -221,9 +221,16 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     uint64_t *__restrict__ flags,
     double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
     const float *__restrict__ sa, const float *__restrict__ sb, const float *__restrict__ sp,
-    double *__restrict__ init, float *__restrict__ fin) {
+    double *__restrict__ init, float *__restrict__ fin, uint64_t *__restrict__ hdr) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
+    // stamp the workspace with what this launch leaves in it (a backward checks it)
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[0] = kWsTag | (KEEP ? kWsKept : kWsInfer);
+        hdr[1] = (uint64_t)(nbg / ngrp);
+        hdr[2] = (uint64_t)T;
+        hdr[3] = (uint64_t)C;
+    }
 
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -453,12 +460,12 @@ static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int6
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
-                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr);
     else
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
-                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin);
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr);
 }
 
 template <Io F>

@@ -40,6 +40,9 @@ int poll_limit();
 constexpr int kRecFields = 5;
 
 // Forward workspace, carved out of the caller's buffer (see wkv_api.hip):
+//   hdr[32]                 uint64 stamp written by the forward that filled it:
+//                           hdr[0] = kWsTag | kWsKept (states kept for a backward) or
+//                           kWsTag | kWsInfer (inference: nothing kept), hdr[1..3] = B, T, C
 //   flags[nseg][B * ngrp]   uint64 publication flags
 //   agg[5][B][nseg][C]      window aggregates (from the empty state)
 //   incl[5][B][nseg][C]     inclusive carries: the state after window s, i.e. entering s+1
@@ -49,8 +52,13 @@ constexpr int kRecFields = 5;
 //                           512 contiguous bytes per field.
 //   init[5][B][C]           the carry entering token 0 as the forward used it (normalized)
 //   fin[3][B][C]            fp32 state (a, b, p) after the last token, when one is asked for
+constexpr uint64_t kWsTag = 0x574b5657534b0000ull;  // "WKVWSK" in the high bytes
+constexpr uint64_t kWsKept = 1;
+constexpr uint64_t kWsInfer = 2;
+constexpr size_t kWsHeaderBytes = 256;
 struct FwdLayout {
     int64_t nseg;
+    uint64_t *hdr;
     uint64_t *flags;
     double *agg;
     double *incl;

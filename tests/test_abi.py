@@ -59,12 +59,13 @@ def _r256(x):
 
 
 def _fwd_bytes(B, T, C, window=64, chunk=32):
-    """Forward workspace: flags, window aggregates and inclusive carries (40 B records), the
-    carry entering each chunk of a window but its first (5 fp64 fields), the carry entering
-    token 0 (40 B per sequence and channel) and the final fp32 state (12 B)."""
+    """Forward workspace: a 256-byte stamp, flags, window aggregates and inclusive carries
+    (40 B records), the carry entering each chunk of a window but its first (5 fp64 fields),
+    the carry entering token 0 (40 B per sequence and channel) and the final fp32 state
+    (12 B)."""
     nseg, ngrp = -(-T // window), -(-C // 64)
     kept = window // chunk - 1
-    return (_r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 40)
+    return (256 + _r256(B * ngrp * nseg * 8) + 2 * _r256(B * nseg * C * 40)
             + _r256(B * nseg * kept * C * 40) + _r256(B * C * 40) + _r256(B * C * 12))
 
 
@@ -82,9 +83,12 @@ def test_sizes(pkg):
         fwd = _fwd_bytes(B, T, C)
         assert lib.wkv_forward_workspace_size(B, T, C) == fwd
         own = _bwd_bytes(B, T, C)
-        assert lib.wkv_backward_workspace_size(B, T, C, 1) == own
-        assert lib.wkv_backward_workspace_size(B, T, C, 0) == own + fwd
-    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 2 * 768 + 768 + 256 + 256
+        assert lib.wkv_backward_workspace_size_ex(B, T, C, 1) == own
+        assert lib.wkv_backward_workspace_size_ex(B, T, C, 0) == own + fwd
+        assert lib.wkv_backward_train_workspace_size(B, T, C) == own
+        assert lib.wkv_backward_workspace_size(B, T, C) == own + fwd
+    assert lib.wkv_forward_workspace_size(1, 257, 3) == 256 + 256 + 2 * 768 + 768 + 256 + 256
+    assert lib.wkv_backward_workspace_size(-1, 4, 4) == 0
     assert lib.wkv_forward_workspace_size(-1, 4, 4) == 0
     assert lib.wkv_forward_workspace_size(1, 4, (1 << 24) + 1) == 0
 
@@ -94,7 +98,32 @@ FAKE = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(12)]
 
 def _fwd(lib, B, T, C, ptrs=None, ws=FAKE[6], wsbytes=1 << 40):
     p = FAKE if ptrs is None else ptrs
-    return lib.wkv_forward(B, T, C, p[0], p[1], p[2], p[3], p[4], ws, wsbytes, None)
+    return lib.wkv_forward_train(B, T, C, p[0], p[1], p[2], p[3], p[4], ws, wsbytes, None)
+
+
+def test_plain_forward_signature_and_validation(pkg):
+    """wkv_forward(B, T, C, w, u, k, v, y, stream): the same argument checks as the training
+    forward, all before any device call (so none of these reaches the GPU)."""
+    lib = pkg.load_library()
+    f = FAKE
+
+    def call(B=2, T=3, C=4, p=None):
+        q = f if p is None else p
+        return lib.wkv_forward(B, T, C, q[0], q[1], q[2], q[3], q[4], None)
+
+    assert call(B=-1) == pkg.WKV_ERR_INVALID_ARG
+    assert b"negative" in lib.wkv_last_error()
+    assert call(C=(1 << 24) + 1) == pkg.WKV_ERR_INVALID_ARG
+    assert call(p=[f[0], f[1], None, f[3], f[4]]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"k is NULL" in lib.wkv_last_error()
+    assert call(p=[f[0], f[1], f[2], f[3], ctypes.c_void_p(f[2].value + 16)]) == \
+        pkg.WKV_ERR_INVALID_ARG
+    assert b"overlaps" in lib.wkv_last_error()
+    assert call(p=[f[0], f[1], f[2], ctypes.c_void_p(0x300002), f[4]]) == pkg.WKV_ERR_INVALID_ARG
+    assert b"aligned" in lib.wkv_last_error()
+    for B, T, C in ((0, 5, 5), (3, 0, 5), (3, 5, 0)):
+        assert call(B, T, C, [None] * 5) == pkg.WKV_OK
+    assert lib.wkv_last_error() == b""
 
 
 def test_forward_rejects_bad_arguments(pkg):
@@ -221,8 +250,11 @@ def test_forward_infer_rejects_bad_arguments(pkg):
 
 def _bwd(lib, B, T, C, fws=None, ws=FAKE[11], wsbytes=1 << 40, dw=FAKE[9], du=FAKE[10]):
     f = FAKE
-    return lib.wkv_backward(B, T, C, f[0], f[1], f[2], f[3], f[4], fws, f[5], f[6], dw, du, ws,
-                            wsbytes, None)
+    if fws is None:
+        return lib.wkv_backward(B, T, C, f[0], f[1], f[2], f[3], f[4], f[5], f[6], dw, du, ws,
+                                wsbytes, None)
+    return lib.wkv_backward_train(B, T, C, f[0], f[1], f[2], f[3], f[4], fws, f[5], f[6], dw,
+                                  du, ws, wsbytes, None)
 
 
 def test_backward_rejects_bad_arguments(pkg):
@@ -236,10 +268,18 @@ def test_backward_rejects_bad_arguments(pkg):
     assert b"workspace has 100 bytes" in lib.wkv_last_error()
     # dk aliasing dy
     f = FAKE
-    rc = lib.wkv_backward(2, 3, 4, f[0], f[1], f[2], f[3], f[4], None, f[4], f[6], f[9], f[10],
+    rc = lib.wkv_backward(2, 3, 4, f[0], f[1], f[2], f[3], f[4], f[4], f[6], f[9], f[10],
                           f[11], 1 << 40, None)
     assert rc == pkg.WKV_ERR_INVALID_ARG and b"overlaps" in lib.wkv_last_error()
     assert _bwd(lib, 2, 3, 0, dw=None, du=None) == pkg.WKV_OK
+    # the training backward: its forward workspace is required, and its own workspace is the
+    # smaller one
+    rc = lib.wkv_backward_train(2, 3, 4, f[0], f[1], f[2], f[3], f[4], None, f[5], f[6], f[9],
+                                f[10], f[11], 1 << 40, None)
+    assert rc == pkg.WKV_ERR_INVALID_ARG and b"fwd_workspace is NULL" in lib.wkv_last_error()
+    need = lib.wkv_backward_train_workspace_size(2, 300, 4)
+    assert _bwd(lib, 2, 300, 4, fws=f[7], wsbytes=need - 1) == pkg.WKV_ERR_INVALID_ARG
+    assert b"workspace has" in lib.wkv_last_error()
 
 
 def test_backward_state_rejects_bad_arguments(pkg):
