@@ -91,6 +91,23 @@ const char *wkv_last_error(void);
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                 const float *k, const float *v, float *y, void *stream);
 
+/* wkv_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same scan and bitwise the
+ * same y, with its scratch (the flags and window records, wkv_forward_noalloc_scratch_bytes
+ * bytes) in an array of wkv_forward_noalloc_max_scratch() bytes (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends. No allocation of any kind happens
+ * in the call. Sizes whose scratch exceeds the array are refused with WKV_ERR_INVALID_ARG
+ * before any launch (the 3B-class layer, B=8 T=4096 C=2560, needs 63 MB). Calls on one GPU
+ * share the array: two such calls that overlap in time on the same GPU (different streams,
+ * or concurrent host threads) race and must not be made; calls one after another on a
+ * stream are fine (nothing needs clearing between them). */
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                        const float *k, const float *v, float *y, void *stream);
+/* Scratch wkv_forward_noalloc needs for (B, T, C) (0 for invalid dims), and the most it can
+ * take. */
+size_t wkv_forward_noalloc_scratch_bytes(int64_t B, int64_t T, int64_t C);
+size_t wkv_forward_noalloc_max_scratch(void);
+
 /* Bytes of device scratch that wkv_forward_train and wkv_forward_state need for (B, T, C):
  * a 256-byte stamp, publication flags plus, for every (b, c) sequence and every 64-token
  * window, the window's aggregate and the recurrent state after it, the state entering the

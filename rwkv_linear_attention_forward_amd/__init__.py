@@ -40,7 +40,9 @@ WKV_ERR_HIP = 3
 # Every symbol the header declares, for the export check.
 EXPORTS = ("wkv_version", "wkv_set_poll_limit", "wkv_poll_limit", "wkv_status_string",
            "wkv_last_error", "wkv_forward_workspace_size",
-           "wkv_forward", "wkv_forward_train", "wkv_forward_state", "wkv_forward_gated",
+           "wkv_forward", "wkv_forward_noalloc", "wkv_forward_noalloc_scratch_bytes",
+           "wkv_forward_noalloc_max_scratch",
+           "wkv_forward_train", "wkv_forward_state", "wkv_forward_gated",
            "wkv_forward_typed", "wkv_forward_infer",
            "wkv_backward_workspace_size", "wkv_backward_train_workspace_size",
            "wkv_backward_workspace_size_ex", "wkv_backward", "wkv_backward_train",
@@ -82,6 +84,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.wkv_forward.restype = ctypes.c_int
     lib.wkv_forward.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+    lib.wkv_forward_noalloc.restype = ctypes.c_int
+    lib.wkv_forward_noalloc.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+    lib.wkv_forward_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.wkv_forward_noalloc_scratch_bytes.argtypes = [_I64, _I64, _I64]
+    lib.wkv_forward_noalloc_max_scratch.restype = ctypes.c_size_t
+    lib.wkv_forward_noalloc_max_scratch.argtypes = []
     lib.wkv_forward_train.restype = ctypes.c_int
     lib.wkv_forward_train.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                       _P]

@@ -116,24 +116,46 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t nseg_of(int64_t T) { return (T + wkvdev::kFwdWindow - 1) / wkvdev::kFwdWindow; }
 int64_t bseg_of(int64_t T) { return (T + wkvdev::kBwdWindow - 1) / wkvdev::kBwdWindow; }
 
-// Forward workspace: the stamp, flags, aggregates, inclusive carries (these four are all
-// the scan itself needs: fwd_scan_bytes), then chunk carries, the carry entering token 0
-// and the final state (see wkv_launch.h).
+// Forward workspace: the stamp, flags, aggregates, inclusive carries, chunk carries, the
+// carry entering token 0 and the final state (see wkv_launch.h).
+size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t nbc = (size_t)B * (size_t)C;
+    const size_t recs = nbc * nseg * (wkvdev::kRecFields * sizeof(double));
+    const size_t cin = recs * (size_t)wkvdev::kCinCarries;
+    return wkvdev::kWsHeaderBytes + round_up((size_t)B * ngrp * nseg * 8u, 256) +
+           2 * round_up(recs, 256) + round_up(cin, 256) +
+           round_up(nbc * (wkvdev::kRecFields * sizeof(double)), 256) +
+           round_up(nbc * 3 * sizeof(float), 256);
+}
+
+// The compact scan layout of a forward that keeps nothing and takes no state: the stamp,
+// the flags, and agg, incl with the three fields (a, b, P) such a forward stores.
+constexpr size_t kScanFields = 3;
 size_t fwd_scan_bytes(int64_t B, int64_t T, int64_t C) {
     const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
-    const size_t recs = (size_t)B * nseg * (size_t)C * (wkvdev::kRecFields * sizeof(double));
+    const size_t recs = (size_t)B * nseg * (size_t)C * (kScanFields * sizeof(double));
     return wkvdev::kWsHeaderBytes + round_up((size_t)B * ngrp * nseg * 8u, 256) +
            2 * round_up(recs, 256);
 }
 
-size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t C) {
-    const size_t nseg = (size_t)nseg_of(T);
-    const size_t nbc = (size_t)B * (size_t)C;
-    const size_t recs = nbc * nseg * (wkvdev::kRecFields * sizeof(double));
-    const size_t cin = recs * (size_t)wkvdev::kCinCarries;
-    return fwd_scan_bytes(B, T, C) + round_up(cin, 256) +
-           round_up(nbc * (wkvdev::kRecFields * sizeof(double)), 256) +
-           round_up(nbc * 3 * sizeof(float), 256);
+wkvdev::FwdLayout scan_layout(int64_t B, int64_t T, int64_t C, void *ws) {
+    wkvdev::FwdLayout L;
+    const size_t nseg = (size_t)nseg_of(T), ngrp = (size_t)((C + 63) / 64);
+    const size_t recs = (size_t)B * nseg * (size_t)C * (kScanFields * sizeof(double));
+    char *p = static_cast<char *>(ws);
+    L.nseg = (int64_t)nseg;
+    L.hdr = reinterpret_cast<uint64_t *>(p);
+    p += wkvdev::kWsHeaderBytes;
+    L.flags = reinterpret_cast<uint64_t *>(p);
+    p += round_up((size_t)B * ngrp * nseg * 8u, 256);
+    L.agg = reinterpret_cast<double *>(p);
+    p += round_up(recs, 256);
+    L.incl = reinterpret_cast<double *>(p);
+    L.cin = nullptr;
+    L.init = nullptr;
+    L.fin = nullptr;
+    return L;
 }
 
 wkvdev::FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C, void *ws) {
@@ -392,6 +414,80 @@ int wkv_forward_train(int64_t B, int64_t T, int64_t C, const float *w, const flo
                         nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of wkv_forward_noalloc: one copy per GPU, held from the library's load to the end
+// of the process. Host code never uses this name as an address (on the host it is only a
+// stand-in); it uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[256];  // per device id; null until looked up
+
+int scratch_address(const char *fn, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, fn);
+    if (dev < 0 || dev >= 256) return fail(WKV_ERR_UNSUPPORTED, "%s: device id %d", fn, dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "wkv_forward_noalloc: scratch address");
+        if (p == nullptr)
+            return fail(WKV_ERR_HIP, "%s: scratch address of device %d is null", fn, dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return WKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv_forward_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+size_t wkv_forward_noalloc_scratch_bytes(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || C > kMaxC) return 0;
+    if (B > 0 && T > 0 && C > 0 && (T > kMaxElems / B || B * T > kMaxElems / C)) return 0;
+    return fwd_scan_bytes(B, T, C);
+}
+
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                        const float *k, const float *v, float *y, void *stream) {
+    static const char *fn = "wkv_forward_noalloc";
+    g_err[0] = '\0';
+    if (!dims_ok(B, T, C, fn)) return WKV_ERR_INVALID_ARG;
+    if (B == 0 || T == 0 || C == 0) return WKV_OK;
+    const size_t need = fwd_scan_bytes(B, T, C);
+    if (need > kNoAllocScratchBytes)
+        return fail(WKV_ERR_INVALID_ARG,
+                    "%s: B=%lld T=%lld C=%lld needs %zu bytes of scratch, more than the %zu the "
+                    "library holds per GPU (use wkv_forward or wkv_forward_infer)", fn,
+                    (long long)B, (long long)T, (long long)C, need, kNoAllocScratchBytes);
+    void *const probe = reinterpret_cast<void *>(uintptr_t(1) << 62);
+    int rc = forward_call(fn, B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, nullptr,
+                          nullptr, nullptr, probe, need, nullptr, false, true);
+    if (rc != WKV_OK) return rc;
+    rc = check_device(fn);
+    if (rc != WKV_OK) return rc;
+    void *ws = nullptr;
+    rc = scratch_address(fn, &ws);
+    if (rc != WKV_OK) return rc;
+    // the flags carry a per-call epoch, so what an earlier call left in the array is never
+    // taken for this call's: nothing needs clearing
+    hipError_t e = wkvdev::launch_forward(B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y,
+                                          nullptr, nullptr, nullptr, scan_layout(B, T, C, ws),
+                                          next_epoch(), false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, fn);
+    return WKV_OK;
+}
+
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                 const float *k, const float *v, float *y, void *stream) {
     static const char *fn = "wkv_forward";
@@ -413,7 +509,7 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
     hipError_t e = hipMallocAsync(&ws, need, st);
     if (e != hipSuccess) return fail_hip(e, "wkv_forward: scratch from the stream-ordered pool");
     e = wkvdev::launch_forward(B, T, C, wkvdev::Io::F32, w, u, k, v, nullptr, y, nullptr,
-                               nullptr, nullptr, fwd_layout(B, T, C, ws), next_epoch(), false,
+                               nullptr, nullptr, scan_layout(B, T, C, ws), next_epoch(), false,
                                st);
     const hipError_t e2 = hipFreeAsync(ws, st);
     if (e != hipSuccess) return fail_hip(e, fn);

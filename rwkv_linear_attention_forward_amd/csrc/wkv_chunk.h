@@ -237,15 +237,16 @@ __device__ __forceinline__ Carry get_rec(const double *r, int64_t n, int64_t i) 
     return Carry{get_u64(r + i), get_u64(r + n + i), get_u64(r + 2 * n + i),
                  get_u64(r + 3 * n + i), get_u64(r + 4 * n + i)};
 }
-// The same records without the age-weighted fields (a, b and P only; a', b' are left as
-// they are in memory and read back as 0), for a forward whose states no backward will use.
+// The same records without the age-weighted fields, for a forward whose states no backward
+// will use: a, b and P in the first three field slots (a', b' read back as 0), so that such
+// a forward's record arrays need only 3 * n doubles each.
 __device__ __forceinline__ void put_rec3(double *r, int64_t n, int64_t i, const Carry &c) {
     put_u64(r + i, c.a);
     put_u64(r + n + i, c.b);
-    put_u64(r + 4 * n + i, c.P);
+    put_u64(r + 2 * n + i, c.P);
 }
 __device__ __forceinline__ Carry get_rec3(const double *r, int64_t n, int64_t i) {
-    return Carry{get_u64(r + i), get_u64(r + n + i), 0.0, 0.0, get_u64(r + 4 * n + i)};
+    return Carry{get_u64(r + i), get_u64(r + n + i), 0.0, 0.0, get_u64(r + 2 * n + i)};
 }
 __device__ __forceinline__ void put_flag(uint64_t *f, uint64_t epoch, uint64_t status) {
     publish_fence();

@@ -52,6 +52,9 @@ constexpr int kRecFields = 5;
 //                           512 contiguous bytes per field.
 //   init[5][B][C]           the carry entering token 0 as the forward used it (normalized)
 //   fin[3][B][C]            fp32 state (a, b, p) after the last token, when one is asked for
+// A forward that keeps nothing for a backward and takes no state (the plain wkv_forward)
+// needs only the stamp, the flags and agg, incl with three fields each (a, b, P): the
+// compact scan layout (cin, init, fin null).
 constexpr uint64_t kWsTag = 0x574b5657534b0000ull;  // "WKVWSK" in the high bytes
 constexpr uint64_t kWsKept = 1;
 constexpr uint64_t kWsInfer = 2;
