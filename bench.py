@@ -509,6 +509,196 @@ def bench_shift(wkv, torch, dev, steps=100, warmup=50):
             "backward_frac_of_peak": 20 * n / (b_us * 1e-6) / 1e9 / PEAK_GBPS, "steps": steps}
 
 
+# ---------------------------------------------------------------------------------------
+# the other synthetic workloads, each with its oracle baseline
+# ---------------------------------------------------------------------------------------
+FLUSH_BYTES = 1 << 30  # written between timed iterations of the small workloads (> MALL)
+
+
+def settle_clocks(torch, dev, seconds=1.0):
+    """Sustained device copies for `seconds` before anything is timed: from idle, the GPU's
+    clocks take a few hundred milliseconds of back-to-back work to reach their steady
+    rate (the first steps otherwise run up to a third slower)."""
+    a = torch.empty(1 << 28, device=dev)
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b.copy_(a)
+        torch.cuda.synchronize(dev)
+
+
+def _oracle_time(fn, min_s=0.3, max_runs=20):
+    """Median seconds of fn() over repeated runs (at least one, until min_s has passed)."""
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > min_s:
+            break
+    return statistics.median(times), len(times)
+
+
+def bench_workload(wkv, torch, dev, name, with_bwd, reps, warmup, flush, cpu=True):
+    """One synthetic workload as the benchmark configures it: the plain forward alone
+    (wkv_forward) or the training pair (wkv_forward_train + wkv_backward_train), each
+    iteration preceded (outside the timed events) by a 1 GiB write that evicts the 256 MB
+    Infinity Cache, so that small inputs are not read from it; median over `reps`."""
+    import oracle
+    import wkv_inputs
+    x = wkv_inputs.generate(name, with_dy=with_bwd)
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in x}
+    B, T, C = t["k"].shape
+    n = B * T * C
+    y = torch.empty_like(t["k"])
+    scrub = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+    if with_bwd:
+        fws = wkv.forward_workspace(B, T, C, dev)
+        bws = torch.empty(max(16, wkv.backward_workspace_size(B, T, C, True)),
+                          dtype=torch.uint8, device=dev)
+        outs = (torch.empty_like(t["k"]), torch.empty_like(t["k"]), torch.empty_like(t["w"]),
+                torch.empty_like(t["u"]))
+
+    def one(ev=None):
+        if scrub is not None:
+            scrub.zero_()
+        if ev is not None:
+            ev[0].record()
+        if with_bwd:
+            wkv.forward(t["w"], t["u"], t["k"], t["v"], workspace=fws, out=y)
+        else:
+            wkv.forward(t["w"], t["u"], t["k"], t["v"], out=y)
+        if ev is not None:
+            ev[1].record()
+        if with_bwd:
+            wkv.backward(t["w"], t["u"], t["k"], t["v"], t["dy"], fwd_workspace=fws,
+                         workspace=bws, out=outs)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in evs:
+        one(e)
+    torch.cuda.synchronize(dev)
+    f_us = statistics.median(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    ok = bool(torch.isfinite(y).all())
+    r = {"workload": "%s B=%d T=%d C=%d" % (name, B, T, C), "B": B, "T": T, "C": C,
+         "ops": "fwd+bwd" if with_bwd else "fwd",
+         "forward_us": f_us, "forward_gbps": 12 * n / (f_us * 1e-6) / 1e9,
+         "forward_frac_of_peak": 12 * n / (f_us * 1e-6) / 1e9 / PEAK_GBPS,
+         "mall_flushed": bool(flush), "reps": reps,
+         "timing": "HIP events on the library's stream, median of the timed iterations"}
+    tot_us = f_us
+    alg = 12 * n
+    if with_bwd:
+        b_us = statistics.median(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+        ok = ok and all(bool(torch.isfinite(a).all()) for a in outs)
+        r.update(backward_us=b_us, backward_gbps=20 * n / (b_us * 1e-6) / 1e9,
+                 backward_frac_of_peak=20 * n / (b_us * 1e-6) / 1e9 / PEAK_GBPS)
+        tot_us += b_us
+        alg += 20 * n
+    r.update(elem_per_s=n / (tot_us * 1e-6), algorithmic_gbps=alg / (tot_us * 1e-6) / 1e9,
+             frac_of_peak=alg / (tot_us * 1e-6) / 1e9 / PEAK_GBPS, outputs_finite=ok)
+    if cpu:
+        def run():
+            oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
+            if with_bwd:
+                oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
+        sec, runs = _oracle_time(run)
+        r["cpu_baseline"] = {
+            "value": n / sec, "unit": "elem/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "full workload, fp64 plain recurrence forward%s (OpenMP over b, c), median "
+                      "of %d runs" % (" + linear-time backward" if with_bwd else "", runs)}
+        r["speedup_vs_cpu"] = r["elem_per_s"] / r["cpu_baseline"]["value"]
+    return r
+
+
+def bench_decode_horizon(wkv, torch, dev, steps=1000):
+    """The batched decode workload over its whole horizon: each step draws the 40 layers'
+    k, v on the device (outside the timing) and replays the step's 40 calls from a captured
+    graph; the time of each step is recorded, so that the first steps and the last (the
+    state then holds 1000 tokens) can be compared: the per-token cost of the recursive form
+    does not grow with the context."""
+    import wkv_inputs
+    cfg = wkv_inputs.DECODE
+    B, C, L = cfg["B"], cfg["C"], cfg["layers"]
+    params = [wkv_inputs.decode_layer_params(l) for l in range(L)]
+    w = [torch.from_numpy(pw).to(dev) for pw, _ in params]
+    u = [torch.from_numpy(pu).to(dev) for _, pu in params]
+    st = [tuple(torch.from_numpy(a).to(dev) for a in wkv_inputs.empty_decode_state(B, C))
+          for _ in range(L)]
+    y = torch.empty(B, C, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+    kv = torch.empty(L, 2, B, C, device=dev)
+
+    def calls():
+        for l in range(L):
+            wkv.decode_step(w[l], u[l], kv[l, 0], kv[l, 1], *st[l], out=y)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    # the captured warm-up call advanced the states: start the horizon from empty again
+    for l in range(L):
+        for a, src in zip(st[l], wkv_inputs.empty_decode_state(B, C)):
+            a.copy_(torch.from_numpy(src))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        kv.normal_(generator=gen)
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize(dev)
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    first = statistics.median(us[:10])
+    last = statistics.median(us[-10:])
+    ok = all(bool(torch.isfinite(a).all()) for s_ in st for a in s_)
+    return {"steps": steps, "calls_per_step": L, "step_us_median": statistics.median(us),
+            "first10_step_us_median": first, "last10_step_us_median": last,
+            "last_over_first": last / first, "states_finite": ok,
+            "timing": "graph replay of the step's 40 calls, HIP events per step"}
+
+
+def decode_cpu_baseline(steps=20):
+    """The oracle's decode step over all 40 layers of the batched decode workload for
+    `steps` steps (each layer's k, v drawn once and reused at every step: the oracle's work
+    does not depend on the values), timed per call; the per-step time is the sum over the
+    40 layers."""
+    import oracle
+    import wkv_inputs
+    cfg = wkv_inputs.DECODE
+    B, C, L = cfg["B"], cfg["C"], cfg["layers"]
+    layers = []
+    for l in range(L):
+        wn, un = wkv_inputs.decode_layer_params(l)
+        kn, vn = wkv_inputs.decode_step_inputs(0, l)
+        layers.append((wn, un, kn, vn))
+    states = [None] * L
+    total = 0.0
+    for s in range(steps):
+        for l, (wn, un, kn, vn) in enumerate(layers):
+            t0 = time.perf_counter()
+            _, states[l] = oracle.decode_step(wn, un, kn, vn, states[l])
+            total += time.perf_counter() - t0
+    per_step = total / steps
+    return {"value": B * C * L / per_step, "unit": "elem/s (B*C per layer-call)",
+            "cores": oracle.num_threads(), "kind": "oracle", "step_ms": per_step * 1e3,
+            "sample": "40 layers x %d steps of the 256 x 5120 decode workload, fp64 rescaled "
+                      "recursion (OpenMP over b, c), measured on %d steps" % (steps, steps)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -522,8 +712,11 @@ def main(argv=None):
                     help="skip the receptance-gated measurement")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bfloat16 measurement")
     ap.add_argument("--no-shift", action="store_true", help="skip the token-shift measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other synthetic workloads (small, 169M-class, long context, "
+                         "the decode horizon)")
     ap.add_argument("--with-copy", action="store_true",
-                    help="also time a 1 GiB device copy (scales rocprofv3 byte counters)")
+                    help="(kept for old commands: the 1 GiB device copy is always timed)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the step's kernel durations from a rocprofv3 --kernel-trace "
@@ -557,6 +750,7 @@ def main(argv=None):
         return 2
     dev = torch.device("cuda:0")
     x = wkv_inputs.generate("l3b", with_dy=True)
+    settle_clocks(torch, dev)
     r = bench_step(wkv, torch, dev, x, args.steps, args.warmup)
     B, T, C = r["B"], r["T"], r["C"]
     n = B * T * C
@@ -585,8 +779,17 @@ def main(argv=None):
         "forward_frac_of_peak": 12 * n / (fwd * 1e-3) / 1e9 / PEAK_GBPS,
         "outputs_finite": r["finite"],
     }
-    if args.with_copy:
-        out["copy_1gib"] = bench_copy(torch, dev)
+    out["copy_1gib"] = bench_copy(torch, dev)
+    if not args.no_configs:
+        cpu = not args.no_cpu
+        out["configs"] = {
+            "small": bench_workload(wkv, torch, dev, "small", True, 50, 10, True, cpu),
+            "l169m": bench_workload(wkv, torch, dev, "l169m", False, 50, 10, True, cpu),
+            "longctx": bench_workload(wkv, torch, dev, "longctx", True, 30, 10, True, cpu),
+        }
+        out["configs"]["decode_horizon"] = bench_decode_horizon(wkv, torch, dev)
+        if cpu:
+            out["configs"]["decode_horizon"]["cpu_baseline"] = decode_cpu_baseline()
     if not args.no_decode:
         out["decode"] = bench_decode(wkv, torch, dev)
         out["decode"]["bf16"] = bench_decode(wkv, torch, dev, dtype=torch.bfloat16)

@@ -640,6 +640,9 @@ __global__ __launch_bounds__(kReduceCh * kReduceSlices) void wkv_reduce_kernel(
     float *__restrict__ du, const uint64_t *__restrict__ hdr, int64_t B, int64_t T) {
     constexpr int RS = kReduceSlices, RB = 8;
     __shared__ double sw_[RS][kReduceCh], su_[RS][kReduceCh];
+    // uniform across the launch: read once, up front
+    const bool stamped = hdr[0] == (kWsTag | kWsKept) && hdr[1] == (uint64_t)B &&
+                         hdr[2] == (uint64_t)T && hdr[3] == (uint64_t)C;
     const int ch = (int)threadIdx.x % kReduceCh;
     const int sl = (int)threadIdx.x / kReduceCh;
     const int64_t c = (int64_t)blockIdx.x * kReduceCh + ch;
@@ -672,8 +675,6 @@ __global__ __launch_bounds__(kReduceCh * kReduceSlices) void wkv_reduce_kernel(
             tw += sw_[r][ch];
             tu += su_[r][ch];
         }
-        const bool stamped = hdr[0] == (kWsTag | kWsKept) && hdr[1] == (uint64_t)B &&
-                             hdr[2] == (uint64_t)T && hdr[3] == (uint64_t)C;
         dw[c] = stamped ? (float)tw : __builtin_nanf("");
         du[c] = stamped ? (float)tu : __builtin_nanf("");
     }

@@ -209,6 +209,16 @@ __device__ __forceinline__ Carry window_aggregate(FwdShared<NW> &sh, int64_t j, 
     return X;
 }
 
+// The workspace stamp (see wkv_launch.h), written by one thread of the first unit; kept out of
+// line so that it costs the kernel no registers.
+__device__ __noinline__ void stamp_workspace(uint64_t *hdr, bool keep, int64_t B, int64_t T,
+                                             int64_t C) {
+    hdr[0] = kWsTag | (keep ? kWsKept : kWsInfer);
+    hdr[1] = (uint64_t)B;
+    hdr[2] = (uint64_t)T;
+    hdr[3] = (uint64_t)C;
+}
+
 // GATE: the output is sigma(r) * y (r [B][T][C]) instead of y. F: the storage format of k,
 // v, r and y. KEEP: the workspace keeps what the backward reads (the age-weighted fields of
 // the records, the carry entering each window's second chunk and token 0); without it the
@@ -221,16 +231,10 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     uint64_t *__restrict__ flags,
     double *__restrict__ agg, double *__restrict__ incl, int64_t nrec, double *__restrict__ cin,
     const float *__restrict__ sa, const float *__restrict__ sb, const float *__restrict__ sp,
-    double *__restrict__ init, float *__restrict__ fin, uint64_t *__restrict__ hdr) {
+    double *__restrict__ init, float *__restrict__ fin, uint64_t *__restrict__ hdr,
+    int64_t B) {
     constexpr int WIN = NW * CH;
     __shared__ FwdShared<NW> sh;
-    // stamp the workspace with what this launch leaves in it (a backward checks it)
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        hdr[0] = kWsTag | (KEEP ? kWsKept : kWsInfer);
-        hdr[1] = (uint64_t)(nbg / ngrp);
-        hdr[2] = (uint64_t)T;
-        hdr[3] = (uint64_t)C;
-    }
 
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -385,6 +389,8 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
         else
             final_state<CH>(kc, vc, Lv, ref, mine, dwfd, fin, nrec / nseg, bidx * C + cl);
     }
+    // stamp the workspace with what this launch leaves in it (a backward checks it)
+    if (blockIdx.x == 0 && threadIdx.x == 0) stamp_workspace(hdr, KEEP, B, T, C);
     if (y == nullptr || Lv == 0) {
         if (q == 0) put_flag(myflag, epoch, kInclusive);
         return;
@@ -460,12 +466,12 @@ static void launch_forward_io(int64_t units, hipStream_t stream, int64_t T, int6
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, true, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
-                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr);
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr, B);
     else
         hipLaunchKernelGGL((wkv_forward_kernel<kFwdWaves, kFwdChunk, false, F, KEEP>),
                            dim3((unsigned)units), dim3(kFwdWaves * 64), 0, stream, T, C, ngrp,
                            nbg, L.nseg, epoch, poll_limit(), w, u, kk, vv, rr, yy, L.flags, L.agg,
-                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr);
+                           L.incl, B * L.nseg * C, L.cin, sa, sb, sp, L.init, fin, L.hdr, B);
 }
 
 template <Io F>
