@@ -142,6 +142,92 @@ def summarize_counters(fetch_dir, write_dir):
     return out
 
 
+# the kernels the counter summary covers (rocprofv3 kernel names) and their algorithmic
+# bytes per element of their launch
+COUNTER_KERNELS = {
+    "forward": ("wkv_forward_kernel<2, 32, false, (wkvdev::Io)0, true>", 12),
+    "forward_infer": ("wkv_forward_kernel<2, 32, false, (wkvdev::Io)0, false>", 12),
+    "backward": ("wkv_backward_kernel<2, 32, false, (wkvdev::Io)0>", 20),
+    "forward_bf16": ("wkv_forward_kernel<2, 32, false, (wkvdev::Io)1, true>", 6),
+    "backward_bf16": ("wkv_backward_kernel<2, 32, false, (wkvdev::Io)1>", 10),
+    "decode": ("wkv_decode_kernel<(wkvdev::Io)0>", 36),
+    "decode_bf16": ("wkv_decode_kernel<(wkvdev::Io)1>", 30),
+    "token_shift": ("wkv_shift_kernel<4>", 16),
+    "token_shift_backward": ("wkv_shift_backward_kernel<1>", 20),
+}
+
+
+def summarize_counter_sets(folders):
+    """Median per dispatch of every counter found in the `rocprofv3 --pmc` output folders of
+    `bench.py --counter-run` runs, for the kernels in COUNTER_KERNELS; FETCH_SIZE and
+    WRITE_SIZE (KiB) are scaled by what they read for the run's 1 GiB device copy (the
+    runtime's copyBuffer kernel, which reads and writes exactly COPY_BYTES) and turned into
+    bytes per element of the kernel's workload."""
+    import wkv_inputs
+    rows = []
+    for folder in folders:
+        rows.extend(_read_counter_rows(folder))
+    counters = sorted({r["Counter_Name"] for r in rows})
+    per = {c: _per_dispatch(rows, c) for c in counters}
+    out = {"source_sha256": source_hash(), "counters": counters, "kernels": {}}
+    big = COPY_BYTES / 1024 / 4
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in per:
+            vals = [v for n, vs in per[c].items() if "copyBuffer" in n for v in vs if v > big]
+            if vals:
+                scale[c] = (COPY_BYTES / 1024) / statistics.median(vals)
+                out["copy_" + c.lower() + "_kib"] = statistics.median(vals)
+    out["scale"] = scale
+    l3b = wkv_inputs.WORKLOADS["l3b"]
+    n_l3b = l3b["B"] * l3b["T"] * l3b["C"]
+    n_dec = wkv_inputs.DECODE["B"] * wkv_inputs.DECODE["C"]
+    for op, (name, alg) in COUNTER_KERNELS.items():
+        n = n_dec if op.startswith("decode") else n_l3b
+        rec = {"kernel": name, "elements": n, "algorithmic_bytes_per_elem": alg}
+        for c in counters:
+            v = _match(per[c], name)
+            if v is not None:
+                rec[c] = v
+        if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec and len(scale) == 2:
+            rec["traffic_bytes"] = 1024 * (rec["FETCH_SIZE"] * scale["FETCH_SIZE"]
+                                           + rec["WRITE_SIZE"] * scale["WRITE_SIZE"])
+            rec["traffic_bytes_per_elem"] = rec["traffic_bytes"] / n
+        out["kernels"][op] = rec
+    return out
+
+
+def counter_run(wkv, torch, dev):
+    """Each kernel of COUNTER_KERNELS launched a few times on its benchmark workload (no
+    graphs, no timing), then the 1 GiB device copy whose byte counters scale the others'."""
+    import wkv_inputs
+    x = wkv_inputs.generate("l3b", with_dy=True)
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in x}
+    B, T, C = t["k"].shape
+    fws = wkv.forward_workspace(B, T, C, dev)
+    for dt in (torch.float32, torch.bfloat16):
+        k, v, dy = (t[n].to(dt) for n in ("k", "v", "dy"))
+        for _ in range(3):
+            wkv.forward(t["w"], t["u"], k, v, workspace=fws)
+            wkv.backward(t["w"], t["u"], k, v, dy, fwd_workspace=fws)
+            if dt == torch.float32:
+                wkv.forward_infer(t["w"], t["u"], k, v, workspace=fws)
+    cfg = wkv_inputs.DECODE
+    wd, ud = (torch.from_numpy(a).to(dev) for a in wkv_inputs.decode_layer_params(0))
+    st = [torch.from_numpy(a).to(dev) for a in wkv_inputs.empty_decode_state(cfg["B"], cfg["C"])]
+    for dt in (torch.float32, torch.bfloat16):
+        kd = torch.randn(cfg["B"], cfg["C"], device=dev).to(dt)
+        for _ in range(5):
+            wkv.decode_step(wd, ud, kd, kd, *st)
+    mu = torch.rand(3, C, device=dev)
+    for _ in range(3):
+        wkv.token_shift(t["k"], mu)
+        wkv.token_shift_backward(t["k"], mu, (t["v"], t["dy"], t["k"]))
+    torch.cuda.synchronize(dev)
+    bench_copy(torch, dev)
+    torch.cuda.synchronize(dev)
+
+
 def counter_traffic(op):
     """HBM bytes per launch of `op` from the committed counter summary, or None if absent or
     taken on different kernel sources."""
@@ -718,6 +804,11 @@ def main(argv=None):
     ap.add_argument("--with-copy", action="store_true",
                     help="(kept for old commands: the 1 GiB device copy is always timed)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--counter-run", action="store_true",
+                    help="launch each kernel of the counter summary a few times (for rocprofv3 "
+                         "--pmc passes) and exit")
+    ap.add_argument("--summarize-counter-sets", nargs="+", metavar="PMC_DIR",
+                    help="summarize the counters of --counter-run passes (JSON)")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the step's kernel durations from a rocprofv3 --kernel-trace "
                          "folder of a run with the same --warmup/--steps")
@@ -728,6 +819,9 @@ def main(argv=None):
         return
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return 0
+    if args.summarize_counter_sets:
+        print(json.dumps(summarize_counter_sets(args.summarize_counter_sets), indent=1))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -749,6 +843,10 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    if args.counter_run:
+        counter_run(wkv, torch, dev)
+        print(json.dumps({"counter_run": "done"}), flush=True)
+        return 0
     x = wkv_inputs.generate("l3b", with_dy=True)
     settle_clocks(torch, dev)
     r = bench_step(wkv, torch, dev, x, args.steps, args.warmup)

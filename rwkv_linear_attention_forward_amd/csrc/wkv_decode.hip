@@ -12,45 +12,81 @@
 
 namespace wkvdev {
 
-// k, v, y in storage format IO (widened on load, rounded on store); the state stays fp32.
+// Grid: x over 256-channel blocks, y over groups of kDecodeRows sequences (strided when there
+// are more groups than a grid's y extent). A lane owns one channel c and kDecodeRows
+// sequences b0 .. b0 + kDecodeRows - 1: the channel's constants (w, u and the decay factors
+// of the rescaled update) are formed once per lane, and the kDecodeRows elements' loads are
+// issued together, each coalesced over the wave's 64 channels. No division or remainder in
+// the index math. On the 256 x 5120 decode workload the grid is 20 x 64 workgroups of four
+// waves: 5,120 waves, all resident at once.
+#ifndef WKV_DECODE_ROWS
+#define WKV_DECODE_ROWS 4
+#endif
+constexpr int kDecodeRows = WKV_DECODE_ROWS;
+constexpr int64_t kDecodeMaxGroups = 65535;
+
+// One group of kDecodeRows sequences for the lane's channel c (vf, vio: its byte offsets
+// in fp32 and in format IO), rows b0 .. b0 + rows - 1.
 template <Io IO>
-__device__ __forceinline__ void decode_elem(int64_t i, int64_t C, const float *__restrict__ w,
-                                            const float *__restrict__ u,
-                                            const io_t<IO> *__restrict__ k,
-                                            const io_t<IO> *__restrict__ v,
-                                            float *__restrict__ a, float *__restrict__ b,
-                                            float *__restrict__ p, io_t<IO> *__restrict__ y) {
-    const int64_t c = i % C;
-    const float wc = w[c], uc = u[c];
-    Rs s{a[i], b[i], p[i]};
-    const float kk = io_ld<IO>(k, i), vv = io_ld<IO>(v, i);
-    io_st<IO>(y, i, rs_out(s, kk, vv, uc));
-    rs_push(s, kk, vv, make_decay(wc));
-    a[i] = s.a;
-    b[i] = s.b;
-    p[i] = s.p;
+__device__ __forceinline__ void decode_group(int64_t b0, int rows, int64_t C, int vf, int vio,
+                                             const float *__restrict__ w,
+                                             const float *__restrict__ u,
+                                             const io_t<IO> *__restrict__ k,
+                                             const io_t<IO> *__restrict__ v, float *__restrict__ a,
+                                             float *__restrict__ b, float *__restrict__ p,
+                                             io_t<IO> *__restrict__ y) {
+    // one buffer resource per tensor at the group's first row (scalar registers), the lane's
+    // channel as a 32-bit byte offset, the row as a scalar offset
+    const int64_t base = b0 * C;
+    const rsrc_t ra = make_rsrc(a + base), rb = make_rsrc(b + base), rp = make_rsrc(p + base);
+    const rsrc_t rk = make_rsrc(k + base), rv = make_rsrc(v + base), ry = make_rsrc(y + base);
+    Rs s[kDecodeRows];
+    float kk[kDecodeRows], vv[kDecodeRows];
+#pragma unroll
+    for (int r = 0; r < kDecodeRows; ++r) {
+        // rows past B re-read the group's first row and are never stored
+        const int rr = r < rows ? r : 0;
+        const int sf = (int)(rr * C * 4), sio = (int)(rr * C * kIoBytes<IO>);
+        s[r] = Rs{bload(ra, vf, sf), bload(rb, vf, sf), bload(rp, vf, sf)};
+        kk[r] = bload_io<IO>(rk, vio, sio);
+        vv[r] = bload_io<IO>(rv, vio, sio);
+    }
+    // the channel's constants, read after the rows' loads are issued, so that their round
+    // trip overlaps the rows' instead of preceding it (the empty statement keeps the
+    // compiler from moving memory accesses across it)
+    asm volatile("" ::: "memory");
+    const float uc = bload(make_rsrc(u), vf, 0);
+    const Decay dc = make_decay(bload(make_rsrc(w), vf, 0));
+    // every row is computed and stored, a row past B as a second copy of the group's first
+    // row (the same inputs, so the same values land on the same addresses); branch-free, so
+    // the compiler cannot sink any row's loads behind a condition
+#pragma unroll
+    for (int r = 0; r < kDecodeRows; ++r) {
+        const int rr = r < rows ? r : 0;
+        const int sf = (int)(rr * C * 4), sio = (int)(rr * C * kIoBytes<IO>);
+        bstore_io<IO>(ry, rs_out(s[r], kk[r], vv[r], uc), vio, sio);
+        rs_push(s[r], kk[r], vv[r], dc);
+        bstore(ra, s[r].a, vf, sf);
+        bstore(rb, s[r].b, vf, sf);
+        bstore(rp, s[r].p, vf, sf);
+    }
 }
 
-// Two elements per lane, 256 apart (both accesses coalesced; the two loads of each tensor are
-// in flight together). Past kDecodeMaxBlocks workgroups (2^29 elements) the grid is capped and
-// lanes loop (LOOP). Measured on the 256 x 5120 decode workload: 11.0 us per call, against
-// 11.2 with one element per lane and 11.5 with four per lane in 16-byte accesses.
-constexpr int kDecodeEpt = 2;
-constexpr int64_t kDecodeMaxBlocks = int64_t(1) << 20;
-
+// LOOP: more row groups than the grid's y extent, taken in strides of gridDim.y; otherwise
+// one group per workgroup row.
 template <bool LOOP, Io IO>
 __global__ __launch_bounds__(256) void wkv_decode_kernel(
-    int64_t n, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
+    int64_t B, int64_t C, int64_t ngroups, const float *__restrict__ w, const float *__restrict__ u,
     const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v, float *__restrict__ a,
     float *__restrict__ b, float *__restrict__ p, io_t<IO> *__restrict__ y) {
-    const int64_t span = (int64_t)256 * kDecodeEpt;
-    const int64_t step = LOOP ? (int64_t)gridDim.x * span : n;
-    for (int64_t i0 = (int64_t)blockIdx.x * span + threadIdx.x; i0 < n; i0 += step) {
-#pragma unroll
-        for (int e = 0; e < kDecodeEpt; ++e) {
-            const int64_t i = i0 + e * 256;
-            if (i < n) decode_elem<IO>(i, C, w, u, k, v, a, b, p, y);
-        }
+    const int c = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (c >= C) return;
+    const int vf = c * 4, vio = c * kIoBytes<IO>;
+    for (int64_t g = blockIdx.y; g < ngroups; g += gridDim.y) {
+        const int64_t b0 = g * kDecodeRows;
+        const int rows = (int)(B - b0 < kDecodeRows ? B - b0 : kDecodeRows);
+        decode_group<IO>(b0, rows, C, vf, vio, w, u, k, v, a, b, p, y);
+        if (!LOOP) break;
     }
 }
 
@@ -61,14 +97,15 @@ static hipError_t launch_decode_io(int64_t B, int64_t C, const float *w, const f
     using E = io_t<IO>;
     const E *kk = static_cast<const E *>(k), *vv = static_cast<const E *>(v);
     E *yy = static_cast<E *>(y);
-    const int64_t n = B * C;
-    const int64_t nblk = (n + 256 * kDecodeEpt - 1) / (256 * kDecodeEpt);
-    if (nblk <= kDecodeMaxBlocks)
-        hipLaunchKernelGGL((wkv_decode_kernel<false, IO>), dim3((unsigned)nblk), dim3(256), 0,
-                           stream, n, C, w, u, kk, vv, a, b, p, yy);
+    const int64_t ngroups = (B + kDecodeRows - 1) / kDecodeRows;
+    const dim3 grid((unsigned)((C + 255) / 256),
+                    (unsigned)(ngroups < kDecodeMaxGroups ? ngroups : kDecodeMaxGroups));
+    if (ngroups <= kDecodeMaxGroups)
+        hipLaunchKernelGGL((wkv_decode_kernel<false, IO>), grid, dim3(256), 0, stream, B, C,
+                           ngroups, w, u, kk, vv, a, b, p, yy);
     else
-        hipLaunchKernelGGL((wkv_decode_kernel<true, IO>), dim3((unsigned)kDecodeMaxBlocks),
-                           dim3(256), 0, stream, n, C, w, u, kk, vv, a, b, p, yy);
+        hipLaunchKernelGGL((wkv_decode_kernel<true, IO>), grid, dim3(256), 0, stream, B, C,
+                           ngroups, w, u, kk, vv, a, b, p, yy);
     return hipGetLastError();
 }
 

@@ -100,6 +100,10 @@ template <Io F> __device__ __forceinline__ io_t<F> io_narrow(float x) {
         const unsigned nan = (u >> 16) | 0x40u;
         return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
     } else {
+        // the fp32 value is materialized first, so that the rounding to 16 bits is always of
+        // the fp32 result (the compiler would otherwise fold a final product into a
+        // mixed-precision multiply-add that rounds once, straight to 16 bits)
+        asm volatile("" : "+v"(x));
         return __builtin_bit_cast(uint16_t, (_Float16)x);
     }
 }
@@ -214,6 +218,8 @@ struct Rs {
 
 // Output for token (k, v) from the state before it:
 //   y = (e^p a + e^{u+k} v) / (e^p b + e^{u+k}), evaluated with the larger exponent as 0.
+// The quotient is taken as a product with the hardware reciprocal (about 1 ulp; the
+// denominator is at least 1 whenever the state holds any mass, and e2 = 1 otherwise).
 __device__ __forceinline__ float rs_out(const Rs &s, float k, float v, float u) {
     const float uk = u + k;
     const float d = s.p - uk;
@@ -221,7 +227,7 @@ __device__ __forceinline__ float rs_out(const Rs &s, float k, float v, float u) 
     const bool sp = d >= 0.0f;
     const float e1 = sp ? 1.0f : e;
     const float e2 = sp ? e : 1.0f;
-    return fmaf(e1, s.a, e2 * v) / fmaf(e1, s.b, e2);
+    return fmaf(e1, s.a, e2 * v) * rcpf(fmaf(e1, s.b, e2));
 }
 
 // Per-channel decay constants for rs_push.
