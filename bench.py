@@ -150,8 +150,8 @@ COUNTER_KERNELS = {
     "backward": ("wkv_backward_kernel<2, 32, false, (wkvdev::Io)0>", 20),
     "forward_bf16": ("wkv_forward_kernel<2, 32, false, (wkvdev::Io)1, true>", 6),
     "backward_bf16": ("wkv_backward_kernel<2, 32, false, (wkvdev::Io)1>", 10),
-    "decode": ("wkv_decode_kernel<(wkvdev::Io)0>", 36),
-    "decode_bf16": ("wkv_decode_kernel<(wkvdev::Io)1>", 30),
+    "decode": ("wkv_decode_kernel<false, (wkvdev::Io)0>", 36),
+    "decode_bf16": ("wkv_decode_kernel<false, (wkvdev::Io)1>", 30),
     "token_shift": ("wkv_shift_kernel<4>", 16),
     "token_shift_backward": ("wkv_shift_backward_kernel<1>", 20),
 }
@@ -182,6 +182,15 @@ def summarize_counter_sets(folders):
     l3b = wkv_inputs.WORKLOADS["l3b"]
     n_l3b = l3b["B"] * l3b["T"] * l3b["C"]
     n_dec = wkv_inputs.DECODE["B"] * wkv_inputs.DECODE["C"]
+    # GRBM_GUI_ACTIVE (busy cycles, summed over the 8 XCDs) over the dispatch's duration is the
+    # clock the kernel ran at; only dispatches of 50 us or more, where the counter's window
+    # is the kernel's own
+    gui = {}
+    for r in rows:
+        if r.get("Counter_Name") == "GRBM_GUI_ACTIVE" and r.get("End_Timestamp"):
+            ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            if ns >= 50000:
+                gui.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) / 8 / ns)
     for op, (name, alg) in COUNTER_KERNELS.items():
         n = n_dec if op.startswith("decode") else n_l3b
         rec = {"kernel": name, "elements": n, "algorithmic_bytes_per_elem": alg}
@@ -189,6 +198,9 @@ def summarize_counter_sets(folders):
             v = _match(per[c], name)
             if v is not None:
                 rec[c] = v
+        ghz = [x for nm, xs in gui.items() if name in nm for x in xs]
+        if ghz:
+            rec["clock_ghz"] = statistics.median(ghz)
         if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec and len(scale) == 2:
             rec["traffic_bytes"] = 1024 * (rec["FETCH_SIZE"] * scale["FETCH_SIZE"]
                                            + rec["WRITE_SIZE"] * scale["WRITE_SIZE"])

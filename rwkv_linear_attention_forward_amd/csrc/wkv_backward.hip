@@ -267,7 +267,7 @@ __device__ __forceinline__ RevCarry chunk_pass(
     }
     const Carry fin = chunk_carry(F, bidx, ci, C, cl);
     const double gap = fin.P - ref2;
-    fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
+    fx = K.slow_wave || wave_any(gap > (double)kCarryGap || chunk_has_faint_key<CH>(kc, Lv, ref));
     double R = 0.0, Q = 0.0;
     if (!fx) {
         if constexpr (GATE) lds_load_fence();
@@ -357,14 +357,19 @@ __device__ __noinline__ RevCarry helper_summary(
     const io_t<IO> *kp = k + (row0 + t0) * C + cl;
     const io_t<IO> *vp = v + (row0 + t0) * C + cl;
     const io_t<IO> *gp = dy + (row0 + t0) * C + cl;
-    float ref = kNegBig;
+    float ref = kNegBig, kmin = __builtin_inff();
 #pragma unroll 1
-    for (int j = 0; j < Lv; ++j) ref = fmaxf(ref, io_ld<IO>(kp, (int64_t)j * C));
+    for (int j = 0; j < Lv; ++j) {
+        const float kj = io_ld<IO>(kp, (int64_t)j * C);
+        ref = fmaxf(ref, kj);
+        kmin = fminf(kmin, kj);
+    }
     const double refd = (double)ref;
     const double ref2 = refd * kLog2eD;
     const Carry fin = chunk_carry(F, bidx, ci, C, cl);
     const double gap = fin.P - ref2;
-    bool fx = K.slow_wave || wave_any(gap > (double)kCarryGap);
+    // the owner's tests, in the same order: carry gap, faint key (chunk_has_faint_key)
+    bool fx = K.slow_wave || wave_any(gap > (double)kCarryGap || ref - kmin > kFaintGap);
     if (!fx) {
         const double s0 = exp2_64(gap);
         double Sx = fin.a * s0, Zx = fin.b * s0;

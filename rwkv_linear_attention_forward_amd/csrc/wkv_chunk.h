@@ -206,6 +206,19 @@ __device__ __forceinline__ float chunk_ref(const float (&kc)[CH], int Lv) {
     return ref;
 }
 
+// True when some valid key of the chunk lies more than 87 below the chunk's largest (ref):
+// its in-frame weight e^{k - ref} is then below the fp32 normal range and would carry only a
+// few significant bits in the fp32 sweeps, which matters where a large bonus e^u lifts it
+// into the denominator. Such chunks take the per-token path (the test is per chunk, ahead of
+// the sweeps, so it costs the unrolled loops nothing).
+template <int CH>
+__device__ __forceinline__ bool chunk_has_faint_key(const float (&kc)[CH], int Lv, float ref) {
+    float kmin = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < CH; ++j) kmin = j < Lv ? fminf(kmin, kc[j]) : kmin;
+    return ref - kmin > kFaintGap;
+}
+
 // ---- publication records (device-scope, see wkv_launch.h for the layout) ----
 // Everything one workgroup publishes for another (records, flags, partials) is written
 // and read only with device-scope atomic loads and stores (sc1: coherent across the XCDs'

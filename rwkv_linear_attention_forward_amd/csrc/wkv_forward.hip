@@ -277,6 +277,8 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     float kc[CH], vc[CH];
     load_chunk<CH, F>(kc, vc, k, v, row0, t0, T, C, voff);
     const float ref = chunk_ref<CH>(kc, Lv);
+    // for the outputs (phase 3); wave-uniform, so it holds no vector register meanwhile
+    const bool faint = wave_any(chunk_has_faint_key<CH>(kc, Lv, ref));
     Carry sum;
     bool exact = chunk_summary<CH, false>(kc, vc, Lv, ref, slow_wave, dwfd, sum);
     if (exact) sum = exact_summary<CH, F>(k, v, row0, t0, Lv, C, cl, ref, wd);
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void wkv_forward_kernel(
     }
     if (!exact) {
         const double gap = mine.P - ref2;
-        bool bad = gap > (double)kCarryGap;
+        bool bad = gap > (double)kCarryGap || faint;
         float dmin = __builtin_inff();
         const double s0 = exp2_64(gap);
         float Sx = (float)(mine.a * s0), Zx = (float)(mine.b * s0);

@@ -116,6 +116,21 @@ def test_large_bonus_with_a_vanishing_first_key(wkv, dev):
     _check(got, ref, "vanishing first key")
 
 
+def test_large_bonus_on_a_whole_wave_with_a_vanishing_first_key(wkv, dev):
+    # As above, with every lane of the wave at u >= 30 (no lane forces the per-token path for
+    # the wave): the first key's in-frame weight is an fp32 subnormal while e^u times it is
+    # not negligible, so the chunk must go per token for dk, dv (and y) to keep full precision
+    B, T, C = 2, 96, 64
+    x = wkv_inputs.generate("l3b", seed=31, B=B, T=T, C=C)
+    x["k"][:, 0, :] = np.float32(-95.0)
+    x["u"] = np.linspace(30, 45, C).astype(np.float32)
+    got = _gpu_backward(wkv, dev, x)
+    for g in got:
+        assert np.all(np.isfinite(g))
+    ref = oracle.backward_direct(x["w"], x["u"], x["k"], x["v"], x["dy"])
+    _check(got, ref, "vanishing first key, whole wave")
+
+
 def test_autograd_wrapper(wkv, dev):
     import torch
     x = wkv_inputs.generate("small", B=2, T=300, C=72)
