@@ -1,13 +1,13 @@
 """Throughput of the WKV operator (RWKV-4 time mixing) on one MI355X.
 
 A step is one forward and one backward pass over one batch of the 3B-class layer shape
-(B=8, T=4096, C=2560, fp32): wkv_forward fills y and its workspace, wkv_backward reads
-that workspace and writes dk, dv, dw, du. Inputs are synthetic and seeded (the
+(B=8, T=4096, C=2560, fp32): wkv_forward_train fills y and its workspace,
+wkv_backward_train reads that workspace and writes dk, dv, dw, du. Inputs are synthetic and seeded (the
 distributions of the 3B-class layer workload in wkv_inputs.py) and resident in HBM
 before timing starts; the step reuses preallocated outputs and workspaces.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-state]
-                    [--no-gated] [--no-bf16] [--no-shift]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--no-cpu] [--no-decode]
+                    [--no-state] [--no-gated] [--no-bf16] [--no-shift] [--no-configs]
 
 prints one JSON line. `value` is B*T*C / step time (elements per second of fwd+bwd);
 `roofline` describes the kernel that takes most of the step, with its algorithmic bytes
@@ -25,19 +25,24 @@ from a given state that also returns the final state (prompt prefill), on the sa
 the step with the [B, T, C] tensors stored as bfloat16 (reported apart: the benchmark's own
 workload is fp32); `token_shift` the mix that produces the projections' inputs.
 
-The default warm-up (200 steps, about 0.12 s) runs the step long enough under sustained
-load for the GPU's clocks to settle: over the first ~100 back-to-back steps after idle the
-kernels run up to a third slower before they reach a steady rate, and the default timed
-steps (100) are taken there.
+Before the W warm-up steps, `--settle` untimed steps (400 by default, about 0.25 s) run the
+step itself under sustained load: from idle the GPU first runs the step's kernels at full
+clock, then, a few steps in, drops its clock for some tens of steps (the kernels then run up
+to a fifth slower) before it settles at its sustained rate; the settle steps take that
+excursion whatever W is, and the K timed steps are taken at the sustained rate.
 
-Helpers for the counter summaries:
-    python bench.py --with-copy ...        also runs a 1 GiB device copy (known bytes)
+Helpers for the profiles:
+    python bench.py --counter-run
+        launches each kernel of the counter summary a few times on its workload, with a
+        1 GiB device copy (known bytes) beside them, for `rocprofv3 --pmc` passes.
+    python bench.py --summarize-counter-sets PMC_DIR [PMC_DIR ...]
+        reads the `rocprofv3 --pmc` output folders of --counter-run passes and prints the
+        summary JSON (per-dispatch counters, bytes scaled by the copy's, clock).
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
-        reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` output folders of a
-        `--with-copy` run and prints the summary JSON (per-dispatch KiB, copy scaling).
-    python bench.py --summarize-trace TRACE_DIR [--warmup W --steps K]
+        the same for two folders holding FETCH_SIZE and WRITE_SIZE only.
+    python bench.py --summarize-trace TRACE_DIR [--settle S --warmup W --steps K]
         prints the step's kernel durations from a `rocprofv3 --kernel-trace` folder of a run
-        with the same W and K (all dispatches, and the timed ones alone).
+        with the same S, W and K (all dispatches, and the timed ones alone).
 """
 from __future__ import annotations
 
@@ -153,7 +158,7 @@ COUNTER_KERNELS = {
     "decode": ("wkv_decode_kernel<false, (wkvdev::Io)0>", 36),
     "decode_bf16": ("wkv_decode_kernel<false, (wkvdev::Io)1>", 30),
     "token_shift": ("wkv_shift_kernel<4>", 16),
-    "token_shift_backward": ("wkv_shift_backward_kernel<1>", 20),
+    "token_shift_backward": ("wkv_shift_backward_kernel", 20),
 }
 
 
@@ -254,11 +259,11 @@ def counter_traffic(op):
     return None if k is None else k["traffic_bytes"]
 
 
-def summarize_trace(folder, warmup, steps):
+def summarize_trace(folder, settle, warmup, steps):
     """Markdown table of the step's kernel durations from a `rocprofv3 --kernel-trace` folder
-    of a bench.py run with the same --warmup and --steps: every dispatch of each kernel, and
-    the timed ones alone (the step runs first, so they are dispatches warmup .. warmup+steps-1
-    of each of its kernels, in launch order)."""
+    of a bench.py run with the same --settle, --warmup and --steps: every dispatch of each
+    kernel, and the timed ones alone (the step runs first, so they are dispatches
+    settle+warmup .. settle+warmup+steps-1 of each of its kernels, in launch order)."""
     rows = []
     for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
         with open(path, newline="") as f:
@@ -279,7 +284,7 @@ def summarize_trace(folder, warmup, steps):
         if not d:
             continue
         us = [(e - s0) / 1e3 for s0, e in d]
-        tw = us[warmup:warmup + steps]
+        tw = us[settle + warmup:settle + warmup + steps]
         if op != "forward":
             timed_sum += statistics.mean(tw)
         gbs = ("%.0f" % (BYTES_PER_ELEM[op] * n / (statistics.mean(tw) * 1e-6) / 1e9)
@@ -317,7 +322,7 @@ def cpu_baseline(x, budget_s=10.0, max_runs=3):
 # ---------------------------------------------------------------------------------------
 # GPU measurement
 # ---------------------------------------------------------------------------------------
-def bench_step(wkv, torch, dev, x, steps, warmup):
+def bench_step(wkv, torch, dev, x, steps, warmup, settle=0):
     t = {n: torch.from_numpy(x[n]).to(dev) for n in ("w", "u", "k", "v", "dy")}
     B, T, C = t["k"].shape
     fws = wkv.forward_workspace(B, T, C, dev)
@@ -338,6 +343,11 @@ def bench_step(wkv, torch, dev, x, steps, warmup):
         if ev is not None:
             ev[2].record()
 
+    t_settle = time.perf_counter()
+    for _ in range(settle):
+        step()
+    torch.cuda.synchronize(dev)
+    t_settle = time.perf_counter() - t_settle
     for _ in range(warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -352,7 +362,7 @@ def bench_step(wkv, torch, dev, x, steps, warmup):
     span_ms = evs[0][0].elapsed_time(evs[-1][2])
     ok = all(bool(torch.isfinite(a).all()) for a in (y,) + outs)
     return {"B": B, "T": T, "C": C, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "span_ms": span_ms,
-            "wall_s": wall, "finite": ok}
+            "wall_s": wall, "finite": ok, "settle_s": t_settle}
 
 
 def bench_copy(torch, dev, reps=3):
@@ -613,19 +623,6 @@ def bench_shift(wkv, torch, dev, steps=100, warmup=50):
 FLUSH_BYTES = 1 << 30  # written between timed iterations of the small workloads (> MALL)
 
 
-def settle_clocks(torch, dev, seconds=1.0):
-    """Sustained device copies for `seconds` before anything is timed: from idle, the GPU's
-    clocks take a few hundred milliseconds of back-to-back work to reach their steady
-    rate (the first steps otherwise run up to a third slower)."""
-    a = torch.empty(1 << 28, device=dev)
-    b = torch.empty_like(a)
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(8):
-            b.copy_(a)
-        torch.cuda.synchronize(dev)
-
-
 def _oracle_time(fn, min_s=0.3, max_runs=20):
     """Median seconds of fn() over repeated runs (at least one, until min_s has passed)."""
     times = []
@@ -802,6 +799,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle", type=int, default=400,
+                    help="untimed steps before the warm-up, run so that the GPU reaches its "
+                         "sustained clock whatever --warmup is")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-state", action="store_true",
@@ -827,7 +827,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
+        print(summarize_trace(args.summarize_trace, args.settle, args.warmup, args.steps))
         return
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
@@ -841,8 +841,8 @@ def main(argv=None):
               "(--gpus %d, WORLD_SIZE %d requested); run with --gpus 1" % (args.gpus, world),
               file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.settle < 0:
+        print("--steps must be >= 1, --warmup and --settle >= 0", file=sys.stderr)
         return 2
 
     sys.path.insert(0, HERE)
@@ -860,8 +860,7 @@ def main(argv=None):
         print(json.dumps({"counter_run": "done"}), flush=True)
         return 0
     x = wkv_inputs.generate("l3b", with_dy=True)
-    settle_clocks(torch, dev)
-    r = bench_step(wkv, torch, dev, x, args.steps, args.warmup)
+    r = bench_step(wkv, torch, dev, x, args.steps, args.warmup, args.settle)
     B, T, C = r["B"], r["T"], r["C"]
     n = B * T * C
     ms_per_step = r["span_ms"] / args.steps
@@ -873,7 +872,8 @@ def main(argv=None):
     achieved = alg / (dur_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": n / (ms_per_step * 1e-3), "unit": "elem/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": args.settle,
+        "settle_s": r["settle_s"], "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "3B-class layer WKV forward+backward", "B": B, "T": T, "C": C,

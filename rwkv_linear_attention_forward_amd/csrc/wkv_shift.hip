@@ -10,8 +10,8 @@
 // Elementwise and HBM-bound: x is read once and the three mixes written (16 B per element;
 // the backward reads the three cotangents and x and writes dx, 20 B). One lane per channel
 // (or per 4 channels, with 16-byte accesses) and one wave per kShiftTokens tokens of one
-// sequence, walking the tokens in order with the previous token carried in registers, so
-// x[t-1] is never read twice.
+// sequence: the wave's loads are issued together, then the tokens are walked in order with
+// the previous token carried in registers, so x[t-1] is never read twice.
 #include <initializer_list>
 
 #include "wkv_device.h"
@@ -75,25 +75,33 @@ __global__ __launch_bounds__(256) void wkv_shift_kernel(
 #pragma unroll
         for (int i = 0; i < VEC; ++i) set_lane<VEC>(prev, i, 0.0f);
     }
-#pragma unroll 4
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t i0 = (b * T + t) * C + cl;
-        const V xt = vload<VEC>(x + i0);
-        V a, bk, cv;
+    // the wave's tokens loaded together (a token past t1 repeats the last), then walked
+    const int n = (int)(t1 - t0);
+    V xs[kShiftTokens];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const float xi = lane_of<VEC>(xt, i), pi = lane_of<VEC>(prev, i);
-            const float r = lane_of<VEC>(mr, i), k = lane_of<VEC>(mk, i), v = lane_of<VEC>(mv, i);
-            set_lane<VEC>(a, i, fmaf(r, xi, (1.0f - r) * pi));
-            set_lane<VEC>(bk, i, fmaf(k, xi, (1.0f - k) * pi));
-            set_lane<VEC>(cv, i, fmaf(v, xi, (1.0f - v) * pi));
+    for (int j = 0; j < kShiftTokens; ++j)
+        xs[j] = vload<VEC>(x + (b * T + t0 + (j < n ? j : n - 1)) * C + cl);
+#pragma unroll
+    for (int j = 0; j < kShiftTokens; ++j) {
+        if (j < n) {
+            const int64_t i0 = (b * T + t0 + j) * C + cl;
+            const V xt = xs[j];
+            V a, bk, cv;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const float xi = lane_of<VEC>(xt, i), pi = lane_of<VEC>(prev, i);
+                const float r = lane_of<VEC>(mr, i), k = lane_of<VEC>(mk, i), v = lane_of<VEC>(mv, i);
+                set_lane<VEC>(a, i, fmaf(r, xi, (1.0f - r) * pi));
+                set_lane<VEC>(bk, i, fmaf(k, xi, (1.0f - k) * pi));
+                set_lane<VEC>(cv, i, fmaf(v, xi, (1.0f - v) * pi));
+            }
+            if (cval) {
+                vstore<VEC>(o_r + i0, a);
+                vstore<VEC>(o_k + i0, bk);
+                vstore<VEC>(o_v + i0, cv);
+            }
+            prev = xt;
         }
-        if (cval) {
-            vstore<VEC>(o_r + i0, a);
-            vstore<VEC>(o_k + i0, bk);
-            vstore<VEC>(o_v + i0, cv);
-        }
-        prev = xt;
     }
     if (x_last != nullptr && t1 == T && cval) vstore<VEC>(x_last + b * C + c, prev);
 }
@@ -102,89 +110,83 @@ __global__ __launch_bounds__(256) void wkv_shift_kernel(
 //   dx[t]    = sum_m mu_m d_m[t] + sum_m (1 - mu_m) d_m[t+1]   (the second sum is 0 at T-1)
 //   dx_prev  = sum_m (1 - mu_m) d_m[0]
 //   dmu_m    = sum_{b,t} (x[t] - x[t-1]) d_m[t]   (fp64; a partial per wave, then summed)
-template <int VEC>
+// One lane per channel; the wave's tokens in batches of kShiftBatch, the last batch first,
+// each batch's loads (three cotangents and x[t-1] per token) issued together before the
+// batch is walked, so that a wave keeps 32 loads in flight (a batch of 8 measured
+// 321 us on the 3B-class shape, 16 tokens 329, the whole 32 at once 375, one token at a
+// time with the loop unrolled twice 366).
+constexpr int kShiftBatch = 8;
+
 __global__ __launch_bounds__(256) void wkv_shift_backward_kernel(
     int64_t T, int64_t C, int ngrp, int64_t nchunk, int64_t nwaves,
     const float *__restrict__ x, const float *__restrict__ x_prev,
     const float *__restrict__ mu, const float *__restrict__ d_r,
     const float *__restrict__ d_k, const float *__restrict__ d_v, float *__restrict__ dx,
     float *__restrict__ dx_prev, double *__restrict__ part) {
-    using V = typename VecT<VEC>::T;
     const int lane = threadIdx.x & 63;
     const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wv >= nwaves) return;
     const int64_t g = wv % ngrp, rest = wv / ngrp;
     const int64_t chunk = rest % nchunk, b = rest / nchunk;
-    const int64_t c = (g * 64 + lane) * VEC;
+    const int64_t c = g * 64 + lane;
     const bool cval = c < C;
-    const int64_t cl = cval ? c : C - VEC;
+    const int64_t cl = cval ? c : C - 1;
+    const int voff = (int)(cl * 4);
+    const int stride = (int)(C * 4);
     const int64_t t0 = chunk * kShiftTokens;
     const int64_t t1 = t0 + kShiftTokens < T ? t0 + kShiftTokens : T;
-    const V mr = vload<VEC>(mu + cl), mk = vload<VEC>(mu + C + cl), mv = vload<VEC>(mu + 2 * C + cl);
-    float next[VEC];  // sum_m (1 - mu_m) d_m[t+1]
-    float xt[VEC];
-    double sr[VEC], sk[VEC], sv[VEC];
-    {
-        V nr, nk, nv;
-        if (t1 < T) {
-            const int64_t i0 = (b * T + t1) * C + cl;
-            nr = vload<VEC>(d_r + i0);
-            nk = vload<VEC>(d_k + i0);
-            nv = vload<VEC>(d_v + i0);
-        }
-        const V x1 = vload<VEC>(x + (b * T + t1 - 1) * C + cl);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            next[i] = t1 < T ? fmaf(1.0f - lane_of<VEC>(mr, i), lane_of<VEC>(nr, i),
-                                    fmaf(1.0f - lane_of<VEC>(mk, i), lane_of<VEC>(nk, i),
-                                         (1.0f - lane_of<VEC>(mv, i)) * lane_of<VEC>(nv, i)))
-                             : 0.0f;
-            xt[i] = lane_of<VEC>(x1, i);
-            sr[i] = sk[i] = sv[i] = 0.0;
-        }
+    const float mr = mu[cl], mk = mu[C + cl], mv = mu[2 * C + cl];
+    const float nr = 1.0f - mr, nk = 1.0f - mk, nv = 1.0f - mv;
+    float next = 0.0f;  // sum_m (1 - mu_m) d_m[t+1]
+    if (t1 < T) {
+        const int64_t i0 = (b * T + t1) * C + cl;
+        next = fmaf(nr, d_r[i0], fmaf(nk, d_k[i0], nv * d_v[i0]));
     }
-#pragma unroll 2
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-        const int64_t i0 = (b * T + t) * C + cl;
-        V xp;
-        if (t > 0) {
-            xp = vload<VEC>(x + i0 - C);
-        } else if (x_prev != nullptr) {
-            xp = vload<VEC>(x_prev + b * C + cl);
-        } else {
+    float xt = x[(b * T + t1 - 1) * C + cl];
+    // x[-1] of the sequence: the previous call's last token, or 0
+    const float xfirst = (t0 == 0 && x_prev != nullptr) ? x_prev[b * C + cl] : 0.0f;
+    double sr = 0.0, sk = 0.0, sv = 0.0;
+    for (int64_t hi = t1; hi > t0; hi -= kShiftBatch) {
+        const int n = (int)(hi - t0 < kShiftBatch ? hi - t0 : kShiftBatch);  // wave-uniform
+        const int64_t tb = hi - n;                                            // first token
+        const int64_t row = (b * T + tb) * C;
+        const rsrc_t rr = make_rsrc(d_r + row), rk = make_rsrc(d_k + row),
+                     rv = make_rsrc(d_v + row), rd = make_rsrc(dx + row);
+        // x[t-1] for t = tb + i: row tb - 1 + i; at tb == 0 the token t = 0 reads row 0 and
+        // takes xfirst instead
+        const rsrc_t rx = make_rsrc(x + (tb > 0 ? row - C : row));
+        float ga[kShiftBatch], gb[kShiftBatch], gc[kShiftBatch], xp[kShiftBatch];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) set_lane<VEC>(xp, i, 0.0f);
+        for (int j = 0; j < kShiftBatch; ++j) {
+            const int i = j < n ? n - 1 - j : 0;  // token tb + i, the last of the batch first
+            const int ix = tb > 0 ? i : (i > 0 ? i - 1 : 0);
+            ga[j] = bload(rr, voff, i * stride);
+            gb[j] = bload(rk, voff, i * stride);
+            gc[j] = bload(rv, voff, i * stride);
+            xp[j] = bload(rx, voff, ix * stride);
         }
-        const V gr = vload<VEC>(d_r + i0), gk = vload<VEC>(d_k + i0), gv = vload<VEC>(d_v + i0);
-        V o;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const float r = lane_of<VEC>(mr, i), k = lane_of<VEC>(mk, i), v = lane_of<VEC>(mv, i);
-            const float a = lane_of<VEC>(gr, i), bb = lane_of<VEC>(gk, i), cc = lane_of<VEC>(gv, i);
-            set_lane<VEC>(o, i, fmaf(r, a, fmaf(k, bb, fmaf(v, cc, next[i]))));
-            const double diff = (double)xt[i] - (double)lane_of<VEC>(xp, i);
-            sr[i] = fma(diff, (double)a, sr[i]);
-            sk[i] = fma(diff, (double)bb, sk[i]);
-            sv[i] = fma(diff, (double)cc, sv[i]);
-            next[i] = fmaf(1.0f - r, a, fmaf(1.0f - k, bb, (1.0f - v) * cc));
-            xt[i] = lane_of<VEC>(xp, i);
+        for (int j = 0; j < kShiftBatch; ++j) {
+            if (j < n) {
+                const int i = n - 1 - j;
+                const float xpj = (tb == 0 && i == 0) ? xfirst : xp[j];
+                const float o = fmaf(mr, ga[j], fmaf(mk, gb[j], fmaf(mv, gc[j], next)));
+                const double diff = (double)xt - (double)xpj;
+                sr = fma(diff, (double)ga[j], sr);
+                sk = fma(diff, (double)gb[j], sk);
+                sv = fma(diff, (double)gc[j], sv);
+                next = fmaf(nr, ga[j], fmaf(nk, gb[j], nv * gc[j]));
+                xt = xpj;
+                if (cval) bstore(rd, o, voff, i * stride);
+            }
         }
-        if (cval) vstore<VEC>(dx + i0, o);
     }
     if (cval) {
-        if (t0 == 0 && dx_prev != nullptr) {
-            V o;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) set_lane<VEC>(o, i, next[i]);
-            vstore<VEC>(dx_prev + b * C + c, o);
-        }
+        if (t0 == 0 && dx_prev != nullptr) dx_prev[b * C + c] = next;
         const int64_t npart = nwaves / ngrp, pr = b * nchunk + chunk;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            part[pr * C + c + i] = sr[i];
-            part[(npart + pr) * C + c + i] = sk[i];
-            part[(2 * npart + pr) * C + c + i] = sv[i];
-        }
+        part[pr * C + c] = sr;
+        part[(npart + pr) * C + c] = sk;
+        part[(2 * npart + pr) * C + c] = sv;
     }
 }
 
@@ -246,11 +248,11 @@ hipError_t launch_shift_backward(int64_t B, int64_t T, int64_t C, const float *x
                                  const float *x_prev, const float *mu, const float *d_r,
                                  const float *d_k, const float *d_v, float *dx, float *dx_prev,
                                  float *dmu, double *part, hipStream_t stream) {
-    // one channel per lane: 4 per lane with 16-byte accesses measured slower here (410 us
-    // against 395 on the 3B-class shape), unlike the forward
+    // one channel per lane: 4 per lane with 16-byte accesses measured slower here, unlike
+    // the forward
     const int ngrp = (int)((C + 63) / 64);
     const int64_t nchunk = shift_chunks(T), nwaves = B * nchunk * ngrp;
-    hipLaunchKernelGGL(wkv_shift_backward_kernel<1>, dim3((unsigned)((nwaves + 3) / 4)),
+    hipLaunchKernelGGL(wkv_shift_backward_kernel, dim3((unsigned)((nwaves + 3) / 4)),
                        dim3(256), 0, stream, T, C, ngrp, nchunk, nwaves, x, x_prev, mu, d_r, d_k,
                        d_v, dx, dx_prev, part);
     hipError_t e = hipGetLastError();
