@@ -713,6 +713,44 @@ def bench_workload(wkv, torch, dev, name, with_bwd, reps, warmup, flush, cpu=Tru
     return r
 
 
+def bench_t_scaling(wkv, torch, dev, Ts=(512, 1024, 2048, 4096, 8192), B=8, C=2560, reps=20):
+    """The plain forward (wkv_forward) at B=8, C=2560 over T = 512 .. 8192: the parallel form's
+    cost is linear in the sequence length, so elements per second should hold roughly flat
+    while T grows 16-fold. Inputs drawn on the device (k, v ~ N(0,1); w = exp(U(-8,2));
+    u ~ U(-1,1), the 3B-class layer's distributions), each iteration preceded (outside the
+    timed events) by a 1 GiB write that evicts the Infinity Cache; median over `reps`."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4096)
+    w = torch.exp(torch.empty(C, device=dev).uniform_(-8.0, 2.0, generator=gen))
+    u = torch.empty(C, device=dev).uniform_(-1.0, 1.0, generator=gen)
+    scrub = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    rows = []
+    for T in Ts:
+        k = torch.randn(B, T, C, device=dev, generator=gen)
+        v = torch.randn(B, T, C, device=dev, generator=gen)
+        y = torch.empty_like(k)
+        for _ in range(3):
+            wkv.forward(w, u, k, v, out=y)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            scrub.zero_()
+            e0.record()
+            wkv.forward(w, u, k, v, out=y)
+            e1.record()
+        torch.cuda.synchronize(dev)
+        us = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+        n = B * T * C
+        rows.append({"T": T, "forward_us": us, "elem_per_s": n / (us * 1e-6),
+                     "frac_of_peak": 12 * n / (us * 1e-6) / 1e9 / PEAK_GBPS,
+                     "outputs_finite": bool(torch.isfinite(y).all())})
+        del k, v, y
+    rates = [r["elem_per_s"] for r in rows]
+    return {"workload": "wkv_forward, B=%d C=%d, T from %d to %d" % (B, C, Ts[0], Ts[-1]),
+            "points": rows, "max_over_min_elem_per_s": max(rates) / min(rates),
+            "timing": "HIP events on the library's stream, median of %d iterations" % reps}
+
+
 def bench_decode_horizon(wkv, torch, dev, steps=1000):
     """The batched decode workload over its whole horizon: each step draws the 40 layers'
     k, v on the device (outside the timing) and replays the step's 40 calls from a captured
@@ -812,7 +850,7 @@ def main(argv=None):
     ap.add_argument("--no-shift", action="store_true", help="skip the token-shift measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other synthetic workloads (small, 169M-class, long context, "
-                         "the decode horizon)")
+                         "the decode horizon, the forward over T = 512 .. 8192)")
     ap.add_argument("--with-copy", action="store_true",
                     help="(kept for old commands: the 1 GiB device copy is always timed)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -898,6 +936,7 @@ def main(argv=None):
             "longctx": bench_workload(wkv, torch, dev, "longctx", True, 30, 10, True, cpu),
         }
         out["configs"]["decode_horizon"] = bench_decode_horizon(wkv, torch, dev)
+        out["configs"]["forward_t_scaling"] = bench_t_scaling(wkv, torch, dev)
         if cpu:
             out["configs"]["decode_horizon"]["cpu_baseline"] = decode_cpu_baseline()
     if not args.no_decode:
