@@ -300,6 +300,18 @@ def summarize_trace(folder, settle, warmup, steps):
 # ---------------------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the same workload
 # ---------------------------------------------------------------------------------------
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, budget_s=10.0, max_runs=3):
     import oracle
     B, T, C = x["k"].shape
@@ -314,7 +326,7 @@ def cpu_baseline(x, budget_s=10.0, max_runs=3):
             break
     t = statistics.median(times)
     return {"value": B * T * C / t, "unit": "elem/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "full workload B=%d T=%d C=%d, fp64 plain recurrence forward + linear-time "
                       "backward (OpenMP over b, c), median of %d runs" % (B, T, C, len(times))}
 
@@ -707,6 +719,7 @@ def bench_workload(wkv, torch, dev, name, with_bwd, reps, warmup, flush, cpu=Tru
         sec, runs = _oracle_time(run)
         r["cpu_baseline"] = {
             "value": n / sec, "unit": "elem/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "full workload, fp64 plain recurrence forward%s (OpenMP over b, c), median "
                       "of %d runs" % (" + linear-time backward" if with_bwd else "", runs)}
         r["speedup_vs_cpu"] = r["elem_per_s"] / r["cpu_baseline"]["value"]
@@ -827,7 +840,8 @@ def decode_cpu_baseline(steps=20):
             total += time.perf_counter() - t0
     per_step = total / steps
     return {"value": B * C * L / per_step, "unit": "elem/s (B*C per layer-call)",
-            "cores": oracle.num_threads(), "kind": "oracle", "step_ms": per_step * 1e3,
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+            "step_ms": per_step * 1e3,
             "sample": "40 layers x %d steps of the 256 x 5120 decode workload, fp64 rescaled "
                       "recursion (OpenMP over b, c), measured on %d steps" % (steps, steps)}
 

@@ -2,8 +2,8 @@
 
 Argument marshalling only: every step of the operator runs in the HIP kernels of
 librwkv_wkv.so (built in-tree by ``build.py``); PyTorch provides device memory and the
-current stream. Importing this module loads the library and fails loudly if it has not
-been built; there is no CPU fallback.
+current stream. Importing this module loads the library (or the file RWKV_WKV_LIB names) and fails
+loudly, with an ImportError naming the path, if it is not there; there is no CPU fallback.
 
 Entry points mirror the C ABI in include/rwkv_wkv.h:
 
@@ -30,7 +30,8 @@ import os
 import torch  # first: its HIP runtime is the one the library binds to
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "librwkv_wkv.so")
+# the in-tree build, unless RWKV_WKV_LIB names another copy of the library
+LIB_PATH = os.environ.get("RWKV_WKV_LIB") or os.path.join(_PKG, "librwkv_wkv.so")
 
 WKV_OK = 0
 WKV_ERR_INVALID_ARG = 1

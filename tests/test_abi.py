@@ -368,3 +368,21 @@ def test_python_layer_rejects_bad_tensors(pkg):
         pkg.forward(torch.zeros(4), torch.zeros(4), x, x)  # CPU tensors
     with pytest.raises(TypeError):
         pkg.forward(torch.zeros(4), torch.zeros(4), x.double(), x)
+
+
+def test_missing_library_fails_loudly_with_its_path(tmp_path):
+    """No CPU fallback: a library that is not there is an ImportError naming the path
+    (RWKV_WKV_LIB points the binding at a copy; here at a file that does not exist)."""
+    import subprocess
+    import sys
+    missing = str(tmp_path / "no_such_librwkv_wkv.so")
+    env = dict(os.environ, RWKV_WKV_LIB=missing)
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n"
+            "    import rwkv_linear_attention_forward_amd\n"
+            "except ImportError as e:\n"
+            "    print('IMPORTERROR', e)\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "IMPORTERROR" in r.stdout and missing in r.stdout
