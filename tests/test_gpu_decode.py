@@ -149,11 +149,12 @@ def _decode_inputs(torch, dev, B, C, seed):
 
 
 def test_decode_grid_stride_pass(wkv, dev):
-    # B*C past 2^29 elements: the launch caps its grid and lanes loop; the result is bitwise
-    # that of the same rows decoded in two calls of one pass each
+    # more groups of four sequences than a grid's y extent (65535): the launch caps its grid
+    # and each workgroup row loops over groups; the last group holds three sequences. The
+    # result is bitwise that of the same rows decoded in two calls of one pass each.
     import torch
-    B, C = 131200, 4099
-    assert B * C > (1 << 29)
+    B, C = 262203, 70
+    assert (B + 3) // 4 > 65535 and (B // 2 + 3) // 4 <= 65535
     w, u, k, v, a, b, p = _decode_inputs(torch, dev, B, C, 32)
     st = [t.clone() for t in (a, b, p)]
     y = wkv.decode_step(w, u, k, v, *st)
