@@ -43,6 +43,38 @@ def backward_state_grad(w, u, k, v, dy, state):
     return (dk[:, 1:], dv[:, 1:], dw, du, dv0 / b, dk0 / b - dv0 * a / (b * b), dk0)
 
 
+def state_token_abs_terms(w, u, k, v, dy, state):
+    """The sums of the absolute values of the terms of the prepended state token's dv0 and
+    dk0: dv0 = sum_t g_t P_t0 with P_t0 >= 0, so |g| in place of g gives sum_t |g_t| P_t0;
+    dk0 = sum_t g_t P_t0 (v0 - y_t), so g_t sign(v0 - y_t) in place of g gives
+    sum_t |g_t| P_t0 |v0 - y_t| (y of the sequence with the token prepended)."""
+    kk, vv = prepend_state_token(state, k, v)
+    dy = np.asarray(dy, np.float64)
+    g = np.abs(np.concatenate([np.zeros_like(dy[:, :1]), dy], axis=1))
+    y = oracle.forward_direct(w, u, kk, vv)
+    _, dv_abs, _, _ = oracle.backward_direct(w, u, kk, vv, g)
+    dk_abs, _, _, _ = oracle.backward_direct(w, u, kk, vv, g * np.sign(vv[:, :1] - y))
+    return dv_abs[:, 0], dk_abs[:, 0]
+
+
+def state_grad_scale(w, u, k, v, dy, state, dA=None, dB=None):
+    """The conditioning of (da, db, dp): for da and db the sum of the absolute values of the
+    terms that make them up (through da = dv0 / b, db = dk0 / b - dv0 a / b^2, and with a
+    cotangent (dA, dB) of the final state the terms final_state_terms adds); for dp, which
+    is a da + b db (the state's gradient along its own scale), |a| times da's plus |b| times
+    db's. An entry is computed to 1e-4 of its scale when its error is below 1e-4 of it; |entry|
+    never exceeds it."""
+    a, b, p = (np.asarray(s, np.float64) for s in state)
+    dv0, dk0 = state_token_abs_terms(w, u, k, v, dy, state)
+    sa = dv0 / b
+    sb = dk0 / b + dv0 * np.abs(a) / (b * b)
+    if dA is not None:
+        *_, xa, xb, _ = final_state_terms(w, u, k, v, state, dA, dB)
+        sa = sa + np.abs(xa)
+        sb = sb + np.abs(xb)
+    return sa, sb, np.abs(a) * sa + np.abs(b) * sb
+
+
 def final_state_terms(w, u, k, v, state, dA, dB):
     """The gradients of sum_{b,c} (dA A_T + dB B_T), (A_T, B_T) the state after the last
     token, in the order (dk, dv, dw, du, da, db, dp). From the recursion unrolled: A_T =

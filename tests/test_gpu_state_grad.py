@@ -13,7 +13,7 @@ import pytest
 
 import wkv_inputs
 from helpers import assert_wkv_close
-from state_ref import backward_state_grad
+from state_ref import backward_state_grad, state_grad_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,16 @@ def _forward_state(wkv, dev, t, state):
     st = [_t(dev, s) for s in state]
     wkv.forward_state(t["w"], t["u"], t["k"], t["v"], *st, workspace=ws)
     return ws
+
+
+def _floors(scale):
+    """The floor of |x - r| <= 1e-4 max(|r|, floor) per gradient: the operator's 0.1 for dk,
+    dv, dr, dw, du; for da, db, dp, which scale with e^p over (b, c) and sum terms of either
+    sign, each entry's own conditioning, the sum of the absolute values of its terms
+    (state_grad_scale, pinned in test_oracle_state.py), so each is judged to 1e-4 of it."""
+    sa, sb, sp = scale
+    return {"dk": 0.1, "dv": 0.1, "dr": 0.1, "dw": 0.1, "du": 0.1, "da": sa, "db": sb,
+            "dp": sp}
 
 
 def _log(name, v):
@@ -49,13 +59,12 @@ def test_state_gradient_parity(wkv, dev, B, T, C, prange):
     got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)
     torch.cuda.synchronize()
     ref = backward_state_grad(x["w"], x["u"], x["k"], x["v"], x["dy"], st)
+    floors = _floors(state_grad_scale(x["w"], x["u"], x["k"], x["v"], x["dy"], st))
     worst = 0.0
     for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
         r = np.asarray(r, np.float64)
-        # the state gradients scale with e^p: judged relative to their own largest entry
-        floor = 0.1 if n[1] in "kvwu" else 0.1 * max(float(np.max(np.abs(r))), 1e-300)
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s B=%d T=%d C=%d p in %s"
-                                            % (n, B, T, C, prange), floor=floor))
+                                            % (n, B, T, C, prange), floor=floors[n]))
     _log("B=%d T=%d C=%d p in %s" % (B, T, C, prange), worst)
 
 
@@ -127,13 +136,14 @@ def test_full_layer_state_gradient(wkv, dev):
     got = wkv.backward_state(t["w"], t["u"], t["k"], t["v"], t["dy"], ws)
     torch.cuda.synchronize()
     ref = backward_state_grad(x["w"], x["u"], x["k"][:, :Tp], x["v"][:, :Tp], dy[:, :Tp], st)
+    floors = _floors(state_grad_scale(x["w"], x["u"], x["k"][:, :Tp], x["v"][:, :Tp],
+                                      dy[:, :Tp], st))
     worst = 0.0
     for g, r, n in ((got[0][:, :Tp], ref[0], "dk"), (got[1][:, :Tp], ref[1], "dv"),
                     (got[2], ref[2], "dw"), (got[3], ref[3], "du"), (got[4], ref[4], "da"),
                     (got[5], ref[5], "db"), (got[6], ref[6], "dp")):
         r = np.asarray(r, np.float64)
-        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
-        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "l3b " + n, floor=floor))
+        worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "l3b " + n, floor=floors[n]))
     assert torch.count_nonzero(got[0][:, Tp:]).item() == 0
     _log("l3b (loss on the first %d tokens)" % Tp, worst)
 
@@ -174,12 +184,12 @@ def test_final_state_cotangent_parity(wkv, dev, B, T, C, prange):
     st = wkv_inputs.random_state(B, C, seed=T + 2 * C, p_range=prange)
     got, dA, dB = _cot_case(wkv, dev, x, st, seed=T + C)
     ref = backward_state_grad_cot(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB)
+    floors = _floors(state_grad_scale(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB))
     worst = 0.0
     for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
         r = np.asarray(r, np.float64)
-        floor = 0.1 if n[1] in "kvwu" else 0.1 * max(float(np.max(np.abs(r))), 1e-300)
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s B=%d T=%d C=%d p in %s"
-                                            % (n, B, T, C, prange), floor=floor))
+                                            % (n, B, T, C, prange), floor=floors[n]))
     _log("final-state cotangent B=%d T=%d C=%d p in %s" % (B, T, C, prange), worst)
 
 
@@ -211,15 +221,15 @@ def test_pieces_chain_to_the_whole_sequence(wkv, dev, cuts):
         dstate = (grads[i][4], grads[i][5])
     torch.cuda.synchronize()
     ref = backward_state_grad(x["w"], x["u"], x["k"], x["v"], x["dy"], st)
+    floors = _floors(state_grad_scale(x["w"], x["u"], x["k"], x["v"], x["dy"], st))
     got = [torch.cat([g[0] for g in grads], dim=1), torch.cat([g[1] for g in grads], dim=1),
            sum(g[2].double() for g in grads), sum(g[3].double() for g in grads),
            grads[0][4], grads[0][5], grads[0][6]]
     worst = 0.0
     for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
         r = np.asarray(r, np.float64)
-        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s cuts=%s" % (n, cuts),
-                                            floor=floor))
+                                            floor=floors[n]))
     _log("pieces %s" % (cuts,), worst)
 
 
@@ -239,12 +249,12 @@ def test_final_state_cotangent_extreme_decay(wkv, dev):
     st = wkv_inputs.random_state(B, C, seed=121, p_range=(-3.0, 3.0))
     got, dA, dB = _cot_case(wkv, dev, x, st, seed=122)
     ref = backward_state_grad_cot(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB)
+    floors = _floors(state_grad_scale(x["w"], x["u"], x["k"], x["v"], x["dy"], st, dA, dB))
     worst = 0.0
     for g, r, n in zip(got, ref, ("dk", "dv", "dw", "du", "da", "db", "dp")):
         r = np.asarray(r, np.float64)
-        floor = 0.1 if n[1] in "kvwu" else 0.1 * float(np.max(np.abs(r)))
         worst = max(worst, assert_wkv_close(g.cpu().numpy(), r, "%s extreme w" % n,
-                                            floor=floor))
+                                            floor=floors[n]))
     _log("final-state cotangent, w up to 200", worst)
 
 
@@ -291,6 +301,7 @@ def test_typed_and_gated_state_pair(wkv, dev, dtype, gated):
     torch.cuda.synchronize()
     dyeff = wide["dy"] * _sig(rw) if gated else wide["dy"]
     ref = list(backward_state_grad_cot(x["w"], x["u"], wide["k"], wide["v"], dyeff, st, dA, dB))
+    floors = _floors(state_grad_scale(x["w"], x["u"], wide["k"], wide["v"], dyeff, st, dA, dB))
     names = ["dk", "dv", "dw", "du", "da", "db", "dp"]
     yref = yo * _sig(rw) if gated else yo
     if gated:
@@ -306,6 +317,5 @@ def test_typed_and_gated_state_pair(wkv, dev, dtype, gated):
         if n in ("dk", "dv", "dr") and dtype != "float32":
             worst = max(worst, assert_io_close(g, r, dtype, what))
         else:
-            floor = 0.1 if n[1] in "kvwur" else 0.1 * float(np.max(np.abs(r)))
-            worst = max(worst, assert_wkv_close(g, r, what, floor=floor))
+            worst = max(worst, assert_wkv_close(g, r, what, floor=floors[n]))
     _log("%s gated=%s with cotangent" % (dtype, gated), worst)

@@ -201,3 +201,61 @@ def test_final_state_cotangent_chains_two_pieces():
     np.testing.assert_allclose(g1[3] + g2[3], whole[3], rtol=1e-9, atol=1e-12)
     for i in (4, 5, 6):
         np.testing.assert_allclose(g1[i], whole[i], rtol=1e-9, atol=1e-12)
+
+
+def _explicit_state_token_terms(w, u, k, v, dy, state):
+    """Brute force in numpy for tiny shapes: the softmax weight P_t0 of the prepended state
+    token in every later output t, and sum_t |g_t| P_t0, sum_t |g_t| P_t0 |v0 - y_t|."""
+    kk, vv = _prepend(state, k, v)
+    B, T1, C = kk.shape
+    dv_abs = np.zeros((B, C))
+    dk_abs = np.zeros((B, C))
+    for b in range(B):
+        for c in range(C):
+            for t in range(1, T1):
+                logit = np.array([-(t - 1 - i) * w[c] + kk[b, i, c] for i in range(t)]
+                                 + [u[c] + kk[b, t, c]])
+                P = np.exp(logit - logit.max())
+                P /= P.sum()
+                y = float(P @ vv[b, :t + 1, c])
+                g = abs(dy[b, t - 1, c])
+                dv_abs[b, c] += g * P[0]
+                dk_abs[b, c] += g * P[0] * abs(vv[b, 0, c] - y)
+    return dv_abs, dk_abs
+
+
+@pytest.mark.parametrize("T", [1, 3, 12])
+def test_state_token_abs_terms_by_brute_force(T):
+    """The conditioning the GPU state-gradient tests are judged against is the sum of the
+    absolute terms of dv0 and dk0; it is checked here against the terms written out."""
+    from state_ref import state_token_abs_terms
+    rng, w, u, k, v = _rand(2, T, 4, 70 + T, kscale=1.5)
+    st = _state(rng, 2, 4)
+    dy = rng.standard_normal((2, T, 4))
+    got = state_token_abs_terms(w, u, k, v, dy, st)
+    want = _explicit_state_token_terms(w, u, k, v, dy, st)
+    for g, r in zip(got, want):
+        np.testing.assert_allclose(g, r, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("T", [1, 9, 40])
+def test_state_grad_scale_bounds_the_gradients(T):
+    """Each of |da|, |db|, |dp| is at most its scale (a sum of absolute terms), with and
+    without a cotangent of the final state, and the scale is not needlessly loose: for a
+    one-signed cotangent dy > 0, dv0 has no cancellation and |da| equals its scale."""
+    from state_ref import state_grad_scale
+    rng, w, u, k, v = _rand(3, T, 5, 80 + T)
+    st = _state(rng, 3, 5)
+    dy = rng.standard_normal((3, T, 5))
+    dA = rng.standard_normal((3, 5))
+    dB = rng.standard_normal((3, 5))
+    for cot in (False, True):
+        ref = (backward_state_grad_cot(w, u, k, v, dy, st, dA, dB) if cot
+               else backward_state_grad(w, u, k, v, dy, st))
+        sc = state_grad_scale(w, u, k, v, dy, st, *((dA, dB) if cot else ()))
+        for r, s in zip(ref[4:], sc):
+            assert np.all(np.abs(r) <= s * (1 + 1e-12))
+    dyp = np.abs(dy)
+    ref = backward_state_grad(w, u, k, v, dyp, st)
+    sc = state_grad_scale(w, u, k, v, dyp, st)
+    np.testing.assert_allclose(np.abs(ref[4]), sc[0], rtol=1e-12)
