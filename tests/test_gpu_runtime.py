@@ -1,4 +1,4 @@
-"""Process-level checks on the GPU machine (marked gpu): the library runs on gfx950 and
+"""Process-level checks on the GPU (marked gpu): the library runs on gfx950 and
 shares the single HIP runtime that torch loaded."""
 import pytest
 
