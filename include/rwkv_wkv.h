@@ -32,7 +32,9 @@
  *   - The library allocates no device memory, with one exception: wkv_forward, whose
  *     signature has no workspace, takes its scan's scratch from the current device's
  *     stream-ordered memory pool (hipMallocAsync) and returns it (hipFreeAsync), both on
- *     `stream`, within the call. Every other entry point uses only memory the caller passes.
+ *     `stream`, within the call. Every other entry point uses only memory the caller passes,
+ *     except wkv_forward_noalloc, whose scratch is a static array of the library's code
+ *     object (64 MiB on each GPU it is loaded on, held until the process ends).
  *
  * Entry points. wkv_forward, wkv_backward_workspace_size, wkv_backward and wkv_decode_step
  * are the operator's three calls with the plainest boundary: a forward that writes y, a
