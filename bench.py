@@ -23,7 +23,9 @@ the forward
 from a given state that also returns the final state (prompt prefill), on the same layer;
 `gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer; `bf16`
 the step with the [B, T, C] tensors stored as bfloat16 (reported apart: the benchmark's own
-workload is fp32); `token_shift` the mix that produces the projections' inputs.
+workload is fp32); `token_shift` the mix that produces the projections' inputs;
+`layout_ceiling` the streaming rate of the kernels' workgroup layout (and of wider ones) from
+librwkv_stream_probe.so, with the step's measured traffic rates against it.
 
 Before the W warm-up steps, `--settle` untimed steps (400 by default, about 0.25 s) run the
 step itself under sustained load: from idle the GPU first runs the step's kernels at full
@@ -764,6 +766,49 @@ def bench_t_scaling(wkv, torch, dev, Ts=(512, 1024, 2048, 4096, 8192), B=8, C=25
             "timing": "HIP events on the library's stream, median of %d iterations" % reps}
 
 
+def bench_layout_ceiling(torch, dev, reps=30):
+    """The streaming ceiling of workgroup layouts (librwkv_stream_probe.so: y = k + v over the
+    3B-class layer's bytes, 12 B per element, no other arithmetic): the forward's and
+    backward's units (two waves over one 64-channel strip and 64 rows) at their occupancy of
+    three waves per SIMD, and two and four adjacent strips per workgroup at the same
+    occupancy. Median of `reps` launches, HIP events."""
+    import ctypes
+    path = os.path.join(PKG_DIR, "librwkv_stream_probe.so")
+    if not os.path.exists(path):
+        return {"error": "librwkv_stream_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    l3b = __import__("wkv_inputs").WORKLOADS["l3b"]
+    R, C = l3b["B"] * l3b["T"], l3b["C"]
+    k = torch.randn(R, C, device=dev)
+    v = torch.randn(R, C, device=dev)
+    y = torch.empty_like(k)
+    out = {}
+    # (strips, chunks, dynamic LDS per workgroup giving three waves per SIMD at 160 KB per CU)
+    for name, strips, chunks, lds in (("units_1x2", 1, 2, 24576), ("strips_2x2", 2, 2, 49152),
+                                      ("strips_4x1", 4, 1, 49152)):
+        def call():
+            rc = lib.wkv_stream_probe(ctypes.c_int64(R), ctypes.c_int64(C),
+                                      ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                      ctypes.c_void_p(y.data_ptr()), strips, chunks, lds,
+                                      ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+            if rc != 0:
+                raise RuntimeError("wkv_stream_probe returned %d" % rc)
+        for _ in range(5):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize(dev)
+        us = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+        out[name] = {"us": us, "tbps": 12 * R * C / (us * 1e-6) / 1e12,
+                     "correct": bool(torch.equal(y, k + v))}
+    out["workload"] = "y = k + v, [%d][%d] fp32, 12 B per element, three waves per SIMD" % (R, C)
+    return out
+
+
 def bench_decode_horizon(wkv, torch, dev, steps=1000):
     """The batched decode workload over its whole horizon: each step draws the 40 layers'
     k, v on the device (outside the timing) and replays the step's 40 calls from a captured
@@ -942,6 +987,15 @@ def main(argv=None):
         "outputs_finite": r["finite"],
     }
     out["copy_1gib"] = bench_copy(torch, dev)
+    ceil = bench_layout_ceiling(torch, dev)
+    unit = ceil.get("units_1x2", {}).get("tbps")
+    for op, ms in (("forward", fwd), ("backward", bwd)):
+        tb = counter_traffic(op)
+        if tb is not None and unit:
+            # measured traffic rate of the step's kernel against the units' layout ceiling
+            ceil[op + "_traffic_tbps"] = tb / (ms * 1e-3) / 1e12
+            ceil[op + "_of_layout_ceiling"] = ceil[op + "_traffic_tbps"] / unit
+    out["layout_ceiling"] = ceil
     if not args.no_configs:
         cpu = not args.no_cpu
         out["configs"] = {

@@ -1,4 +1,5 @@
-"""Build librwkv_wkv.so in-tree with hipcc for gfx950.
+"""Build librwkv_wkv.so (and the benchmark's librwkv_stream_probe.so) in-tree with hipcc for
+gfx950.
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel) and the
 objects are linked into rwkv_linear_attention_forward_amd/librwkv_wkv.so. The build
@@ -16,6 +17,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librwkv_wkv.so")
+# the benchmark's streaming-ceiling probe: a library of its own, not part of the operator's
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "librwkv_stream_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 out of scalar fp32 code.
@@ -55,7 +59,20 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """librwkv_stream_probe.so (bench.py's layout-ceiling leg)."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s" % (PROBE_SRC, r.stdout + r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
