@@ -38,7 +38,8 @@
 //          look-back toward later windows) into the future sums at each chunk's end.
 //   R3     the same recursion from the incoming future sums gives, per token,
 //          e^{k_i} G_i = e_i R_i and e^{k_i} H_i = e_i Q_i, hence dv and dk.
-// Chunks whose frame would under- or overflow are redone with a per-token rescaled
+// Chunks whose frame would under- or overflow, or that hold a key more than 87 below their
+// largest (an fp32 weight without full precision), are redone with a per-token rescaled
 // recursion in fp64 (exact_chunk).
 #include "wkv_chunk.h"
 

@@ -32,11 +32,12 @@
 //            y_j = (S_j + e^u e_j v_j) / (Z_j + e^u e_j),  S_{j+1} = e^{-w} S_j + e_j v_j.
 // One fp64 exp2 per element in phase 1, one fp32 reciprocal per element in phase 3.
 //
-// The fixed frame is exact in real arithmetic but can underflow when k varies by more
-// than ~70 inside one chunk, or overflow when the incoming carry exceeds the chunk frame
-// by 2^64. Such chunks (rare; only far outside the training distributions) are detected
-// per wave and recomputed with the per-token rescaled recursion in fp64, which is safe
-// for any finite k.
+// The fixed frame is exact in real arithmetic, but its fp32 weights e^{k - ref} keep full
+// precision only for keys within ~87 of the chunk's largest (the fp64 summaries to ~600),
+// and the incoming carry must not exceed the frame by more than 2^64. A chunk outside
+// either bound, or on a wave with a bonus |u| > 60, is detected per wave and computed with
+// the per-token rescaled recursion in fp64 instead, which is safe for any finite k (rare:
+// only far outside the training distributions).
 #include "wkv_chunk.h"
 
 namespace wkvdev {
