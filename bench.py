@@ -314,23 +314,49 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(x, budget_s=10.0, max_runs=3):
+def _violation(got, ref):
+    """Largest |got - ref| / (1e-4 max(|ref|, 0.1)) over the arrays (<= 1: within the
+    operator's tolerance), None when there is nothing to compare."""
+    import numpy as np
+    worst = None
+    for g, r in zip(got, ref):
+        g = np.asarray(g, np.float64)
+        r = np.asarray(r, np.float64)
+        if g.size == 0:
+            continue
+        v = float(np.max(np.abs(g - r) / (1e-4 * np.maximum(np.abs(r), 0.1))))
+        if not np.all(np.isfinite(g)):
+            v = float("inf")
+        worst = v if worst is None else max(worst, v)
+    return worst
+
+
+def cpu_baseline(x, budget_s=10.0, max_runs=3, gpu_out=None):
+    """The oracle timed on the host (median of up to `max_runs` runs within `budget_s`);
+    with the GPU's outputs (y, dk, dv, dw, du) of the same inputs, also their largest
+    violation of the tolerance against the oracle's outputs of the timed runs."""
     import oracle
     B, T, C = x["k"].shape
     times = []
     t_start = time.perf_counter()
+    ref = None
     while len(times) < max_runs:
         t0 = time.perf_counter()
-        oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
-        oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
+        y = oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
+        g = oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
         times.append(time.perf_counter() - t0)
+        ref = (y,) + tuple(g)
         if time.perf_counter() - t_start > budget_s:
             break
     t = statistics.median(times)
-    return {"value": B * T * C / t, "unit": "elem/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": "full workload B=%d T=%d C=%d, fp64 plain recurrence forward + linear-time "
-                      "backward (OpenMP over b, c), median of %d runs" % (B, T, C, len(times))}
+    out = {"value": B * T * C / t, "unit": "elem/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": "full workload B=%d T=%d C=%d, fp64 plain recurrence forward + linear-time "
+                     "backward (OpenMP over b, c), median of %d runs" % (B, T, C, len(times))}
+    if gpu_out is not None:
+        out["gpu_max_violation"] = _violation(gpu_out, ref)
+        out["gpu_max_violation_of"] = "y, dk, dv, dw, du of the timed step against these runs"
+    return out
 
 
 # ---------------------------------------------------------------------------------------
@@ -376,7 +402,8 @@ def bench_step(wkv, torch, dev, x, steps, warmup, settle=0):
     span_ms = evs[0][0].elapsed_time(evs[-1][2])
     ok = all(bool(torch.isfinite(a).all()) for a in (y,) + outs)
     return {"B": B, "T": T, "C": C, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "span_ms": span_ms,
-            "wall_s": wall, "finite": ok, "settle_s": t_settle}
+            "wall_s": wall, "finite": ok, "settle_s": t_settle,
+            "outputs": (y,) + outs}
 
 
 def bench_copy(torch, dev, reps=3):
@@ -714,10 +741,13 @@ def bench_workload(wkv, torch, dev, name, with_bwd, reps, warmup, flush, cpu=Tru
     r.update(elem_per_s=n / (tot_us * 1e-6), algorithmic_gbps=alg / (tot_us * 1e-6) / 1e9,
              frac_of_peak=alg / (tot_us * 1e-6) / 1e9 / PEAK_GBPS, outputs_finite=ok)
     if cpu:
+        ref = []
+
         def run():
-            oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
-            if with_bwd:
-                oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
+            yr = oracle.forward_recurrent(x["w"], x["u"], x["k"], x["v"])
+            gr = (oracle.backward_recurrent(x["w"], x["u"], x["k"], x["v"], x["dy"])
+                  if with_bwd else ())
+            ref[:] = [yr] + list(gr)
         sec, runs = _oracle_time(run)
         r["cpu_baseline"] = {
             "value": n / sec, "unit": "elem/s", "cores": oracle.num_threads(), "kind": "oracle",
@@ -725,6 +755,8 @@ def bench_workload(wkv, torch, dev, name, with_bwd, reps, warmup, flush, cpu=Tru
             "sample": "full workload, fp64 plain recurrence forward%s (OpenMP over b, c), median "
                       "of %d runs" % (" + linear-time backward" if with_bwd else "", runs)}
         r["speedup_vs_cpu"] = r["elem_per_s"] / r["cpu_baseline"]["value"]
+        got = [y] + (list(outs) if with_bwd else [])
+        r["cpu_baseline"]["gpu_max_violation"] = _violation([a.cpu().numpy() for a in got], ref)
     return r
 
 
@@ -1019,7 +1051,8 @@ def main(argv=None):
     if not args.no_shift:
         out["token_shift"] = bench_shift(wkv, torch, dev)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x)
+        out["cpu_baseline"] = cpu_baseline(
+            x, gpu_out=[a.cpu().numpy() for a in r["outputs"]])
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -1,8 +1,9 @@
 """Host logic of bench.py, on the CPU: the one-GPU refusal, the kernel-trace summary (which
 dispatches are the timed ones), the counter summary (bytes scaled by the device copy's
-counters, traffic per element, clock) and the rule that counter traffic is reported only
-for the kernel sources it was taken on. No GPU and no rocprofv3 output needed: the CSV
-files are written here in rocprofv3's column layout."""
+counters, traffic per element, clock), the rule that counter traffic is reported only for
+the kernel sources it was taken on, and the tolerance figure the oracle legs report. No GPU
+and no rocprofv3 output needed: the CSV files are written here in rocprofv3's column
+layout."""
 import csv
 import json
 import os
@@ -122,3 +123,18 @@ def test_committed_counter_summary_matches_the_sources():
     assert rec["source_sha256"] == bench.source_hash()
     for op in ("forward", "backward"):
         assert rec["kernels"][op]["traffic_bytes"] > 0
+
+
+def test_violation_is_the_operators_tolerance():
+    """The bench line's parity figure: the largest |x - r| / (1e-4 max(|r|, 0.1))."""
+    import numpy as np
+    r = np.array([1.0, -2.0, 0.01, 0.0])
+    assert bench._violation([r], [r]) == 0.0
+    g = r + np.array([1e-4, 0.0, 0.0, 0.0])
+    assert bench._violation([g], [r]) == pytest.approx(1.0)
+    g = r + np.array([0.0, 0.0, 5e-6, 0.0])
+    assert bench._violation([g, r], [r, r]) == pytest.approx(0.5)
+    g = r.copy()
+    g[3] = np.nan
+    assert bench._violation([g], [r]) == float("inf")
+    assert bench._violation([np.zeros(0)], [np.zeros(0)]) is None
