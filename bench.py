@@ -18,7 +18,8 @@ reported only while the kernel sources still hash to the value recorded there.
 `cpu_baseline` times the fp64 CPU oracle (test infrastructure, OpenMP over all host
 threads) on the same workload. `decode` reports the batched decode step separately
 (B=256, C=5120, 40 layer states, 36 B per element per call; the step's 40 calls replayed
-from a captured HIP graph, with the eager Python-launched rate beside it); `forward_state`
+from a captured HIP graph, with the eager Python-launched rate beside it, and a pure stream of
+its traffic in its layout from librwkv_stream_probe.so as its ceiling); `forward_state`
 the forward
 from a given state that also returns the final state (prompt prefill), on the same layer;
 `gated` the receptance-gated forward + backward (out = sigma(r) y) on the same layer; `bf16`
@@ -841,6 +842,55 @@ def bench_layout_ceiling(torch, dev, reps=30):
     return out
 
 
+def bench_decode_ceiling(torch, dev, steps=20, warmup=3):
+    """The streaming ceiling of the decode's traffic in its own layout
+    (librwkv_stream_probe.so's wkv_stream_probe_decode: read k, v, a, b, p and write y = k + v,
+    a + k, b + v, p + 1, 36 B per element, one channel and four sequences per lane) over the
+    batched decode workload's 40 layers of [256][5120] fp32 tensors, timed as the decode leg
+    times the decode: the 40 calls captured once and replayed, median per call."""
+    import ctypes
+    import wkv_inputs
+    path = os.path.join(PKG_DIR, "librwkv_stream_probe.so")
+    if not os.path.exists(path):
+        return {"error": "librwkv_stream_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    cfg = wkv_inputs.DECODE
+    B, C, L = cfg["B"], cfg["C"], cfg["layers"]
+    bufs = torch.randn(L, 6, B, C, device=dev)  # k, v, a, b, p, y per layer
+
+    def calls():
+        st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        for l in range(L):
+            ptr = [ctypes.c_void_p(bufs[l, i].data_ptr()) for i in range(6)]
+            rc = lib.wkv_stream_probe_decode(ctypes.c_int64(B), ctypes.c_int64(C), *ptr, st)
+            if rc != 0:
+                raise RuntimeError("wkv_stream_probe_decode returned %d" % rc)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    ms = []
+    for s in range(warmup + steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        if s >= warmup:
+            ms.append(e0.elapsed_time(e1))
+    us = statistics.median(ms) * 1e3 / L
+    correct = bool(torch.equal(bufs[:, 5], bufs[:, 0] + bufs[:, 1]))
+    del graph, bufs
+    return {"us_per_call": us, "tbps": 36 * B * C / (us * 1e-6) / 1e12, "correct": correct,
+            "workload": "read k, v, a, b, p, write y, a, b, p: [%d][%d] fp32 x %d layers, "
+                        "the decode's layout, graph replay" % (B, C, L)}
+
+
 def bench_decode_horizon(wkv, torch, dev, steps=1000):
     """The batched decode workload over its whole horizon: each step draws the 40 layers'
     k, v on the device (outside the timing) and replays the step's 40 calls from a captured
@@ -1042,6 +1092,11 @@ def main(argv=None):
     if not args.no_decode:
         out["decode"] = bench_decode(wkv, torch, dev)
         out["decode"]["bf16"] = bench_decode(wkv, torch, dev, dtype=torch.bfloat16)
+        dceil = bench_decode_ceiling(torch, dev)
+        if "us_per_call" in dceil:
+            # the decode's rate against a pure stream of its traffic in its layout
+            dceil["decode_of_copy_ceiling"] = dceil["us_per_call"] / out["decode"]["us_per_call"]
+        out["decode"]["copy_ceiling"] = dceil
     if not args.no_state:
         out["forward_state"] = bench_forward_state(wkv, torch, dev, x)
     if not args.no_gated:

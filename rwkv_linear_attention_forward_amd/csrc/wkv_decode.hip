@@ -15,10 +15,11 @@ namespace wkvdev {
 // Grid: x over 256-channel blocks, y over groups of kDecodeRows sequences (strided when there
 // are more groups than a grid's y extent). A lane owns one channel c and kDecodeRows
 // sequences b0 .. b0 + kDecodeRows - 1: the channel's constants (w, u and the decay factors
-// of the rescaled update) are formed once per lane, and the kDecodeRows elements' loads are
-// issued together, each coalesced over the wave's 64 channels. No division or remainder in
-// the index math. On the 256 x 5120 decode workload the grid is 20 x 64 workgroups of four
-// waves: 5,120 waves, all resident at once.
+// of the rescaled update) are formed once per lane, and the rows go through a two-stage
+// pipeline, row r + 1's loads issued before row r's arithmetic and stores, so that a wave's
+// loads and stores overlap. No division or remainder in the index math. On the 256 x 5120
+// decode workload the grid is 20 x 64 workgroups of four waves: 5,120 waves, all resident at
+// once.
 #ifndef WKV_DECODE_ROWS
 #define WKV_DECODE_ROWS 4
 #endif
@@ -40,35 +41,46 @@ __device__ __forceinline__ void decode_group(int64_t b0, int rows, int64_t C, in
     const int64_t base = b0 * C;
     const rsrc_t ra = make_rsrc(a + base), rb = make_rsrc(b + base), rp = make_rsrc(p + base);
     const rsrc_t rk = make_rsrc(k + base), rv = make_rsrc(v + base), ry = make_rsrc(y + base);
-    Rs s[kDecodeRows];
-    float kk[kDecodeRows], vv[kDecodeRows];
-#pragma unroll
-    for (int r = 0; r < kDecodeRows; ++r) {
-        // rows past B re-read the group's first row and are never stored
-        const int rr = r < rows ? r : 0;
-        const int sf = (int)(rr * C * 4), sio = (int)(rr * C * kIoBytes<IO>);
-        s[r] = Rs{bload(ra, vf, sf), bload(rb, vf, sf), bload(rp, vf, sf)};
-        kk[r] = bload_io<IO>(rk, vio, sio);
-        vv[r] = bload_io<IO>(rv, vio, sio);
-    }
-    // the channel's constants, read after the rows' loads are issued, so that their round
-    // trip overlaps the rows' instead of preceding it (the empty statement keeps the
+    // row r's scalar byte offsets (a row past B reads the group's first row: in bounds)
+    auto sf = [&](int r) { return (int)((r < rows ? r : 0) * C * 4); };
+    auto sio = [&](int r) { return (int)((r < rows ? r : 0) * C * kIoBytes<IO>); };
+    const Rs s0{bload(ra, vf, 0), bload(rb, vf, 0), bload(rp, vf, 0)};
+    const float k0 = bload_io<IO>(rk, vio, 0), v0 = bload_io<IO>(rv, vio, 0);
+    // the channel's constants, read after the first row's loads are issued, so that their
+    // round trip overlaps the row's instead of preceding it (the empty statement keeps the
     // compiler from moving memory accesses across it)
     asm volatile("" ::: "memory");
     const float uc = bload(make_rsrc(u), vf, 0);
     const Decay dc = make_decay(bload(make_rsrc(w), vf, 0));
-    // every row is computed and stored, a row past B as a second copy of the group's first
-    // row (the same inputs, so the same values land on the same addresses); branch-free, so
-    // the compiler cannot sink any row's loads behind a condition
+    Rs s = s0;
+    float kk = k0, vv = v0;
 #pragma unroll
     for (int r = 0; r < kDecodeRows; ++r) {
-        const int rr = r < rows ? r : 0;
-        const int sf = (int)(rr * C * 4), sio = (int)(rr * C * kIoBytes<IO>);
-        bstore_io<IO>(ry, rs_out(s[r], kk[r], vv[r], uc), vio, sio);
-        rs_push(s[r], kk[r], vv[r], dc);
-        bstore(ra, s[r].a, vf, sf);
-        bstore(rb, s[r].b, vf, sf);
-        bstore(rp, s[r].p, vf, sf);
+        Rs sn{0.0f, 0.0f, 0.0f};
+        float kn = 0.0f, vn = 0.0f;
+        if (r + 1 < kDecodeRows) {
+            // row r + 1's loads go out before row r's stores. A row past B takes the first
+            // row's inputs as loaded before any store (its own load of that row may see the
+            // row already updated) and so stores the first row's results again, the same
+            // values at the same addresses: every row is computed and stored branch-free and
+            // the compiler cannot sink a row's loads behind a condition.
+            const bool dup = r + 1 >= rows;
+            const Rs sl{bload(ra, vf, sf(r + 1)), bload(rb, vf, sf(r + 1)),
+                        bload(rp, vf, sf(r + 1))};
+            const float kl = bload_io<IO>(rk, vio, sio(r + 1));
+            const float vl = bload_io<IO>(rv, vio, sio(r + 1));
+            sn = dup ? s0 : sl;
+            kn = dup ? k0 : kl;
+            vn = dup ? v0 : vl;
+        }
+        bstore_io<IO>(ry, rs_out(s, kk, vv, uc), vio, sio(r));
+        rs_push(s, kk, vv, dc);
+        bstore(ra, s.a, vf, sf(r));
+        bstore(rb, s.b, vf, sf(r));
+        bstore(rp, s.p, vf, sf(r));
+        s = sn;
+        kk = kn;
+        vv = vn;
     }
 }
 
@@ -80,6 +92,11 @@ __global__ __launch_bounds__(256) void wkv_decode_kernel(
     const io_t<IO> *__restrict__ k, const io_t<IO> *__restrict__ v, float *__restrict__ a,
     float *__restrict__ b, float *__restrict__ p, io_t<IO> *__restrict__ y) {
     const int c = (int)(blockIdx.x * 256 + threadIdx.x);
+    // the arguments are read into scalar registers before the channel guard, in one round
+    // trip (the compiler would otherwise read the size first, branch, then read the pointers:
+    // two dependent round trips ahead of every wave's first load; 4-5% of the decode's time)
+    asm volatile("" ::"s"(B), "s"(C), "s"(ngroups), "s"(w), "s"(u), "s"(k), "s"(v), "s"(a),
+                 "s"(b), "s"(p), "s"(y));
     if (c >= C) return;
     const int vf = c * 4, vio = c * kIoBytes<IO>;
     for (int64_t g = blockIdx.y; g < ngroups; g += gridDim.y) {

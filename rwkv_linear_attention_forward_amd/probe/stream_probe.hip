@@ -9,6 +9,10 @@
 // STRIPS = 1, CHUNKS = 2 is the layout of the forward's and backward's units (two waves
 // over one 64-channel strip and 64 consecutive rows). Dynamic LDS (unused) sets the number
 // of workgroups a CU holds, i.e. the occupancy.
+//
+// wkv_stream_probe_decode is the same measure for the decode step: the decode's 36 bytes per
+// element (read k, v, a, b, p; write y, a, b, p) in the decode kernel's layout, with a
+// minimum of arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +51,39 @@ hipError_t launch(int64_t R, int64_t C, const float *k, const float *v, float *y
     return hipGetLastError();
 }
 
+// Decode layout: a lane owns one channel and kDecRows consecutive sequences of [B][C] fp32
+// tensors; the grid is x over 256-channel blocks, y over groups of kDecRows sequences. All
+// rows' loads are issued first; then y = k + v, a + k, b + v and p + 1 are stored in place
+// (non-temporal, as the decode's accesses).
+constexpr int kDecRows = 4;
+
+__global__ __launch_bounds__(256) void decode_stream_kernel(int64_t C, const float *__restrict__ k,
+                                                            const float *__restrict__ v,
+                                                            float *__restrict__ a,
+                                                            float *__restrict__ b,
+                                                            float *__restrict__ p,
+                                                            float *__restrict__ y) {
+    const int64_t base = (int64_t)blockIdx.y * kDecRows * C + blockIdx.x * 256 + threadIdx.x;
+    float ka[kDecRows], va[kDecRows], aa[kDecRows], ba[kDecRows], pa[kDecRows];
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+        const int64_t i = base + r * C;
+        ka[r] = __builtin_nontemporal_load(k + i);
+        va[r] = __builtin_nontemporal_load(v + i);
+        aa[r] = __builtin_nontemporal_load(a + i);
+        ba[r] = __builtin_nontemporal_load(b + i);
+        pa[r] = __builtin_nontemporal_load(p + i);
+    }
+#pragma unroll
+    for (int r = 0; r < kDecRows; ++r) {
+        const int64_t i = base + r * C;
+        __builtin_nontemporal_store(ka[r] + va[r], y + i);
+        __builtin_nontemporal_store(aa[r] + ka[r], a + i);
+        __builtin_nontemporal_store(ba[r] + va[r], b + i);
+        __builtin_nontemporal_store(pa[r] + 1.0f, p + i);
+    }
+}
+
 }  // namespace
 
 // y = k + v over [R][C] in the layout (strips, chunks) with `lds_bytes` of dynamic LDS per
@@ -70,4 +107,20 @@ extern "C" int wkv_stream_probe(int64_t R, int64_t C, const float *k, const floa
     else
         return 1;
     return e == hipSuccess ? 0 : 2;
+}
+
+// The decode's traffic over [B][C] fp32 tensors in the decode kernel's layout: y = k + v,
+// a += k, b += v, p += 1 (in place). Returns 0, 1 for a shape the layout does not tile (C a
+// multiple of 256, B of 4 with B / 4 <= 65535, B * C < 2^40) or a null pointer, 2 for a
+// launch error.
+extern "C" int wkv_stream_probe_decode(int64_t B, int64_t C, const float *k, const float *v,
+                                       float *a, float *b, float *p, float *y, void *stream) {
+    if (B <= 0 || C <= 0 || C % 256 != 0 || B % kDecRows != 0 || B / kDecRows > 65535 ||
+        B > (int64_t(1) << 40) / C || k == nullptr || v == nullptr || a == nullptr ||
+        b == nullptr || p == nullptr || y == nullptr)
+        return 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(decode_stream_kernel, dim3((unsigned)(C / 256), (unsigned)(B / kDecRows)),
+                       dim3(256), 0, st, C, k, v, a, b, p, y);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -33,6 +33,30 @@ def test_decode_chain_equals_parallel_form(wkv, dev):
         assert_wkv_close(y.cpu().numpy(), ref[:, t], "t=%d" % t)
 
 
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 6, 7, 9])
+def test_decode_ragged_row_groups(wkv, dev, B):
+    """A lane decodes a group of four sequences; a group cut short by B (remainders 1, 2 and 3,
+    alone and after whole groups) repeats its first sequence in the missing rows, and that
+    repeat must not apply the first sequence's update twice: several steps against the
+    oracle's chain, then the state."""
+    import torch
+    C, steps, layer = 70, 6, 3
+    wn, un = wkv_inputs.decode_layer_params(layer, C=C)
+    w, u = _t(dev, wn), _t(dev, un)
+    ost = wkv_inputs.empty_decode_state(B, C)
+    a, b, p = (_t(dev, s) for s in ost)
+    for s in range(steps):
+        kn, vn = wkv_inputs.decode_step_inputs(s, layer, B=B, C=C)
+        y = wkv.decode_step(w, u, _t(dev, kn), _t(dev, vn), a, b, p)
+        yr, ost = oracle.decode_step(wn, un, kn, vn, ost)
+        torch.cuda.synchronize()
+        assert_wkv_close(y.cpu().numpy(), yr, "B=%d step %d" % (B, s))
+    ga, gb, gp = (t.cpu().numpy().astype(np.float64) for t in (a, b, p))
+    oa, ob, op = ost
+    assert_wkv_close(ga / gb, oa / ob, "state ratio")
+    np.testing.assert_allclose(gp + np.log(gb), op + np.log(ob), rtol=0, atol=1e-4)
+
+
 @pytest.mark.parametrize("layer,B,steps", [(0, 256, 1000), (39, 256, 1000), (7, 8, 1000)])
 def test_batched_decode_workload(wkv, dev, layer, B, steps):
     """The batched decode workload's full width (256 sequences x 5120 channels) over its whole
